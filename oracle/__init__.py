@@ -1,0 +1,27 @@
+"""Reference oracle for paged decode attention — TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, CPU-only float64 implementation of what the GPU path computes, written from the
+definitions on the pages. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import it; the library under ``paged_kv_cache_287_amd`` never does, and this package
+imports nothing from it.
+
+Modules:
+
+* :mod:`oracle.attention` — decode attention read through block tables (fp16 or E4M3 KV);
+* :mod:`oracle.cache_ops` — slot-mapped KV append and copy-on-write block copies;
+* :mod:`oracle.fp8` — OCP E4M3 decoding from its bit-field definition;
+* :mod:`oracle.capacity` — the pages' KV-size and waste arithmetic.
+
+Every function is pinned by ``-m "not gpu"`` tests to something other than itself (the pages'
+printed numbers, closed forms, torch's independent attention routine, brute force on tiny
+inputs, invariants). No function here is "parity unpinned".
+"""
+from .attention import decode, gather_sequence  # noqa: F401
+from .cache_ops import copy_blocks, kv_write  # noqa: F401
+from .capacity import (  # noqa: F401
+    kv_cache_bytes,
+    max_concurrent_requests,
+    naive_waste_fraction,
+    paged_waste_slots,
+)
+from .fp8 import E4M3_TABLE, e4m3_to_float  # noqa: F401

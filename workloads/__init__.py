@@ -1,0 +1,18 @@
+"""Seeded synthetic inputs for paged decode attention (shared by the oracle tests, the GPU
+parity tests and the benchmark). No attention arithmetic lives here."""
+from .block_manager import AppendPlan, BlockManager, PoolExhausted, check_plan  # noqa: F401
+from .configs import (  # noqa: F401
+    SEEDS,
+    DecodeCase,
+    StepInputs,
+    by_name,
+    eight_b,
+    normal_f16,
+    random_case,
+    shared_prefix,
+    softmax_scale,
+    sweep,
+    tiny,
+    variant,
+)
+from .quant import quantize_pool, quantize_tile  # noqa: F401
