@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+One step is one decode step of the whole path over one batch: ``pa_copy_blocks`` (the step's
+copy-on-write pairs, if any), ``pa_kv_write`` (one new token per sequence into its slot) and
+``pa_decode`` over every attended token. Inputs are synthetic, seeded, and resident in HBM
+before the timed region starts. The default workload is the 8B-shaped decode: 64 sequences x
+4096 tokens, 32 query / 8 KV heads, head dim 128, block size 16, fp16 KV, blocks scattered over
+a pool 1.25x the live blocks.
+
+Prints ONE JSON line. ``value`` is KV bytes attended per second (GB/s, decimal) over whole
+steps; ``roofline`` prices ``pa_decode`` (its algorithmic bytes: KV + q + out + tables) per
+call against the 8 TB/s HBM peak, with the call's duration taken from HIP events recorded on
+the stream the kernels run on; ``cpu_baseline`` times the float64 CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8b_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_287_amd", "csrc", f)
+                  for f in ("decode.hip", "pa_internal.hpp")]
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="8b",
+                    help="8b | tiny | prefix | sweep_bs{8,16,32,64} | variant_hkv{32,8,1}_{f16,fp8_e4m3}")
+    ap.add_argument("--flushed-calls", type=int, default=50,
+                    help="pa_decode calls timed one by one after evicting the caches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    return ap.parse_args()
+
+
+def describe(case) -> str:
+    lens = case.context_lens
+    same = int(lens.min()) == int(lens.max())
+    ctx = f"{int(lens[0])} tokens" if same else f"{int(lens.min())}-{int(lens.max())} tokens"
+    return (f"paged decode {case.name}: {case.num_seqs} seqs x {ctx}, {case.num_q_heads}q/"
+            f"{case.num_kv_heads}kv heads, head_dim {case.head_dim}, block_size {case.block_size}, "
+            f"{case.kv_dtype} KV, pool {case.num_blocks} blocks")
+
+
+def kv_bytes(case, unique: bool = True) -> int:
+    """Algorithmic KV bytes one decode reads: every attended token's K and V for every KV head
+    (shared blocks counted once when ``unique``), plus per-block scales for 8-bit caches."""
+    bs, esz = case.block_size, case.kv_bytes_per_value
+    per_tok = 2 * case.num_kv_heads * case.head_dim * esz
+    used = {}
+    total_tok = 0
+    for row, L in zip(case.block_tables, case.context_lens):
+        L = int(L)
+        total_tok += L
+        for i in range(-(-L // bs)):
+            n = min(bs, L - i * bs)
+            blk = int(row[i])
+            used[blk] = max(used.get(blk, 0), n)
+    tok = sum(used.values()) if unique else total_tok
+    blocks = len(used) if unique else sum(-(-int(L) // bs) for L in case.context_lens)
+    scales = 2 * case.num_kv_heads * 4 * blocks if case.kv_dtype != "f16" else 0
+    return tok * per_tok + scales
+
+
+def decode_call_bytes(case) -> int:
+    s, hq, d = case.q.shape
+    tables = sum(4 * -(-int(L) // case.block_size) for L in case.context_lens) + 4 * s
+    return kv_bytes(case) + 2 * s * hq * d * 2 + tables
+
+
+def make_step_inputs(case):
+    """The step's cache updates. Workloads without an explicit step rewrite each sequence's
+    newest token (position L - 1) in place, which keeps the inputs identical across steps."""
+    import numpy as np
+
+    if case.step is not None:
+        st = case.step
+        return st.block_mapping.reshape(-1, 2), st.new_k, st.new_v, st.slot_mapping
+    bs = case.block_size
+    ks, vs, slots = [], [], []
+    for b, L in enumerate(case.context_lens):
+        L = int(L)
+        if L == 0:
+            continue
+        ks.append(case.logical_k[b][L - 1])
+        vs.append(case.logical_v[b][L - 1])
+        slots.append(int(case.block_tables[b, (L - 1) // bs]) * bs + (L - 1) % bs)
+    return (np.zeros((0, 2), np.int32), np.stack(ks), np.stack(vs), np.asarray(slots, np.int64))
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the float64 oracle, sequence by sequence, until the budget is spent."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    done, bytes_done, tok_done = 0, 0, 0
+    bs = case.block_size
+    per_tok = 2 * case.num_kv_heads * case.head_dim * case.kv_bytes_per_value
+    t0 = time.perf_counter()
+    for b in range(case.num_seqs):
+        oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                      case.scale, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                      v_scale=case.v_scale, seqs=[b])
+        done += 1
+        tok_done += int(case.context_lens[b])
+        bytes_done += int(case.context_lens[b]) * per_tok
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": bytes_done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {case.num_seqs} sequences of the same workload ({tok_done} "
+                      f"seq-tokens, {dt:.1f} s, float64 numpy, BLAS limited to 1 thread)",
+            "seq_tokens_per_s": tok_done / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_287_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    progress(f"generating workload {args.workload}")
+    case = workloads.by_name(args.workload)
+    pairs, nk, nv, slots = make_step_inputs(case)
+
+    def dev(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.float16:
+            return torch.from_numpy(x.view(np.uint16)).cuda().view(torch.float16)
+        return torch.from_numpy(x).cuda()
+
+    q, kc, vc = dev(case.q), dev(case.k_cache), dev(case.v_cache)
+    ks, vs = dev(case.k_scale), dev(case.v_scale)
+    tables, lens = dev(case.block_tables), dev(case.context_lens)
+    g_pairs, g_nk, g_nv, g_slots = dev(pairs.astype(np.int32)), dev(nk), dev(nv), dev(slots)
+    out = torch.empty_like(q)
+    max_ctx = int(case.context_lens.max())
+    ws_bytes = pa.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
+                                         case.block_size, max_ctx,
+                                         pa.PA_KV_F16 if case.kv_dtype == "f16" else pa.PA_KV_FP8_E4M3)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def decode():
+        pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
+                     max_context_len=max_ctx, workspace=ws)
+
+    def step(ev0=None, ev1=None):
+        if g_pairs.shape[0]:
+            pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
+        if case.kv_dtype == "f16":
+            pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots)
+        if ev0 is not None:
+            ev0.record(stream)
+        decode()
+        if ev1 is not None:
+            ev1.record(stream)
+
+    progress(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    progress(f"timing {args.steps} steps")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    call_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    avg_call_ms = sum(call_ms) / len(call_ms)
+
+    # per-call timing after evicting L2 and the 256 MiB Infinity Cache with a 1 GiB copy
+    flushed = None
+    if args.flushed_calls > 0:
+        progress(f"timing {args.flushed_calls} flushed calls")
+        fa = torch.empty(256 * 2 ** 20, dtype=torch.float32, device="cuda")
+        fb = torch.empty_like(fa)
+        times = []
+        for _ in range(args.flushed_calls):
+            fb.copy_(fa)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            decode()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        times.sort()
+        flushed = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
+                   "p90_us": times[(9 * len(times)) // 10]}
+        del fa, fb
+
+    kvb = kv_bytes(case)
+    seq_tokens = int(case.context_lens.sum())
+    value = kvb / (ms_per_step * 1e-3) / 1e9
+    call_bytes = decode_call_bytes(case)
+    achieved = call_bytes / (avg_call_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_sha256") == kernel_source_hash() and tr.get("workload") == args.workload:
+            traffic = tr.get("hbm_bytes_per_call")
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+                "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3}
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+    line = {
+        "metric": "paged decode attention: KV GB/s (% of HBM peak) + seq-tokens/s, 8B-shaped, 1 GPU",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) fp16 q/K/V, scattered blocks, NaN-poisoned unused slots)",
+        "config": {"workload": describe(case), "num_seqs": case.num_seqs,
+                   "max_context_len": max_ctx, "q_heads": case.num_q_heads,
+                   "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+                   "block_size": case.block_size, "kv_dtype": case.kv_dtype,
+                   "step": "copy_blocks(pairs) + kv_write(1 token/seq) + decode"},
+        "hbm_frac": value / HBM_PEAK_GBS,
+        "seq_tokens_per_s": seq_tokens / (ms_per_step * 1e-3),
+        "kv_bytes_per_step": kvb,
+        "flushed_decode": flushed,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * pa.h — paged decode attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The KV cache is a pool of fixed-size blocks that need not be contiguous in memory; each
+ * sequence keeps a block table whose entry i names the physical block that holds its logical
+ * block i, and attention reads the scattered blocks through that table
+ * ("serving-paged-attention", section "블록으로 쪼개고 표로 잇는다"; the talk summary's vLLM
+ * paragraph: logically contiguous, physically scattered). New tokens are placed by slot
+ * ("vLLM의 핵심 이해: PagedAttention", section 6, TokenTable / SlotAllocator), and a shared
+ * block that is still filling is copied before a sequence writes into it
+ * ("serving-paged-attention", section "공유는 표를 베끼는 일이 된다").
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked otherwise; every call only enqueues work on
+ *     `stream` (a hipStream_t; NULL = the legacy default stream) and returns without waiting.
+ *   - The caller owns every buffer (including the decode workspace). The library allocates,
+ *     frees and synchronises nothing and keeps no per-call state; calls are re-entrant.
+ *   - Only host-side scalars and pointers are validated, before anything is enqueued. On a
+ *     validation failure nothing is enqueued and the status code says why. Launch failures
+ *     return PA_ERR_HIP; pa_last_hip_error() then gives the hipError_t (per calling thread).
+ *   - Device-side data is NOT validated (documented preconditions below); violating them gives
+ *     wrong values, but out-of-range block ids and slots are clamped or skipped on the device,
+ *     so no access leaves the caller's buffers.
+ *   - All arrays are row-major and densely packed.
+ *
+ * Layouts (S sequences, Hq query heads, Hkv KV heads, D head dim, BS block size, NB blocks):
+ *   q, out        [S, Hq, D]            fp16
+ *   k_cache       [NB, Hkv, BS, D]      fp16, or uint8 OCP FP8 E4M3 codes
+ *   v_cache       [NB, Hkv, BS, D]      same type as k_cache
+ *   k_scale       [NB, Hkv]             fp32 per (block, KV head) dequant scale (E4M3 only)
+ *   v_scale       [NB, Hkv]             fp32
+ *   block_tables  [S, max_blocks_per_seq] int32 physical block ids
+ *   context_lens  [S]                   int32 tokens attended per sequence
+ *   k, v (new)    [T, Hkv, D]           fp16
+ *   slot_mapping  [T]                   int64, slot = block * BS + offset, < 0 = skip
+ *   block_mapping [P, 2]                int32 (src, dst) pairs
+ * Supported: D in {64, 128}; BS in {8, 16, 32, 64}; any Hq that is a multiple of Hkv.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, Hq % Hkv != 0, ...     */
+  PA_ERR_UNSUPPORTED = 2, /* head_dim / block_size / dtype combination not compiled in     */
+  PA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required             */
+  PA_ERR_HIP = 4          /* a HIP launch failed; see pa_last_hip_error()                  */
+} pa_status;
+
+typedef enum {
+  PA_KV_F16 = 0,      /* IEEE binary16 keys and values                                      */
+  PA_KV_FP8_E4M3 = 1  /* OCP FP8 E4M3 codes (bias 7, max 448, S.1111.111 = NaN), with one     */
+                      /* fp32 scale per (block, KV head): value = decode(code) * scale        */
+} pa_kv_dtype;
+
+/* Returns PA_ABI_VERSION of the loaded library. */
+int pa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* pa_status_str(int status);
+
+/* hipError_t value behind the most recent PA_ERR_HIP returned on the calling thread (0 if none). */
+int pa_last_hip_error(void);
+
+/* Context tokens handled by one workgroup of pa_decode (the split-context partition size). */
+int32_t pa_decode_partition_tokens(int32_t head_dim, int32_t block_size, int32_t kv_dtype);
+
+/* Bytes of device workspace pa_decode needs for this shape; 0 if none is needed
+ * (max_context_len <= one partition) or if the arguments are invalid. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_context_len, int32_t kv_dtype);
+
+/*
+ * pa_decode — one query token per sequence attends over its paged KV cache.
+ *
+ * For every sequence b with L = context_lens[b] and every query head h, with G = Hq / Hkv and
+ * g = h / G (query heads share KV heads in contiguous groups: MHA G = 1, GQA, MQA Hkv = 1; the
+ * talk summary's attention-heads paragraph):
+ *     K_b[t] = k_cache[block_tables[b, t / BS], g, t % BS, :]   (t < L, likewise V_b)
+ *     out[b, h, :] = softmax(scale * K_b q[b, h]) V_b           (fp32 accumulate, fp16 out)
+ * evaluated with an online softmax (running max, running sum, running output) over tiles and
+ * split across context partitions that a second kernel merges exactly (talk summary,
+ * FlashAttention paragraph). L = 0 gives out = 0. For E4M3 caches each value is
+ * decode(code) * scale[block, g] before use. context_lens counts every token to attend,
+ * including one appended by this step's pa_kv_write.
+ *
+ *   max_context_len  host-side upper bound on context_lens[] used to size the grid;
+ *                    <= 0 means max_blocks_per_seq * block_size.
+ *   scale            softmax scale (finite), usually 1/sqrt(head_dim).
+ *   workspace        >= pa_decode_workspace_bytes(...) bytes of device memory, 256-byte
+ *                    aligned (may be NULL when that size is 0). Contents are scratch.
+ *   num_blocks       NB, the number of blocks in each cache.
+ * Preconditions (not checked): 0 <= context_lens[b] <= max_context_len (as passed or implied);
+ * 0 <= block_tables[b, i] < num_blocks for i < ceil(L / BS) (later entries are never read);
+ * attended E4M3 codes are not NaN; out does not alias any input. Violations give wrong values
+ * but no access outside the buffers: block ids are clamped into [0, num_blocks), tokens beyond
+ * the grid's partitions are dropped.
+ * Validated: non-NULL pointers (k_scale/v_scale must be NULL for fp16 and non-NULL for E4M3),
+ * 16-byte alignment of q, out, k_cache, v_cache; 4-byte alignment of the int arrays and scales;
+ * positive sizes; Hq % Hkv == 0; supported head_dim, block_size and dtype; workspace size.
+ * Deterministic: results depend only on logical token positions, not on physical ids.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+              int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_kv_write — slot-mapped append of new keys and values.
+ *
+ * For each token t < num_tokens with slot = slot_mapping[t] >= 0, writes
+ *     k_cache[slot / BS, h, slot % BS, :] = k[t, h, :]   and the same for v, for all h.
+ * Tokens with a negative slot, or a slot >= num_blocks * block_size, are skipped. Nothing else
+ * in the caches changes.
+ * Supports PA_KV_F16 caches only (E4M3 append returns PA_ERR_UNSUPPORTED).
+ * Precondition (not checked): non-negative slots are distinct.
+ * Validated: pointers, 16-byte alignment of k, v, caches; 8-byte alignment of slot_mapping;
+ * sizes; num_blocks * block_size < 2^31.
+ */
+int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                void* stream);
+
+/*
+ * pa_copy_blocks — copy-on-write block copies.
+ *
+ * For each pair p < num_pairs: cache[dst] = cache[src] for K and V over all KV heads, and for
+ * E4M3 caches also k_scale[dst, :] = k_scale[src, :] and v_scale[dst, :] = v_scale[src, :],
+ * with (src, dst) = block_mapping[p]. Every copy reads the state before the call.
+ * Pairs with an id outside [0, num_blocks) are skipped. Precondition (not checked):
+ * destinations are distinct and none is a source. Validated: pointers (scales NULL for fp16, non-NULL for E4M3), 16-byte alignment
+ * of the caches, sizes, num_blocks * block_size < 2^31.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int32_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

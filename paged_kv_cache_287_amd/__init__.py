@@ -1,0 +1,188 @@
+"""Python binding of ``libpa.so``: paged decode attention for MI355X (gfx950).
+
+The binding only marshals arguments: it turns torch device tensors into pointers and sizes,
+passes torch's current HIP stream, and turns a non-zero status into :class:`PaError`. Every
+step of the computation runs in the library's HIP kernels; there is no fallback. Importing
+this package fails if ``libpa.so`` has not been built (``python -m paged_kv_cache_287_amd.build``).
+
+torch is imported first so that its HIP runtime (``libamdhip64.so.7``) is the one the library
+binds to: the library is linked without an RPATH and resolves that SONAME to the copy already
+in the process, so torch's stream handles and device pointers are valid inside it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
+    "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
+    "decode_workspace_bytes", "decode_partition_tokens", "pa_decode", "pa_kv_write",
+    "pa_copy_blocks",
+]
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_KV_F16, PA_KV_FP8_E4M3 = 0, 1
+ABI_VERSION = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+_p, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+#: every entry point declared in include/pa.h with its (restype, argtypes)
+EXPORTED_SYMBOLS = {
+    "pa_abi_version": (ctypes.c_int, []),
+    "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_hip_error": (ctypes.c_int, []),
+    "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.pa_status_str(status).decode()
+        if status == PA_ERR_HIP:
+            msg += f" (hipError_t {lib.pa_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [status {status}]")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_287_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTED_SYMBOLS.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    if handle.pa_abi_version() != ABI_VERSION:
+        raise ImportError(f"libpa.so ABI {handle.pa_abi_version()} != binding ABI {ABI_VERSION}")
+    return handle
+
+
+lib = _load()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _kv_dtype(cache: torch.Tensor) -> int:
+    if cache.dtype == torch.float16:
+        return PA_KV_F16
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_KV_FP8_E4M3
+    raise TypeError(f"KV cache dtype {cache.dtype} is not supported")
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, block_size: int,
+                           max_context_len: int, kv_dtype: int = PA_KV_F16) -> int:
+    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size,
+                                             max_context_len, kv_dtype))
+
+
+def decode_partition_tokens(head_dim: int, block_size: int, kv_dtype: int = PA_KV_F16) -> int:
+    return int(lib.pa_decode_partition_tokens(head_dim, block_size, kv_dtype))
+
+
+def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
+              k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+              max_context_len: int = 0, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Enqueue paged decode attention; writes ``out`` [S, Hq, D] fp16 and returns it.
+
+    ``workspace`` (uint8 device tensor) is allocated here when omitted and needed.
+    """
+    _check(q, "q", (torch.float16,), 3)
+    _check(out, "out", (torch.float16,), 3)
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(block_tables, "block_tables", (torch.int32,), 2)
+    _check(context_lens, "context_lens", (torch.int32,), 1)
+    kvt = _kv_dtype(k_cache)
+    if kvt == PA_KV_FP8_E4M3:
+        for n, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{n} is required for an 8-bit cache")
+            _check(s, n, (torch.float32,), 2)
+    num_seqs, num_q_heads, head_dim = q.shape
+    nb, num_kv_heads, block_size, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != head_dim or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    mbps = block_tables.shape[1]
+    need = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size,
+                                  max_context_len if max_context_len > 0 else mbps * block_size, kvt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                       _ptr(block_tables), _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, nb, mbps, max_context_len, float(scale), kvt,
+                       _ptr(workspace), ws_bytes, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode")
+    return out
+
+
+def pa_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                slot_mapping: torch.Tensor, *, stream=None) -> None:
+    """Enqueue the slot-mapped append of new K/V rows [T, Hkv, D] into the caches."""
+    _check(k, "k", (torch.float16,), 3)
+    _check(v, "v", (torch.float16,), 3)
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    nb, hkv, bs, d = k_cache.shape
+    if k.shape != v.shape or k.shape[1:] != (hkv, d) or slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("shape mismatch between k, v, slot_mapping and the caches")
+    st = lib.pa_kv_write(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+                         k.shape[0], hkv, d, bs, nb, _kv_dtype(k_cache), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_kv_write")
+
+
+def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor, *,
+                   k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Enqueue copy-on-write block copies for every (src, dst) row of ``block_mapping`` [P, 2]."""
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(block_mapping, "block_mapping", (torch.int32,), 2)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2]")
+    nb, hkv, bs, d = k_cache.shape
+    st = lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(block_mapping), block_mapping.shape[0], hkv, d, bs, nb,
+                            _kv_dtype(k_cache), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_copy_blocks")

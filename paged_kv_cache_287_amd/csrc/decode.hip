@@ -1,0 +1,413 @@
+// Paged decode attention for gfx950 (CDNA4): split-context partition kernel + exact merge.
+//
+// What is computed (per sequence b, query head h, KV head g = h / G):
+//   out[b, h] = softmax(scale * K_b q) V_b, where token t of K_b / V_b lives in physical block
+//   block_tables[b, t / BS] at offset t % BS ("serving-paged-attention", section "블록으로
+//   쪼개고 표로 잇는다": attention looks the scattered blocks up through the table). The softmax
+//   is evaluated online, tile by tile, tracking a running maximum, a running sum of
+//   exponentials and a running weighted value sum, so no score matrix ever leaves the chip
+//   (talk summary, FlashAttention paragraph: tiles kept on chip, three running quantities).
+//   Decode reads every cached byte once per step and is bound by memory bandwidth (talk
+//   summary, prefill/decode paragraphs), so the kernel is organised around HBM traffic.
+//
+// Mapping onto CDNA4:
+//   * workgroup = (KV head [x GT query heads], sequence, 512-token context partition), 4 waves;
+//     each wave owns 128 consecutive tokens, walked in 16-token tiles.
+//   * within a wave, each 16-lane row holds one token per step; lane `col` of the row holds
+//     elements [col*E, col*E+E) of that token (E = D/16). One step of the wave therefore loads
+//     4 consecutive token rows of a block: for D = 128 fp16 that is 1 KiB of contiguous memory
+//     with one 16-byte load per lane. K and V use the same addressing.
+//   * q . k: v_dot2 (fp16 x fp16 -> fp32) over the lane's elements, then a 16-lane all-reduce
+//     with four DPP adds (quad_perm xor 1, xor 2, row_half_mirror, row_mirror). Every lane of a
+//     row ends with the bit-identical score.
+//   * each row keeps its own online-softmax state (max, sum) per query head and a partial
+//     output of E floats per lane and head; rows and waves are merged once, through LDS, at the
+//     end of the partition. Scores are kept in log2 units (scale * log2 e folded in) so the
+//     exponentials are single v_exp_f32 instructions.
+//   * the block ids a wave needs are fetched once, one per lane, and read back with
+//     v_readlane, so the table walk costs no memory latency inside the tile loop; the next
+//     tile's K and V loads are issued before the current tile is consumed.
+//   * grid x = KV head (x head group) is the fastest-varying dimension; with 8 KV heads the
+//     round-robin dispatch of workgroups over the 8 XCDs puts every workgroup of one KV head on
+//     one XCD, so blocks shared by several sequences (a common prefix) are re-read from that
+//     XCD's L2.
+//   * results depend only on logical token positions (fixed tile, row and merge order), so
+//     they are deterministic and independent of physical block placement.
+#include "pa_internal.hpp"
+
+namespace pa {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the same bits.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror: pairs the two quads of each half-row
+  x += dpp_mov<0x140>(x);  // row_mirror: pairs the two half-rows
+  return x;
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                c, false);
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Two E4M3 codes held in bits [7:0] and [23:16] -> two fp16 holding decode(code) * 2^-8,
+// exactly: the 7 magnitude bits land on the fp16 exponent/mantissa fields (E4M3 subnormals map
+// onto fp16 subnormals), the sign bit moves to bit 15.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_div256(uint32_t x) {
+  return ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
+}
+
+template <int NWORDS>
+struct Chunk {
+  uint32_t w[NWORDS];
+};
+
+template <int NWORDS>
+__device__ __forceinline__ Chunk<NWORDS> load_chunk(const uint8_t* ptr) {
+  Chunk<NWORDS> c;
+  if constexpr (NWORDS == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(ptr);
+    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+  } else if constexpr (NWORDS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(ptr);
+    c.w[0] = v.x; c.w[1] = v.y;
+  } else {
+    c.w[0] = *reinterpret_cast<const uint32_t*>(ptr);
+  }
+  return c;
+}
+
+// Per-lane view of one token's elements as fp16 pairs (E/2 words).
+template <int E, bool KV8>
+__device__ __forceinline__ void to_half_pairs(const Chunk<(KV8 ? E : 2 * E) / 4>& c,
+                                              uint32_t (&h)[E / 2]) {
+  if constexpr (!KV8) {
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) h[i] = c.w[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const uint32_t w = c.w[i];
+      const uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8);
+      const uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u);
+      h[2 * i] = e4m3x2_to_f16x2_div256(lo);
+      h[2 * i + 1] = e4m3x2_to_f16x2_div256(hi);
+    }
+  }
+}
+
+template <int D, int BS, int GT, bool KV8>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
+  constexpr int E = D / 16;                 // elements per lane per token
+  constexpr int ESZ = KV8 ? 1 : 2;          // bytes per cached element
+  constexpr int LANE_BYTES = E * ESZ;       // 16, 8 or 4
+  constexpr int NWORDS = LANE_BYTES / 4;
+  constexpr int NH2 = E / 2;                // fp16 pairs per lane per token
+  constexpr int ROW_BYTES = D * ESZ;        // one token of one head
+  constexpr int TILE_BYTES = BS * ROW_BYTES;  // one (block, head) tile
+  static_assert(kWaveTokens % BS == 0 && kWaveTokens / BS <= kWave, "block ids per wave");
+  static_assert(BS % kRows == 0, "a step's four tokens must share a block");
+
+  const int hg = blockIdx.x;
+  const int b = blockIdx.y;
+  const int part = blockIdx.z;
+  const int kvh = hg / p.head_groups;
+  const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * GT;
+  const int L = p.context_lens[b];
+  // partitions beyond the grid's (context longer than the host bound) are dropped, never
+  // written outside the workspace
+  const int nparts = min(L > 0 ? (L + kPartTokens - 1) / kPartTokens : 1, p.max_parts);
+  if (part >= nparts) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int row = lane >> 4;
+  const int col = lane & 15;
+
+  // ---- query rows of this head group: E fp16 per lane per head -------------------------
+  uint32_t qw[GT][NH2];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(
+        p.q + ((size_t)b * p.num_q_heads + h0 + h) * D + col * E);
+    const Chunk<E / 2> c = load_chunk<E / 2>(qp);
+#pragma unroll
+    for (int i = 0; i < NH2; ++i) qw[h][i] = c.w[i];
+  }
+
+  // ---- block ids of this wave's tokens: lane j holds logical block lb0 + j ---------------
+  const int wbase = part * kPartTokens + wave * kWaveTokens;
+  const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
+  int my_id = 0;
+  if (wbase < L) {
+    const int lb = min(wbase / BS + lane, nblk - 1);
+    my_id = p.block_tables[(size_t)b * p.max_blocks_per_seq + lb];
+    my_id = min(max(my_id, 0), p.num_blocks - 1);  // a bad id reads a wrong block, never outside the pool
+  }
+
+  const uint8_t* kbase = p.k_cache + (size_t)kvh * TILE_BYTES;
+  const uint8_t* vbase = p.v_cache + (size_t)kvh * TILE_BYTES;
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE_BYTES;
+  const int lane_off = row * ROW_BYTES + col * LANE_BYTES;
+
+  float m[GT], l[GT], acc[GT][E];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
+
+  Chunk<NWORDS> ka[kSteps], va[kSteps], kb[kSteps], vb[kSteps];
+
+  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[kSteps], Chunk<NWORDS>(&vc)[kSteps]) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int t = kTileTokens * i + kRows * s;  // first token of the step, wave-relative
+      const int id = __builtin_amdgcn_readlane(my_id, t / BS);
+      const size_t off = (size_t)id * blk_stride + (size_t)((t % BS) * ROW_BYTES + lane_off);
+      kc[s] = load_chunk<NWORDS>(kbase + off);
+      vc[s] = load_chunk<NWORDS>(vbase + off);
+    }
+  };
+
+  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[kSteps],
+                          const Chunk<NWORDS>(&vc)[kSteps], bool masked) {
+    const int tok0 = wbase + kTileTokens * i;
+    float sc[kSteps][GT];
+    float kmul[kSteps], vmul[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      kmul[s] = p.scale_log2;
+      vmul[s] = 1.f;
+      if constexpr (KV8) {
+        const int t = kTileTokens * i + kRows * s;
+        const int id = __builtin_amdgcn_readlane(my_id, t / BS);
+        kmul[s] *= 256.f * p.k_scale[(size_t)id * p.num_kv_heads + kvh];
+        vmul[s] = 256.f * p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+      }
+      uint32_t kh[NH2];
+      to_half_pairs<E, KV8>(kc[s], kh);
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int w = 0; w < NH2; ++w) d = dot2(kh[w], qw[h][w], d);
+        sc[s][h] = d;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const bool valid = !masked || (tok0 + kRows * s + row < L);
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float x = row_sum16(sc[s][h]) * kmul[s];
+        sc[s][h] = valid ? x : kNegInf;
+      }
+    }
+    // online softmax: new running max, rescale, exponentiate this tile's scores
+    float pw[kSteps][GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float mt = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
+      const float mn = fmaxf(m[h], mt);
+      const float ms = (masked && mn == kNegInf) ? 0.f : mn;
+      const float alpha = fexp2(m[h] - ms);
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) pw[s][h] = fexp2(sc[s][h] - ms);
+      l[h] = l[h] * alpha + ((pw[0][h] + pw[1][h]) + (pw[2][h] + pw[3][h]));
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    }
+    // weighted value sum
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      uint32_t vh[NH2];
+      to_half_pairs<E, KV8>(vc[s], vh);
+      if (masked) {
+        const bool valid = tok0 + kRows * s + row < L;
+#pragma unroll
+        for (int w = 0; w < NH2; ++w) vh[w] = valid ? vh[w] : 0u;
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float pv = KV8 ? pw[s][h] * vmul[s] : pw[s][h];
+#pragma unroll
+        for (int w = 0; w < NH2; ++w) {
+          acc[h][2 * w] = fmaf(pv, half_lo(vh[w]), acc[h][2 * w]);
+          acc[h][2 * w + 1] = fmaf(pv, half_hi(vh[w]), acc[h][2 * w + 1]);
+        }
+      }
+    }
+  };
+
+  // Tiles [0, n_full) are complete; tile n_full is the masked tail when the context ends
+  // inside this wave's range. Two register buffers alternate so the next tile's loads are in
+  // flight while the current one is consumed.
+  const int avail = max(0, min(L - wbase, kWaveTokens));
+  const int n_full = avail / kTileTokens;
+  const bool has_tail = (avail % kTileTokens) != 0;
+  const int n_tiles = n_full + (has_tail ? 1 : 0);
+  if (n_tiles > 0) issue_tile(0, ka, va);
+  int i = 0;
+  for (; i + 1 < n_full; i += 2) {
+    issue_tile(i + 1, kb, vb);
+    consume_tile(i, ka, va, false);
+    if (i + 2 < n_tiles) issue_tile(i + 2, ka, va);
+    consume_tile(i + 1, kb, vb, false);
+  }
+  if (i < n_full) {
+    if (has_tail) issue_tile(i + 1, kb, vb);
+    consume_tile(i, ka, va, false);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      ka[s] = kb[s];
+      va[s] = vb[s];
+    }
+    ++i;
+  }
+  if (has_tail) consume_tile(i, ka, va, true);
+
+  // ---- merge the 4 rows x kWaves waves of this workgroup through LDS --------------------
+  __shared__ float s_acc[kWaves * kRows][GT][D];
+  __shared__ float s_ml[kWaves * kRows][GT][2];
+  const int sub = wave * kRows + row;
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) s_acc[sub][h][col * E + e] = acc[h][e];
+    if (col == 0) {
+      s_ml[sub][h][0] = m[h];
+      s_ml[sub][h][1] = l[h];
+    }
+  }
+  __syncthreads();
+
+  const bool single = nparts == 1;
+  for (int idx = tid; idx < GT * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kWaves * kRows; ++k) mx = fmaxf(mx, s_ml[k][h][0]);
+    const float ms = mx == kNegInf ? 0.f : mx;
+    float ls = 0.f, a = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves * kRows; ++k) {
+      const float w = fexp2(s_ml[k][h][0] - ms);
+      ls = fmaf(w, s_ml[k][h][1], ls);
+      a = fmaf(w, s_acc[k][h][d], a);
+    }
+    const size_t oh = (size_t)b * p.num_q_heads + h0 + h;
+    if (single) {
+      p.out[oh * D + d] = (_Float16)(ls > 0.f ? a / ls : 0.f);
+    } else {
+      const size_t slot = oh * p.max_parts + part;
+      p.ws_acc[slot * D + d] = a;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = mx;
+        p.ws_ml[slot * 2 + 1] = ls;
+      }
+    }
+  }
+}
+
+// Exact merge of the partitions of one (sequence, query head): with partition maxima m_p, sums
+// l_p and value sums a_p, out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+template <int D>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
+  constexpr int PER = D / kWave;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int L = p.context_lens[b];
+  const int np = min((L + kPartTokens - 1) / kPartTokens, p.max_parts);
+  if (np <= 1) return;
+  const int lane = threadIdx.x;
+  const size_t oh = (size_t)b * p.num_q_heads + h;
+  const float* ml = p.ws_ml + oh * p.max_parts * 2;
+  const float* ac = p.ws_acc + oh * p.max_parts * D + lane * PER;
+  float mx = kNegInf;
+  for (int i = 0; i < np; ++i) mx = fmaxf(mx, ml[2 * i]);
+  float ls = 0.f, a[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) a[e] = 0.f;
+  for (int i = 0; i < np; ++i) {
+    const float w = fexp2(ml[2 * i] - mx);
+    ls = fmaf(w, ml[2 * i + 1], ls);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) a[e] = fmaf(w, ac[(size_t)i * D + e], a[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) p.out[oh * D + lane * PER + e] = (_Float16)(a[e] / ls);
+}
+
+template <int D, int BS, int GT, bool KV8>
+hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  const dim3 grid(p.num_kv_heads * p.head_groups, num_seqs, p.max_parts);
+  decode_partition_kernel<D, BS, GT, KV8><<<grid, kThreads, 0, stream>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_parts <= 1) return e;
+  decode_reduce_kernel<D><<<dim3(p.num_q_heads, num_seqs), kWave, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int D, int BS, bool KV8>
+hipError_t dispatch_gt(const DecodeParams& p, int num_seqs, int gt, hipStream_t stream) {
+  switch (gt) {
+    case 1: return launch_one<D, BS, 1, KV8>(p, num_seqs, stream);
+    case 2: return launch_one<D, BS, 2, KV8>(p, num_seqs, stream);
+    case 4: return launch_one<D, BS, 4, KV8>(p, num_seqs, stream);
+    case 8: return launch_one<D, BS, 8, KV8>(p, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool KV8>
+hipError_t dispatch_bs(const DecodeParams& p, int num_seqs, int bs, int gt, hipStream_t stream) {
+  switch (bs) {
+    case 8: return dispatch_gt<D, 8, KV8>(p, num_seqs, gt, stream);
+    case 16: return dispatch_gt<D, 16, KV8>(p, num_seqs, gt, stream);
+    case 32: return dispatch_gt<D, 32, KV8>(p, num_seqs, gt, stream);
+    case 64: return dispatch_gt<D, 64, KV8>(p, num_seqs, gt, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
+                         int head_tile, bool kv_fp8, hipStream_t stream) {
+  if (head_dim == 128)
+    return kv_fp8 ? dispatch_bs<128, true>(p, num_seqs, block_size, head_tile, stream)
+                  : dispatch_bs<128, false>(p, num_seqs, block_size, head_tile, stream);
+  if (head_dim == 64)
+    return kv_fp8 ? dispatch_bs<64, true>(p, num_seqs, block_size, head_tile, stream)
+                  : dispatch_bs<64, false>(p, num_seqs, block_size, head_tile, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

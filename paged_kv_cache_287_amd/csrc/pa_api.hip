@@ -1,0 +1,165 @@
+// C-ABI entry points: host-side validation, grid sizing and launch on the caller's stream.
+// Nothing here allocates, frees or synchronises; all buffers belong to the caller.
+#include <math.h>
+
+#include "../../include/pa.h"
+#include "pa_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32 || bs == 64; }
+bool known_dtype(int t) { return t == PA_KV_F16 || t == PA_KV_FP8_E4M3; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return PA_ERR_HIP;
+}
+
+size_t workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+  if (max_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  const size_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+  return ml + rows * head_dim * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim / block_size / dtype";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int pa_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t pa_decode_partition_tokens(int32_t head_dim, int32_t block_size, int32_t kv_dtype) {
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || !known_dtype(kv_dtype))
+    return 0;
+  return pa::kPartTokens;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_context_len, int32_t kv_dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || !supported_head_dim(head_dim) ||
+      !supported_block_size(block_size) || !known_dtype(kv_dtype))
+    return 0;
+  return workspace_bytes(num_seqs, num_q_heads, head_dim, pa::decode_num_parts(max_context_len));
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+              int32_t kv_dtype, void* workspace, size_t workspace_bytes_given, void* stream) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const bool fp8 = kv_dtype == PA_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || (fp8 && (!aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))))
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return PA_ERR_INVALID_ARG;
+  const long long max_ctx = max_context_len > 0 ? (long long)max_context_len
+                                                : (long long)max_blocks_per_seq * block_size;
+  if (max_ctx > (long long)max_blocks_per_seq * block_size || max_ctx > (1LL << 30))
+    return PA_ERR_INVALID_ARG;
+  const int max_parts = pa::decode_num_parts((int)max_ctx);
+  if (max_parts > 65535) return PA_ERR_INVALID_ARG;
+  const size_t need = workspace_bytes(num_seqs, num_q_heads, head_dim, max_parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes_given < need || !aligned(workspace, 256)))
+    return PA_ERR_WORKSPACE;
+
+  pa::DecodeParams p{};
+  p.out = static_cast<_Float16*>(out);
+  p.q = static_cast<const _Float16*>(q);
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  p.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  p.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             (rows * 2 * sizeof(float) + 255) / 256 * 256)
+                  : nullptr;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.max_parts = max_parts;
+  p.group = num_q_heads / num_kv_heads;
+  const int gt = pa::pick_head_tile(p.group);
+  p.head_groups = p.group / gt;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (!known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype != PA_KV_F16) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if ((long long)num_blocks * block_size >= (1LL << 31)) return PA_ERR_INVALID_ARG;
+  if ((long long)num_tokens * num_kv_heads * (head_dim * 2 / 16) >= (1LL << 31))
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_kv_write(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                        num_kv_heads, head_dim, block_size, num_blocks,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int32_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                   void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (!known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if ((long long)num_blocks * block_size >= (1LL << 31)) return PA_ERR_INVALID_ARG;
+  if (num_kv_heads > 65535) return PA_ERR_INVALID_ARG;
+  const bool fp8 = kv_dtype == PA_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, block_mapping,
+                                           num_pairs, num_kv_heads, head_dim, block_size,
+                                           num_blocks, fp8 ? 1 : 2,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -32,23 +32,27 @@ def quantize_tile(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
     return codes, s
 
 
-def quantize_pool(cache: np.ndarray, live_blocks: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """Quantize a ``[NB, Hkv, BS, D]`` fp16 pool tile by tile.
+def quantize_pool(cache: np.ndarray, live_blocks: np.ndarray, chunk: int = 2048) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize a ``[NB, Hkv, BS, D]`` fp16 pool tile by tile (same rule as :func:`quantize_tile`).
 
     Blocks not in ``live_blocks`` become all-NaN codes with a NaN scale (they are never read).
-    Returns ``(codes uint8 [NB, Hkv, BS, D], scales float32 [NB, Hkv])``.
+    Works on ``chunk`` blocks at a time. Returns ``(codes uint8 [NB, Hkv, BS, D], scales float32
+    [NB, Hkv])``.
     """
     nb, hkv = cache.shape[:2]
     codes = np.full(cache.shape, E4M3_NAN_CODE, dtype=np.uint8)
     scales = np.full((nb, hkv), np.nan, dtype=np.float32)
-    xf = cache[live_blocks].astype(np.float32)  # [n, Hkv, BS, D]
-    live = ~np.isnan(xf)
-    amax = np.max(np.where(live, np.abs(xf), 0.0), axis=(2, 3))  # [n, Hkv]
-    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    y = np.clip(np.where(live, xf, 0.0) / s[:, :, None, None], -E4M3_MAX, E4M3_MAX)
-    c = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(torch.float8_e4m3fn)
-    c = c.view(torch.uint8).numpy().copy()
-    c[~live] = E4M3_NAN_CODE
-    codes[live_blocks] = c
-    scales[live_blocks] = s
+    live_blocks = np.asarray(live_blocks, dtype=np.int64)
+    for i in range(0, len(live_blocks), chunk):
+        ids = live_blocks[i: i + chunk]
+        x = torch.from_numpy(cache[ids]).float()  # [n, Hkv, BS, D]
+        live = ~torch.isnan(x)
+        xz = torch.where(live, x, torch.zeros((), dtype=torch.float32))
+        amax = xz.abs().amax(dim=(2, 3))
+        s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones((), dtype=torch.float32))
+        y = (xz / s[:, :, None, None]).clamp(-E4M3_MAX, E4M3_MAX)
+        c = y.to(torch.float8_e4m3fn).view(torch.uint8)
+        c[~live] = E4M3_NAN_CODE
+        codes[ids] = c.numpy()
+        scales[ids] = s.numpy()
     return codes, scales
