@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--flushed-calls", type=int, default=50,
                     help="pa_decode calls timed one by one after evicting the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-gib", type=float, default=4.0,
+                    help="size of the streaming-read probe that measures attainable bandwidth (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     return ap.parse_args()
 
@@ -236,6 +238,24 @@ def main():
                    "p90_us": times[(9 * len(times)) // 10]}
         del fa, fb
 
+    attainable = None
+    if args.probe_gib > 0:
+        progress(f"streaming-read probe over {args.probe_gib:g} GiB")
+        buf = torch.empty(int(args.probe_gib * 2 ** 30), dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        times = []
+        for i in range(12):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.stream_read_probe(buf, sink)
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 2:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        attainable = buf.numel() / statistics.median(times) / 1e9
+        del buf
+
     kvb = kv_bytes(case)
     seq_tokens = int(case.context_lens.sum())
     value = kvb / (ms_per_step * 1e-3) / 1e9
@@ -273,6 +293,8 @@ def main():
                    "block_size": case.block_size, "kv_dtype": case.kv_dtype,
                    "step": "copy_blocks(pairs) + kv_write(1 token/seq) + decode"},
         "hbm_frac": value / HBM_PEAK_GBS,
+        "attainable_read_gbs": attainable,
+        "frac_of_attainable": None if attainable is None else value / attainable,
         "seq_tokens_per_s": seq_tokens / (ms_per_step * 1e-3),
         "kv_bytes_per_step": kvb,
         "flushed_decode": flushed,

@@ -148,6 +148,17 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
                    void* stream);
 
+/*
+ * pa_stream_read_probe — measurement utility, not part of the decode path.
+ *
+ * Reads the first floor(bytes / 16) * 16 bytes of `buf` once with 16-byte loads spread over
+ * the whole GPU, so that timing it gives the attainable HBM read bandwidth that pa_decode's
+ * KV bandwidth is compared against. `sink` (4 bytes) is written only in the rare case that
+ * the folded data equals a fixed constant; its contents are meaningless.
+ * Validated: non-NULL, bytes >= 16, buf 16-byte aligned, sink 4-byte aligned.
+ */
+int pa_stream_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

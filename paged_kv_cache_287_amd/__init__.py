@@ -3,7 +3,7 @@
 The binding only marshals arguments: it turns torch device tensors into pointers and sizes,
 passes torch's current HIP stream, and turns a non-zero status into :class:`PaError`. Every
 step of the computation runs in the library's HIP kernels; there is no fallback. Importing
-this package fails if ``libpa.so`` has not been built (``python -m paged_kv_cache_287_amd.build``).
+this package fails if ``libpa.so`` has not been built (``python paged_kv_cache_287_amd/build.py``).
 
 torch is imported first so that its HIP runtime (``libamdhip64.so.7``) is the one the library
 binds to: the library is linked without an RPATH and resolves that SONAME to the copy already
@@ -21,7 +21,7 @@ __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
     "decode_workspace_bytes", "decode_partition_tokens", "pa_decode", "pa_kv_write",
-    "pa_copy_blocks",
+    "pa_copy_blocks", "stream_read_probe",
 ]
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = {
                                  _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
 }
 
 
@@ -57,7 +58,7 @@ class PaError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_287_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_287_amd/build.py`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in EXPORTED_SYMBOLS.items():
         fn = getattr(handle, name)
@@ -186,3 +187,12 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: 
                             _kv_dtype(k_cache), _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_copy_blocks")
+
+
+def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, *, stream=None) -> None:
+    """Enqueue one streaming read of ``buf`` (attainable-bandwidth measurement utility)."""
+    if buf.device.type != "cuda" or sink.device.type != "cuda":
+        raise ValueError("probe buffers must be device tensors")
+    st = lib.pa_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_stream_read_probe")

@@ -1,6 +1,7 @@
 """Compile the HIP sources under csrc/ for gfx950 into the in-tree shared library libpa.so.
 
-Usage: ``python -m paged_kv_cache_287_amd.build`` (or ``build()`` from Python).
+Usage: ``python paged_kv_cache_287_amd/build.py`` (run by path: importing the package itself
+requires the built library), or ``build()`` from ``__graft_entry__``.
 Every call recompiles. Objects go to ``_build/`` next to this file; the library lands next to
 this file so that the binding (and anything copying the source tree) finds it.
 """
@@ -17,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "decode.hip", "cache_ops.hip"]
+SOURCES = ["pa_api.hip", "decode.hip", "cache_ops.hip", "probe.hip"]
 
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -162,4 +162,10 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                                            static_cast<hipStream_t>(stream)));
 }
 
+int pa_stream_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || !aligned(buf, 16) || !aligned(sink, 4)) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink),
+                                           static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -64,4 +64,6 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               int head_dim, int block_size, int num_blocks, int elem_bytes,
                               hipStream_t stream);
 
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace pa

@@ -118,6 +118,12 @@ def test_kv_write_rejects_bad_arguments(over, expect):
     assert pa.lib.pa_kv_write(*kvw_args(**over)) == expect
 
 
+def test_probe_rejects_bad_arguments():
+    assert pa.lib.pa_stream_read_probe(None, 1024, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert pa.lib.pa_stream_read_probe(FAKE, 8, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert pa.lib.pa_stream_read_probe(FAKE + 4, 1024, FAKE, None) == pa.PA_ERR_INVALID_ARG
+
+
 def test_zero_work_calls_return_ok_without_launching():
     assert pa.lib.pa_kv_write(*kvw_args(num_tokens=0, k=None, v=None)) == pa.PA_OK
     assert pa.lib.pa_copy_blocks(FAKE, FAKE, None, None, None, 0, 2, 128, 16, 10, 0, None) == pa.PA_OK

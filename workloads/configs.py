@@ -155,19 +155,21 @@ def random_case(seed, lens, hq, hkv, d, bs, *, kv_dtype="f16", pool_factor=1.25,
                 name="random", extra_width=0) -> DecodeCase:
     """General seeded case: independent sequences of the given lengths.
 
-    Draw order: block permutation, q, then K and V per sequence.
+    Draw order: q, then K and V per sequence, then the block permutation; the values therefore
+    do not depend on the block size or the pool size.
     """
     rng = np.random.default_rng(seed)
     lens = [int(x) for x in lens]
-    live = sum(-(-L // bs) for L in lens)
-    nb = max(int(math.ceil(pool_factor * live)), live + 1)
-    bm = BlockManager(nb, bs, free_order=rng.permutation(nb))
     q = normal_f16(rng, (len(lens), hq, d))
     lk, lv = [], []
     for L in lens:
-        bm.new_sequence(L)
         lk.append(normal_f16(rng, (L, hkv, d)))
         lv.append(normal_f16(rng, (L, hkv, d)))
+    live = sum(-(-L // bs) for L in lens)
+    nb = max(int(math.ceil(pool_factor * live)), live + 1)
+    bm = BlockManager(nb, bs, free_order=rng.permutation(nb))
+    for L in lens:
+        bm.new_sequence(L)
     case = _finish(name, seed, rng, bm, lk, lv, hq, d, kv_dtype, q=q)
     if extra_width:
         w = case.block_tables.shape[1] + extra_width
