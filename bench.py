@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--probe-gib", type=float, default=4.0,
                     help="size of the streaming-read probe that measures attainable bandwidth (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="split-context partition size passed to pa_decode (0 = library's choice)")
     return ap.parse_args()
 
 
@@ -179,26 +181,38 @@ def main():
     g_pairs, g_nk, g_nv, g_slots = dev(pairs.astype(np.int32)), dev(nk), dev(nv), dev(slots)
     out = torch.empty_like(q)
     max_ctx = int(case.context_lens.max())
-    ws_bytes = pa.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
-                                         case.block_size, max_ctx,
-                                         pa.PA_KV_F16 if case.kv_dtype == "f16" else pa.PA_KV_FP8_E4M3)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    kvt = pa.PA_KV_F16 if case.kv_dtype == "f16" else pa.PA_KV_FP8_E4M3
+    part_tokens = pa.decode_partition_tokens(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                             case.head_dim, case.block_size, max_ctx, kvt,
+                                             args.partition_tokens)
+    ws_bytes = pa.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                         case.head_dim, case.block_size, max_ctx, kvt, part_tokens)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def decode():
         pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
-                     max_context_len=max_ctx, workspace=ws)
+                     max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws)
 
-    def step(ev0=None, ev1=None):
+    def step():
         if g_pairs.shape[0]:
             pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
         if case.kv_dtype == "f16":
             pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots)
-        if ev0 is not None:
-            ev0.record(stream)
         decode()
-        if ev1 is not None:
-            ev1.record(stream)
+
+    def timed(fn, n):
+        """Wall-clock and HIP-event time of n back-to-back calls (events only at the ends:
+        an event between kernels adds a cache flush of its own)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n, e0.elapsed_time(e1) * 1e-3 / n
 
     progress(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -206,27 +220,22 @@ def main():
     torch.cuda.synchronize()
 
     progress(f"timing {args.steps} steps")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    call_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    avg_call_ms = sum(call_ms) / len(call_ms)
+    wall_step, event_step = timed(step, args.steps)
+    ms_per_step = wall_step * 1e3
+    progress(f"timing {args.steps} decode calls")
+    _, event_call = timed(decode, args.steps)
+    avg_call_ms = event_call * 1e3
 
-    # per-call timing after evicting L2 and the 256 MiB Infinity Cache with a 1 GiB copy
+    # per-call timing after evicting L2 and the 256 MiB Infinity Cache with a 1 GiB read (a
+    # read leaves no dirty lines behind whose write-back would slow the timed call)
     flushed = None
     if args.flushed_calls > 0:
         progress(f"timing {args.flushed_calls} flushed calls")
-        fa = torch.empty(256 * 2 ** 20, dtype=torch.float32, device="cuda")
-        fb = torch.empty_like(fa)
+        fa = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
+        fsink = torch.zeros(1, dtype=torch.int32, device="cuda")
         times = []
         for _ in range(args.flushed_calls):
-            fb.copy_(fa)
+            pa.stream_read_probe(fa, fsink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             decode()
@@ -236,7 +245,7 @@ def main():
         times.sort()
         flushed = {"median_us": statistics.median(times), "p10_us": times[len(times) // 10],
                    "p90_us": times[(9 * len(times)) // 10]}
-        del fa, fb
+        del fa
 
     attainable = None
     if args.probe_gib > 0:
@@ -269,7 +278,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
-                "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3}
+                "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3,
+                "timing": "HIP events around the timed back-to-back pa_decode calls"}
     cpu = None
     if not args.no_cpu_baseline:
         progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
@@ -282,6 +292,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "event_ms_per_step": event_step * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -291,7 +302,8 @@ def main():
                    "max_context_len": max_ctx, "q_heads": case.num_q_heads,
                    "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
                    "block_size": case.block_size, "kv_dtype": case.kv_dtype,
-                   "step": "copy_blocks(pairs) + kv_write(1 token/seq) + decode"},
+                   "step": "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
+                   "partition_tokens": part_tokens},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attainable_read_gbs": attainable,
         "frac_of_attainable": None if attainable is None else value / attainable,

@@ -71,13 +71,23 @@ const char* pa_status_str(int status);
 /* hipError_t value behind the most recent PA_ERR_HIP returned on the calling thread (0 if none). */
 int pa_last_hip_error(void);
 
-/* Context tokens handled by one workgroup of pa_decode (the split-context partition size). */
-int32_t pa_decode_partition_tokens(int32_t head_dim, int32_t block_size, int32_t kv_dtype);
+/*
+ * Split-context partition size pa_decode uses for this shape: context tokens handled by one
+ * workgroup. partition_tokens = 0 asks for the automatic choice (the largest power of two in
+ * [256, 4096] that still gives at least 1024 workgroups for max_context_len, i.e. four per
+ * compute unit of a 256-CU gfx950); an explicit value must be a power of two in [256, 4096]
+ * with value <= 256 * block_size. Returns 0 if the arguments are invalid.
+ */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                   int32_t kv_dtype, int32_t partition_tokens);
 
-/* Bytes of device workspace pa_decode needs for this shape; 0 if none is needed
- * (max_context_len <= one partition) or if the arguments are invalid. */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t max_context_len, int32_t kv_dtype);
+/* Bytes of device workspace pa_decode needs for these arguments (same meaning as in pa_decode;
+ * max_context_len must be the value pa_decode will see, > 0); 0 if none is needed (every
+ * sequence fits one partition) or if the arguments are invalid. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t kv_dtype, int32_t partition_tokens);
 
 /*
  * pa_decode — one query token per sequence attends over its paged KV cache.
@@ -88,16 +98,23 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *     K_b[t] = k_cache[block_tables[b, t / BS], g, t % BS, :]   (t < L, likewise V_b)
  *     out[b, h, :] = softmax(scale * K_b q[b, h]) V_b           (fp32 accumulate, fp16 out)
  * evaluated with an online softmax (running max, running sum, running output) over tiles and
- * split across context partitions that a second kernel merges exactly (talk summary,
- * FlashAttention paragraph). L = 0 gives out = 0. For E4M3 caches each value is
+ * split across context partitions of partition_tokens tokens that are merged exactly (talk
+ * summary, FlashAttention paragraph); the workgroup that finishes a sequence's last partition
+ * does the merge, so one kernel launch covers the whole call. L = 0 gives out = 0. For E4M3 caches each value is
  * decode(code) * scale[block, g] before use. context_lens counts every token to attend,
  * including one appended by this step's pa_kv_write.
  *
  *   max_context_len  host-side upper bound on context_lens[] used to size the grid;
  *                    <= 0 means max_blocks_per_seq * block_size.
+ *   partition_tokens 0 = automatic, else an explicit split size (see
+ *                    pa_decode_partition_tokens). Results are bit-identical for a given
+ *                    partition size; different sizes round differently (within tolerance).
  *   scale            softmax scale (finite), usually 1/sqrt(head_dim).
  *   workspace        >= pa_decode_workspace_bytes(...) bytes of device memory, 256-byte
- *                    aligned (may be NULL when that size is 0). Contents are scratch.
+ *                    aligned (may be NULL when that size is 0). It must be ZERO-FILLED before
+ *                    its first use; every call leaves the bytes it uses as counters at zero
+ *                    again, so one zero-fill serves any later calls that fit in it. Calls that
+ *                    share a workspace must not overlap in time (same stream, or synchronised).
  *   num_blocks       NB, the number of blocks in each cache.
  * Preconditions (not checked): 0 <= context_lens[b] <= max_context_len (as passed or implied);
  * 0 <= block_tables[b, i] < num_blocks for i < ceil(L / BS) (later entries are never read);
@@ -106,15 +123,17 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * the grid's partitions are dropped.
  * Validated: non-NULL pointers (k_scale/v_scale must be NULL for fp16 and non-NULL for E4M3),
  * 16-byte alignment of q, out, k_cache, v_cache; 4-byte alignment of the int arrays and scales;
- * positive sizes; Hq % Hkv == 0; supported head_dim, block_size and dtype; workspace size.
+ * positive sizes; Hq % Hkv == 0; supported head_dim, block_size and dtype; partition_tokens
+ * (PA_ERR_UNSUPPORTED if it is not a valid explicit size); workspace size and alignment.
  * Deterministic: results depend only on logical token positions, not on physical ids.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-              int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream);
+              int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_tokens,
+              float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes,
+              void* stream);
 
 /*
  * pa_kv_write — slot-mapped append of new keys and values.

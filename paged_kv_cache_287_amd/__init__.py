@@ -37,10 +37,10 @@ EXPORTED_SYMBOLS = {
     "pa_abi_version": (ctypes.c_int, []),
     "pa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_hip_error": (ctypes.c_int, []),
-    "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32]),
-    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
-                                 _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+                                 _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
@@ -103,24 +103,30 @@ def _kv_dtype(cache: torch.Tensor) -> int:
     raise TypeError(f"KV cache dtype {cache.dtype} is not supported")
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, block_size: int,
-                           max_context_len: int, kv_dtype: int = PA_KV_F16) -> int:
-    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size,
-                                             max_context_len, kv_dtype))
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           block_size: int, max_context_len: int, kv_dtype: int = PA_KV_F16,
+                           partition_tokens: int = 0) -> int:
+    """Workspace bytes for pa_decode (allocate zero-filled: it holds counters)."""
+    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len, kv_dtype, partition_tokens))
 
 
-def decode_partition_tokens(head_dim: int, block_size: int, kv_dtype: int = PA_KV_F16) -> int:
-    return int(lib.pa_decode_partition_tokens(head_dim, block_size, kv_dtype))
+def decode_partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            block_size: int, max_context_len: int, kv_dtype: int = PA_KV_F16,
+                            partition_tokens: int = 0) -> int:
+    return int(lib.pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, kv_dtype, partition_tokens))
 
 
 def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
               k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-              max_context_len: int = 0, workspace: Optional[torch.Tensor] = None,
-              stream=None) -> torch.Tensor:
+              max_context_len: int = 0, partition_tokens: int = 0,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Enqueue paged decode attention; writes ``out`` [S, Hq, D] fp16 and returns it.
 
-    ``workspace`` (uint8 device tensor) is allocated here when omitted and needed.
+    ``workspace`` (uint8 device tensor, zero-filled before its first use) is allocated here,
+    zero-filled, when omitted and needed.
     """
     _check(q, "q", (torch.float16,), 3)
     _check(out, "out", (torch.float16,), 3)
@@ -141,14 +147,16 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
         raise ValueError("block_tables / context_lens must have one row per sequence")
     mbps = block_tables.shape[1]
-    need = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size,
-                                  max_context_len if max_context_len > 0 else mbps * block_size, kvt)
+    need = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_context_len if max_context_len > 0 else mbps * block_size,
+                                  kvt, partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                        _ptr(block_tables), _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads,
-                       head_dim, block_size, nb, mbps, max_context_len, float(scale), kvt,
+                       head_dim, block_size, nb, mbps, max_context_len, partition_tokens,
+                       float(scale), kvt,
                        _ptr(workspace), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode")

@@ -21,11 +21,21 @@ int hip_status(hipError_t e) {
   return PA_ERR_HIP;
 }
 
-size_t workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
-  if (max_parts <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-  const size_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
-  return ml + rows * head_dim * sizeof(float);
+// Resolves the partition size (0 = automatic) and the grid's partition count; false if invalid.
+bool resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int block_size,
+                       long long max_ctx, int partition_tokens, int* part_tokens, int* max_parts) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_ctx > (1LL << 30)) return false;
+  const int group = num_q_heads / num_kv_heads;
+  const int units_per_seq = num_kv_heads * (group / pa::pick_head_tile(group));
+  const int ctx = (int)(max_ctx > 0 ? max_ctx : 1);
+  int pt = partition_tokens;
+  if (pt == 0) pt = pa::auto_part_tokens(num_seqs, units_per_seq, ctx, block_size);
+  if (!pa::valid_part_tokens(pt, block_size)) return false;
+  const long long parts = pa::ceil_div(ctx, pt);
+  if (parts > 65535) return false;
+  *part_tokens = pt;
+  *max_parts = (int)parts;
+  return true;
 }
 
 }  // namespace
@@ -47,26 +57,39 @@ const char* pa_status_str(int status) {
 
 int pa_last_hip_error(void) { return g_last_hip_error; }
 
-int32_t pa_decode_partition_tokens(int32_t head_dim, int32_t block_size, int32_t kv_dtype) {
-  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || !known_dtype(kv_dtype))
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                   int32_t kv_dtype, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || !supported_head_dim(head_dim) ||
+      !supported_block_size(block_size) || !known_dtype(kv_dtype) || max_context_len <= 0)
     return 0;
-  return pa::kPartTokens;
+  int pt = 0, parts = 0;
+  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, max_context_len,
+                         partition_tokens, &pt, &parts))
+    return 0;
+  return pt;
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t max_context_len, int32_t kv_dtype) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || !supported_head_dim(head_dim) ||
-      !supported_block_size(block_size) || !known_dtype(kv_dtype))
-    return 0;
-  return workspace_bytes(num_seqs, num_q_heads, head_dim, pa::decode_num_parts(max_context_len));
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t kv_dtype, int32_t partition_tokens) {
+  const int pt = pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            block_size, max_context_len, kv_dtype,
+                                            partition_tokens);
+  if (pt == 0) return 0;
+  const int group = num_q_heads / num_kv_heads;
+  const int hg_total = num_kv_heads * (group / pa::pick_head_tile(group));
+  return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
+                              (int)pa::ceil_div(max_context_len, pt)).total;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-              int32_t kv_dtype, void* workspace, size_t workspace_bytes_given, void* stream) {
+              int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_tokens,
+              float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes_given,
+              void* stream) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -87,10 +110,16 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                                                 : (long long)max_blocks_per_seq * block_size;
   if (max_ctx > (long long)max_blocks_per_seq * block_size || max_ctx > (1LL << 30))
     return PA_ERR_INVALID_ARG;
-  const int max_parts = pa::decode_num_parts((int)max_ctx);
-  if (max_parts > 65535) return PA_ERR_INVALID_ARG;
-  const size_t need = workspace_bytes(num_seqs, num_q_heads, head_dim, max_parts);
-  if (need > 0 && (workspace == nullptr || workspace_bytes_given < need || !aligned(workspace, 256)))
+  int part_tokens = 0, max_parts = 0;
+  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, max_ctx,
+                         partition_tokens, &part_tokens, &max_parts))
+    return partition_tokens != 0 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  const int gt = pa::pick_head_tile(group);
+  const pa::WorkspaceLayout ws =
+      pa::workspace_layout(num_seqs, num_q_heads, num_kv_heads * (group / gt), head_dim, max_parts);
+  if (ws.total > 0 &&
+      (workspace == nullptr || workspace_bytes_given < ws.total || !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
 
   pa::DecodeParams p{};
@@ -102,19 +131,18 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   p.v_scale = v_scale;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-  p.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
-  p.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             (rows * 2 * sizeof(float) + 255) / 256 * 256)
-                  : nullptr;
+  char* wsb = static_cast<char*>(workspace);
+  p.counters = ws.total ? reinterpret_cast<int32_t*>(wsb + ws.counters_off) : nullptr;
+  p.ws_ml = ws.total ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
+  p.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc_off) : nullptr;
+  p.part_tokens = part_tokens;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_blocks = num_blocks;
   p.max_parts = max_parts;
-  p.group = num_q_heads / num_kv_heads;
-  const int gt = pa::pick_head_tile(p.group);
-  p.head_groups = p.group / gt;
+  p.group = group;
+  p.head_groups = group / gt;
   p.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8,
                                       static_cast<hipStream_t>(stream)));

@@ -9,17 +9,66 @@ namespace pa {
 
 // ---- decode geometry -------------------------------------------------------------------
 // A workgroup of kWaves wavefronts owns one (sequence, KV-head group, context partition) and
-// processes kPartTokens consecutive logical tokens; each wave owns kWaveTokens of them and walks
-// them in tiles of kTileTokens (four 16-lane rows x four steps of one token per row).
+// processes `part_tokens` consecutive logical tokens; each wave owns a quarter of them and walks
+// them in tiles of kTileTokens (four 16-lane rows x four steps of one token per row). The block
+// ids of a wave's tokens are held one per lane, so a wave may span at most kWave blocks:
+// part_tokens / kWaves <= kWave * block_size.
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRows = 4;
 constexpr int kSteps = 4;
 constexpr int kTileTokens = kRows * kSteps;
-constexpr int kPartTokens = 512;
-constexpr int kWaveTokens = kPartTokens / kWaves;
-constexpr int kTilesPerWave = kWaveTokens / kTileTokens;
+constexpr int kMinPartTokens = 256;
+constexpr int kMaxPartTokens = 4096;
+// Compute units of an MI355X / MI350X (gfx950): the automatic partition choice aims to give the
+// grid enough workgroups to fill them.
+constexpr int kNumCUs = 256;
+
+inline bool valid_part_tokens(int pt, int block_size) {
+  if (pt < kMinPartTokens || pt > kMaxPartTokens || (pt & (pt - 1)) != 0) return false;
+  return pt / kWaves <= kWave * block_size;
+}
+
+// Largest compiled query-head tile (GT) dividing the group size G.
+inline int pick_head_tile(int group) {
+  for (int gt : {8, 4, 2, 1})
+    if (group % gt == 0) return gt;
+  return 1;
+}
+
+inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Automatic split-context partition size: the largest power of two in [256, 4096] whose grid
+// still has at least kTargetUnits workgroups for the given upper bound on context length.
+// Longer partitions amortise each workgroup's start-up (q, table and first-tile latency) and
+// its merge; shorter ones give more parallelism and a shorter tail when lengths are uneven.
+constexpr long long kTargetUnits = 4LL * kNumCUs;
+inline int auto_part_tokens(int num_seqs, int units_per_seq, int max_context_len, int block_size) {
+  for (int pt = kMaxPartTokens; pt > kMinPartTokens; pt /= 2) {
+    if (!valid_part_tokens(pt, block_size)) continue;
+    const long long units = (long long)num_seqs * units_per_seq * ceil_div(max_context_len, pt);
+    if (units >= kTargetUnits) return pt;
+  }
+  return kMinPartTokens;
+}
+
+// Workspace layout: [counters: S * HG_total int32][ml: S*Hq*P*2 f32][acc: S*Hq*P*D f32], each
+// section 256-byte aligned. Needed only when a sequence may span more than one partition.
+struct WorkspaceLayout {
+  size_t counters_off, ml_off, acc_off, total;
+};
+inline WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_groups_total,
+                                        int head_dim, int max_parts) {
+  WorkspaceLayout w{0, 0, 0, 0};
+  if (max_parts <= 1) return w;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  w.ml_off = up((size_t)num_seqs * head_groups_total * sizeof(int32_t));
+  w.acc_off = w.ml_off + up(rows * 2 * sizeof(float));
+  w.total = w.acc_off + rows * head_dim * sizeof(float);
+  return w;
+}
 
 struct DecodeParams {
   _Float16* out;
@@ -30,28 +79,19 @@ struct DecodeParams {
   const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_ml;   // [S, Hq, max_parts, 2] (running max in log2 units, running sum)
-  float* ws_acc;  // [S, Hq, max_parts, D] unnormalised weighted value sums
+  int32_t* counters;  // [S, HG_total] arrival counters; zero before and after every call
+  float* ws_ml;       // [S, Hq, max_parts, 2] (running max in log2 units, running sum)
+  float* ws_acc;      // [S, Hq, max_parts, D] unnormalised weighted value sums
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
   int32_t num_blocks;
   int32_t max_parts;
+  int32_t part_tokens;  // tokens per workgroup (power of two, 256..4096)
   int32_t group;        // G = Hq / Hkv
   int32_t head_groups;  // G / GT workgroups per KV head
   float scale_log2;     // softmax scale * log2(e)
 };
-
-// Largest compiled query-head tile (GT) dividing the group size G.
-inline int pick_head_tile(int group) {
-  for (int gt : {8, 4, 2, 1})
-    if (group % gt == 0) return gt;
-  return 1;
-}
-
-inline int decode_num_parts(int max_context_len) {
-  return max_context_len <= 0 ? 1 : (max_context_len + kPartTokens - 1) / kPartTokens;
-}
 
 // Launchers: return hipSuccess or the launch error. Arguments are already validated.
 hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
@@ -63,7 +103,6 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               const int32_t* block_mapping, int num_pairs, int num_kv_heads,
                               int head_dim, int block_size, int num_blocks, int elem_bytes,
                               hipStream_t stream);
-
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace pa

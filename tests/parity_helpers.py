@@ -52,7 +52,8 @@ def case_to_device(case):
                 v_scale=dev(case.v_scale))
 
 
-def gpu_decode(d, scale, *, block_tables=None, context_lens=None, max_context_len=0) -> torch.Tensor:
+def gpu_decode(d, scale, *, block_tables=None, context_lens=None, max_context_len=0,
+               partition_tokens=0) -> torch.Tensor:
     import paged_kv_cache_287_amd as pa
 
     q = d["q"]
@@ -60,7 +61,8 @@ def gpu_decode(d, scale, *, block_tables=None, context_lens=None, max_context_le
     pa.pa_decode(out, q, d["k_cache"], d["v_cache"],
                  d["block_tables"] if block_tables is None else block_tables,
                  d["context_lens"] if context_lens is None else context_lens, float(scale),
-                 k_scale=d["k_scale"], v_scale=d["v_scale"], max_context_len=max_context_len)
+                 k_scale=d["k_scale"], v_scale=d["v_scale"], max_context_len=max_context_len,
+                 partition_tokens=partition_tokens)
     return out
 
 

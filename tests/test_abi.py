@@ -48,23 +48,34 @@ def test_abi_version_and_status_strings():
     assert pa.lib.pa_status_str(99) == b"unknown status"
 
 
-def test_workspace_and_partition_queries():
-    part = pa.decode_partition_tokens(128, 16)
-    assert part == 512
-    assert pa.decode_workspace_bytes(64, 32, 128, 16, part) == 0  # one partition: none needed
+def test_partition_choice_and_workspace_size():
+    # 8B-shaped: 64 seqs x 8 KV heads x ceil(4096 / 2048) = 1024 workgroups >= 4 per CU
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096) == 2048
+    # few sequences: smaller partitions for parallelism, down to 256
+    assert pa.decode_partition_tokens(1, 32, 8, 128, 16, 4096) == 256
+    assert pa.decode_partition_tokens(4, 32, 8, 128, 16, 32768) == 1024
+    # block size 8 caps a partition at 8 * 64 * 4 = 2048 tokens
+    assert pa.decode_partition_tokens(512, 32, 8, 128, 8, 8192) == 2048
+    # explicit sizes are validated
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096, 0, 512) == 512
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096, 0, 768) == 0
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 8, 4096, 0, 4096) == 0
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096, 7, 0) == 0
+    # one partition: no workspace
+    assert pa.decode_workspace_bytes(64, 32, 8, 128, 16, 512, 0, 512) == 0
+    # counters (64 seqs x 8 head groups) + (m, l) + values, 256-byte aligned sections
     rows = 64 * 32 * 8
-    ml = (rows * 8 + 255) // 256 * 256
-    assert pa.decode_workspace_bytes(64, 32, 128, 16, 4096) == ml + rows * 128 * 4
-    assert pa.decode_workspace_bytes(64, 32, 96, 16, 4096) == 0  # unsupported head_dim
-    assert pa.decode_workspace_bytes(64, 32, 128, 12, 4096) == 0  # unsupported block size
-    assert pa.decode_partition_tokens(128, 16, 7) == 0
+    expect = (64 * 8 * 4 + 255) // 256 * 256 + (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    assert pa.decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0, 512) == expect
+    assert pa.decode_workspace_bytes(64, 32, 8, 96, 16, 4096) == 0  # unsupported head_dim
+    assert pa.decode_workspace_bytes(64, 32, 8, 128, 12, 4096) == 0  # unsupported block size
 
 
 def decode_args(**over):
     a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
              block_tables=FAKE, context_lens=FAKE, num_seqs=4, num_q_heads=8, num_kv_heads=2,
              head_dim=128, block_size=16, num_blocks=10, max_blocks_per_seq=4, max_context_len=0,
-             scale=0.125,
+             partition_tokens=0, scale=0.125,
              kv_dtype=0, workspace=None, workspace_bytes=0, stream=None)
     a.update(over)
     return list(a.values())
@@ -88,9 +99,12 @@ def decode_args(**over):
     (dict(context_lens=FAKE + 2), pa.PA_ERR_INVALID_ARG),
     (dict(max_context_len=65), pa.PA_ERR_INVALID_ARG),  # longer than the table allows
     (dict(num_seqs=70000), pa.PA_ERR_INVALID_ARG),
-    (dict(max_blocks_per_seq=64), pa.PA_ERR_WORKSPACE),  # 1024 tokens -> 2 partitions
+    (dict(max_blocks_per_seq=64), pa.PA_ERR_WORKSPACE),  # 1024 tokens -> 4 partitions of 256
     (dict(max_blocks_per_seq=64, workspace=FAKE, workspace_bytes=10), pa.PA_ERR_WORKSPACE),
     (dict(max_blocks_per_seq=64, workspace=FAKE + 16, workspace_bytes=1 << 30), pa.PA_ERR_WORKSPACE),
+    (dict(partition_tokens=300), pa.PA_ERR_UNSUPPORTED),
+    (dict(partition_tokens=8192), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8, partition_tokens=4096), pa.PA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments(over, expect):
     assert pa.lib.pa_decode(*decode_args(**over)) == expect
