@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--probe-gib", type=float, default=4.0,
                     help="size of the streaming-read probe that measures attainable bandwidth (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy three times: a kernel of "
+                         "known traffic that hardware byte counters are scaled against")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="split-context partition size passed to pa_decode (0 = library's choice)")
     return ap.parse_args()
@@ -213,6 +216,15 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / n, e0.elapsed_time(e1) * 1e-3 / n
+
+    if args.calibrate:
+        progress("calibration copy: 3 x 256 MiB read + 256 MiB written")
+        src = torch.ones(2 ** 28, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     progress(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
