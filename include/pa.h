@@ -73,10 +73,11 @@ int pa_last_hip_error(void);
 
 /*
  * Split-context partition size pa_decode uses for this shape: context tokens handled by one
- * workgroup. partition_tokens = 0 asks for the automatic choice (the largest power of two in
- * [256, 4096] that still gives at least 1024 workgroups for max_context_len, i.e. four per
- * compute unit of a 256-CU gfx950); an explicit value must be a power of two in [256, 4096]
- * with value <= 256 * block_size. Returns 0 if the arguments are invalid.
+ * workgroup. partition_tokens = 0 asks for the automatic choice: the largest power of two in
+ * [256, 4096], at most max_context_len / 2, that still gives at least 1024 workgroups for
+ * max_context_len (four per compute unit of a 256-CU gfx950), else 256. An explicit value must
+ * be a power of two in [256, 4096] with value <= 256 * block_size. Returns 0 if the arguments
+ * are invalid.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -118,7 +119,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   num_blocks       NB, the number of blocks in each cache.
  * Preconditions (not checked): 0 <= context_lens[b] <= max_context_len (as passed or implied);
  * 0 <= block_tables[b, i] < num_blocks for i < ceil(L / BS) (later entries are never read);
- * attended E4M3 codes are not NaN; out does not alias any input. Violations give wrong values
+ * out does not alias any input. Violations give wrong values
  * but no access outside the buffers: block ids are clamped into [0, num_blocks), tokens beyond
  * the grid's partitions are dropped.
  * Validated: non-NULL pointers (k_scale/v_scale must be NULL for fp16 and non-NULL for E4M3),

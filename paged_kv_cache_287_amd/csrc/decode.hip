@@ -71,11 +71,12 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// Two E4M3 codes held in bits [7:0] and [23:16] -> two fp16 holding decode(code) * 2^-8,
-// exactly: the 7 magnitude bits land on the fp16 exponent/mantissa fields (E4M3 subnormals map
-// onto fp16 subnormals), the sign bit moves to bit 15.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_div256(uint32_t x) {
-  return ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
+// Two OCP E4M3 codes (bytes 0-1, or 2-3 with hi) -> two fp16, exactly: every E4M3 value,
+// subnormals included, is representable in fp16, and the NaN code decodes to NaN. gfx950's
+// conversion uses the OCP encoding (checked against the format's definition for all 256 codes).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
 // Partials of one partition are read by whichever workgroup finishes a sequence last, possibly on
@@ -127,11 +128,8 @@ __device__ __forceinline__ void to_half_pairs(const Chunk<(KV8 ? E : 2 * E) / 4>
   } else {
 #pragma unroll
     for (int i = 0; i < E / 4; ++i) {
-      const uint32_t w = c.w[i];
-      const uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8);
-      const uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u);
-      h[2 * i] = e4m3x2_to_f16x2_div256(lo);
-      h[2 * i + 1] = e4m3x2_to_f16x2_div256(hi);
+      h[2 * i] = e4m3x2_to_f16x2<false>(c.w[i]);
+      h[2 * i + 1] = e4m3x2_to_f16x2<true>(c.w[i]);
     }
   }
 }
@@ -228,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
       if constexpr (KV8) {
         const int t = kTileTokens * i + kRows * s;
         const int id = __builtin_amdgcn_readlane(my_id, t / BS);
-        kmul[s] *= 256.f * p.k_scale[(size_t)id * p.num_kv_heads + kvh];
-        vmul[s] = 256.f * p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+        kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
+        vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
       }
       uint32_t kh[NH2];
       to_half_pairs<E, KV8>(kc[s], kh);
@@ -393,14 +391,34 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.max_parts;
     const float* ml = p.ws_ml + row0 * 2;
     const float* ac = p.ws_acc + row0 * D + d;
-    float mx = kNegInf;
-    for (int i = 0; i < nparts; ++i) mx = fmaxf(mx, fetch(ml + 2 * i));
-    float ls = 0.f, a = 0.f;
-    for (int i = 0; i < nparts; ++i) {
-      const float m_i = fetch(ml + 2 * i);
-      const float w = fexp2(m_i - mx);
-      ls = fmaf(w, fetch(ml + 2 * i + 1), ls);
-      a = fmaf(w, fetch(ac + (size_t)i * D), a);
+    // partitions are taken kChunk at a time with all their loads in flight together, merged
+    // into a running (max, sum, value) exactly as the tiles were
+    constexpr int kChunk = 8;
+    float mx = kNegInf, ls = 0.f, a = 0.f;
+    for (int i0 = 0; i0 < nparts; i0 += kChunk) {
+      float mv[kChunk], lv[kChunk], av[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const bool in = i0 + j < nparts;
+        const int i = in ? i0 + j : i0;
+        mv[j] = fetch(ml + 2 * i);
+        lv[j] = fetch(ml + 2 * i + 1);
+        av[j] = fetch(ac + (size_t)i * D);
+        if (!in) mv[j] = kNegInf;
+      }
+      float mc = mx;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
+      const float r = fexp2(mx - mc);  // mx = -inf only before the first chunk: r = 0
+      ls *= r;
+      a *= r;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const float w = fexp2(mv[j] - mc);
+        ls = fmaf(w, lv[j], ls);
+        a = fmaf(w, av[j], a);
+      }
+      mx = mc;
     }
     p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(a / ls);
   }

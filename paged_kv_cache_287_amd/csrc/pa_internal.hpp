@@ -39,14 +39,16 @@ inline int pick_head_tile(int group) {
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Automatic split-context partition size: the largest power of two in [256, 4096] whose grid
-// still has at least kTargetUnits workgroups for the given upper bound on context length.
-// Longer partitions amortise each workgroup's start-up (q, table and first-tile latency) and
-// its merge; shorter ones give more parallelism and a shorter tail when lengths are uneven.
+// Automatic split-context partition size: the largest power of two in [256, 4096], and at most
+// half the longest context, whose grid still has at least kTargetUnits workgroups; if none has,
+// the smallest. Longer partitions amortise each workgroup's start-up (q, table and first-tile
+// latency) and its merge; shorter ones give more parallelism and a shorter tail when lengths are
+// uneven, and splitting the longest sequences at least in two keeps one workgroup from holding
+// a whole long sequence while the rest of the GPU idles.
 constexpr long long kTargetUnits = 4LL * kNumCUs;
 inline int auto_part_tokens(int num_seqs, int units_per_seq, int max_context_len, int block_size) {
   for (int pt = kMaxPartTokens; pt > kMinPartTokens; pt /= 2) {
-    if (!valid_part_tokens(pt, block_size)) continue;
+    if (!valid_part_tokens(pt, block_size) || 2LL * pt > max_context_len) continue;
     const long long units = (long long)num_seqs * units_per_seq * ceil_div(max_context_len, pt);
     if (units >= kTargetUnits) return pt;
   }

@@ -51,11 +51,14 @@ def test_abi_version_and_status_strings():
 def test_partition_choice_and_workspace_size():
     # 8B-shaped: 64 seqs x 8 KV heads x ceil(4096 / 2048) = 1024 workgroups >= 4 per CU
     assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096) == 2048
+    # at most half the longest context: 2048-token contexts split at least in two
+    assert pa.decode_partition_tokens(64, 32, 32, 128, 16, 2048) == 1024
+    assert pa.decode_partition_tokens(100, 32, 8, 128, 16, 1409) == 512
     # few sequences: smaller partitions for parallelism, down to 256
     assert pa.decode_partition_tokens(1, 32, 8, 128, 16, 4096) == 256
     assert pa.decode_partition_tokens(4, 32, 8, 128, 16, 32768) == 1024
     # block size 8 caps a partition at 8 * 64 * 4 = 2048 tokens
-    assert pa.decode_partition_tokens(512, 32, 8, 128, 8, 8192) == 2048
+    assert pa.decode_partition_tokens(512, 32, 8, 128, 8, 16384) == 2048
     # explicit sizes are validated
     assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096, 0, 512) == 512
     assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096, 0, 768) == 0
