@@ -110,3 +110,52 @@ def test_fork_copy_on_write_step_and_isolation():
                        context_lens=dev(st.pre_context_lens))
     torch.cuda.synchronize()
     assert (bits(before) == bits(after)).all()
+
+
+def test_step_captured_in_a_graph_replays_exactly():
+    """copy -> write -> decode captured once and replayed several times, with eager work and
+    synchronisations in between; every replay matches the eager step bit for bit (the decode
+    counters reset themselves, nothing in the step clears memory)."""
+    import paged_kv_cache_287_amd as pa
+
+    case = gen(workloads.shared_prefix, True)
+    st = case.step
+    d = case_to_device(case)
+    pairs, nk, nv, slots = (dev(st.block_mapping.reshape(-1, 2)), dev(st.new_k), dev(st.new_v),
+                            dev(st.slot_mapping))
+    max_ctx = int(case.context_lens.max())
+    need = pa.decode_workspace_bytes(case.num_seqs, 32, 8, 128, 16, max_ctx, 0, 256)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+
+    def step():
+        pa.pa_copy_blocks(d["k_cache"], d["v_cache"], pairs)
+        pa.pa_kv_write(nk, nv, d["k_cache"], d["v_cache"], slots)
+        pa.pa_decode(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                     float(case.scale), max_context_len=max_ctx, partition_tokens=256, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_attention_close(eager, oracle_decode(case, k_cache=_expected_pool(case)[0],
+                                                v_cache=_expected_pool(case)[1]), "eager step")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert (bits(out) == bits(eager)).all(), f"replay {i} differs from the eager step"
+        step()  # and an eager step in between
+        torch.cuda.synchronize()
+        assert (bits(out) == bits(eager)).all()
+    counters = ws[: case.num_seqs * 8 * 4].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
