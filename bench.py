@@ -203,8 +203,7 @@ def main():
     def step():
         if g_pairs.shape[0]:
             pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
-        if case.kv_dtype == "f16":
-            pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots)
+        pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
         decode()
 
     def timed(fn, n):

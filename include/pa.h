@@ -142,16 +142,26 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * For each token t < num_tokens with slot = slot_mapping[t] >= 0, writes
  *     k_cache[slot / BS, h, slot % BS, :] = k[t, h, :]   and the same for v, for all h.
  * Tokens with a negative slot, or a slot >= num_blocks * block_size, are skipped. Nothing else
- * in the caches changes.
- * Supports PA_KV_F16 caches only (E4M3 append returns PA_ERR_UNSUPPORTED).
- * Precondition (not checked): non-negative slots are distinct.
- * Validated: pointers, 16-byte alignment of k, v, caches; 8-byte alignment of slot_mapping;
- * sizes; num_blocks * block_size < 2^31.
+ * in the caches changes (except, for E4M3, the earlier codes of a block whose scale grows).
+ *
+ * PA_KV_FP8_E4M3 caches (k_scale, v_scale non-NULL) are written under this scale policy, per
+ * (token, KV head), all in fp32 with IEEE division:
+ *     s_prev = scale[blk, h], or 0 when the token lands at offset 0 (the block starts fresh);
+ *     a = max |x| over the token's row; s = a / 448 if a > s_prev * 448, else s = s_prev;
+ *     s = 1 if it is still 0; when s grows and the block already holds tokens, each earlier
+ *     code c of that (block, head) becomes enc((dec(c) * s_prev) / s); the token is stored as
+ *     enc(x / s) and scale[blk, h] = s. enc clamps to [-448, 448] and rounds to nearest even.
+ * The scale thus stays >= the block's max |value| / 448, the rule used to quantize whole blocks.
+ *
+ * Precondition (not checked): non-negative slots are distinct; for E4M3 caches at most one
+ * token per block per call (one decode step appends one token per sequence).
+ * Validated: pointers (scales NULL for fp16, non-NULL for E4M3), 16-byte alignment of k, v,
+ * caches; 8-byte alignment of slot_mapping; sizes; num_blocks * block_size < 2^31.
  */
-int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
-                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
-                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
-                void* stream);
+int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache, float* k_scale,
+                float* v_scale, const int64_t* slot_mapping, int32_t num_tokens,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t kv_dtype, void* stream);
 
 /*
  * pa_copy_blocks — copy-on-write block copies.

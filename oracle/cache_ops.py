@@ -15,6 +15,10 @@ from typing import Optional, Tuple
 
 import numpy as np
 
+from .fp8 import E4M3_TABLE, float_to_e4m3
+
+E4M3_MAX = np.float32(448.0)
+
 
 def kv_write(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
              slot_mapping: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
@@ -45,4 +49,46 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_mapping: np.ndar
             ks[dst] = k_scale[src]
         if vs is not None:
             vs[dst] = v_scale[src]
+    return kc, vc, ks, vs
+
+
+def kv_write_fp8(k: np.ndarray, v: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray,
+                 k_scale: np.ndarray, v_scale: np.ndarray, slot_mapping: np.ndarray):
+    """Slot-mapped append into an E4M3 cache with one fp32 scale per (block, KV head).
+
+    The pages give no scale policy for appending to an 8-bit cache; the one computed here keeps
+    each scale an upper bound of its block's content over 448, the rule the input quantizer
+    uses. For each token (at most one per block per call) and KV head, all in float32:
+
+    * ``s_prev`` = the block's scale, or 0 when the token lands at offset 0 (a fresh block);
+    * ``a`` = max |x| over the token's row; ``s = a / 448`` if ``a > s_prev * 448``, else
+      ``s = s_prev``; a fresh all-zero row gets ``s = 1``;
+    * if ``s`` changed and the block already holds tokens, each stored code ``c`` at offsets
+      before the token is re-encoded as ``enc(f32(f32(dec(c) * s_prev) / s))``;
+    * the token itself is stored as ``enc(f32(x) / s)``; ``enc`` clamps to [-448, 448] and rounds
+      to nearest-even (:func:`oracle.fp8.float_to_e4m3`).
+
+    Returns new ``(k_codes, v_codes, k_scale, v_scale)``.
+    """
+    kc, vc = k_codes.copy(), v_codes.copy()
+    ks, vs = k_scale.copy(), v_scale.copy()
+    bs = kc.shape[2]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        blk, off = int(slot // bs), int(slot % bs)
+        for codes, scales, rows in ((kc, ks, k), (vc, vs, v)):
+            for h in range(codes.shape[1]):
+                x = np.asarray(rows[t, h], dtype=np.float16).astype(np.float32)
+                s_prev = np.float32(0.0) if off == 0 else np.float32(scales[blk, h])
+                a = np.float32(np.max(np.abs(x)))
+                s = np.float32(a / E4M3_MAX) if a > np.float32(s_prev * E4M3_MAX) else s_prev
+                if s == 0:
+                    s = np.float32(1.0)
+                if s != s_prev and off > 0:
+                    old = E4M3_TABLE[codes[blk, h, :off]].astype(np.float32)
+                    y = (old * s_prev).astype(np.float32) / s
+                    codes[blk, h, :off] = float_to_e4m3(np.clip(y, -E4M3_MAX, E4M3_MAX))
+                codes[blk, h, off] = float_to_e4m3(np.clip(x / s, -E4M3_MAX, E4M3_MAX))
+                scales[blk, h] = s
     return kc, vc, ks, vs

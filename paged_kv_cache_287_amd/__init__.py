@@ -41,7 +41,8 @@ EXPORTED_SYMBOLS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
-    "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _p]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
 }
@@ -164,18 +165,27 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
 
 
 def pa_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                slot_mapping: torch.Tensor, *, stream=None) -> None:
-    """Enqueue the slot-mapped append of new K/V rows [T, Hkv, D] into the caches."""
+                slot_mapping: torch.Tensor, *, k_scale: Optional[torch.Tensor] = None,
+                v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue the slot-mapped append of new K/V rows [T, Hkv, D] into the caches (E4M3 caches
+    need their per-(block, head) scales, which the append updates)."""
     _check(k, "k", (torch.float16,), 3)
     _check(v, "v", (torch.float16,), 3)
     _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
     _check(v_cache, "v_cache", (k_cache.dtype,), 4)
     _check(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    kvt = _kv_dtype(k_cache)
+    if kvt == PA_KV_FP8_E4M3:
+        for n, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{n} is required for an 8-bit cache")
+            _check(s, n, (torch.float32,), 2)
     nb, hkv, bs, d = k_cache.shape
     if k.shape != v.shape or k.shape[1:] != (hkv, d) or slot_mapping.shape[0] != k.shape[0]:
         raise ValueError("shape mismatch between k, v, slot_mapping and the caches")
-    st = lib.pa_kv_write(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
-                         k.shape[0], hkv, d, bs, nb, _kv_dtype(k_cache), _stream(stream))
+    st = lib.pa_kv_write(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                         _ptr(v_scale), _ptr(slot_mapping), k.shape[0], hkv, d, bs, nb, kvt,
+                         _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_kv_write")
 

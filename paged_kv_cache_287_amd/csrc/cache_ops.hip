@@ -40,6 +40,83 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint4* __restrict__
   v_cache[dst] = v[src];
 }
 
+// ---- append into an 8-bit (OCP E4M3) cache --------------------------------------------------
+// The pages say only that the KV cache may be kept in 8 bits ("serving-paged-attention", section
+// "실무에서 만지는 지점"). Each (block, KV head) carries one fp32 scale; the append keeps it an
+// upper bound of the block's content over 448:
+//   s_prev = scale[blk, h], or 0 when the token is the block's first (offset 0);
+//   a = max |x| over the token's row; s = a / 448 if a > s_prev * 448 else s_prev; s = 1 if 0;
+//   if s changed and earlier tokens exist, their codes c become enc((dec(c) * s_prev) / s);
+//   the token is stored as enc(x / s); enc clamps to +-448 and rounds to nearest-even.
+// All arithmetic is fp32 with IEEE division. At most one token per block per call (a decode
+// step appends one token per sequence, and sequences never write into a shared block).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float e4m3_max() { return 448.f; }
+
+// Clamp two floats to the E4M3 range and convert them, round-to-nearest-even, into bytes 0-1
+// (HI = false) or 2-3 (HI = true) of `old`.
+template <bool HI>
+__device__ __forceinline__ uint32_t enc_pair(float a, float b, uint32_t old) {
+  a = fminf(fmaxf(a, -e4m3_max()), e4m3_max());
+  b = fminf(fmaxf(b, -e4m3_max()), e4m3_max());
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void kv_write_fp8_kernel(
+    const _Float16* __restrict__ k, const _Float16* __restrict__ v, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
+    const int64_t* __restrict__ slot_mapping, int num_kv_heads, int block_size, int64_t num_slots) {
+  constexpr int PER = D / 64;  // elements per lane: 2 (D 128) or 1 (D 64)
+  const int t = blockIdx.x / num_kv_heads;
+  const int h = blockIdx.x - t * num_kv_heads;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot - blk * block_size);
+  const int lane = threadIdx.x;
+  for (int which = 0; which < 2; ++which) {
+    const _Float16* row = (which == 0 ? k : v) + ((size_t)t * num_kv_heads + h) * D;
+    uint8_t* tile = (which == 0 ? k_cache : v_cache) + ((size_t)blk * num_kv_heads + h) * block_size * D;
+    float* sc = (which == 0 ? k_scale : v_scale) + (size_t)blk * num_kv_heads + h;
+    float x[PER];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      x[e] = (float)row[lane * PER + e];
+      amax = fmaxf(amax, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float s_prev = off == 0 ? 0.f : *sc;
+    float s = amax > s_prev * e4m3_max() ? amax / e4m3_max() : s_prev;
+    if (s == 0.f) s = 1.f;
+    if (s != s_prev && off > 0) {
+      // re-encode the codes already in the block, four per lane per step
+      uint32_t* words = reinterpret_cast<uint32_t*>(tile);
+      const int nwords = off * D / 4;
+      for (int i = lane; i < nwords; i += 64) {
+        const uint32_t w = words[i];
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+        uint32_t o = enc_pair<false>((lo.x * s_prev) / s, (lo.y * s_prev) / s, 0u);
+        o = enc_pair<true>((hi.x * s_prev) / s, (hi.y * s_prev) / s, o);
+        words[i] = o;
+      }
+    }
+    uint8_t* dst = tile + (size_t)off * D + lane * PER;
+    if constexpr (PER == 2) {
+      const uint32_t o = enc_pair<false>(x[0] / s, x[1] / s, 0u);
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(o & 0xFFFFu);
+    } else {
+      const uint32_t o = enc_pair<false>(x[0] / s, 0.f, 0u);
+      *dst = (uint8_t)(o & 0xFFu);
+    }
+    if (lane == 0) *sc = s;
+  }
+}
+
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, float* __restrict__ k_scale,
     float* __restrict__ v_scale, const int32_t* __restrict__ block_mapping, int num_kv_heads,
@@ -76,6 +153,25 @@ hipError_t launch_kv_write(const void* k, const void* v, void* k_cache, void* v_
       static_cast<const uint4*>(k), static_cast<const uint4*>(v), static_cast<uint4*>(k_cache),
       static_cast<uint4*>(v_cache), slot_mapping, num_rows, num_kv_heads, chunks_per_row,
       block_size, (int64_t)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                               float* k_scale, float* v_scale, const int64_t* slot_mapping,
+                               int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, hipStream_t stream) {
+  const int grid = num_tokens * num_kv_heads;
+  const int64_t slots = (int64_t)num_blocks * block_size;
+  auto kk = static_cast<const _Float16*>(k);
+  auto vv = static_cast<const _Float16*>(v);
+  auto kc = static_cast<uint8_t*>(k_cache);
+  auto vc = static_cast<uint8_t*>(v_cache);
+  if (head_dim == 128)
+    kv_write_fp8_kernel<128><<<grid, 64, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
+                                                      slot_mapping, num_kv_heads, block_size, slots);
+  else
+    kv_write_fp8_kernel<64><<<grid, 64, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
+                                                     slot_mapping, num_kv_heads, block_size, slots);
   return hipGetLastError();
 }
 

@@ -148,22 +148,28 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                                       static_cast<hipStream_t>(stream)));
 }
 
-int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
-                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
-                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
-                void* stream) {
+int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache, float* k_scale,
+                float* v_scale, const int64_t* slot_mapping, int32_t num_tokens,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t kv_dtype, void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
   if (!known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
-  if (kv_dtype != PA_KV_F16) return PA_ERR_UNSUPPORTED;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const bool fp8 = kv_dtype == PA_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return PA_ERR_INVALID_ARG;
   if ((long long)num_blocks * block_size >= (1LL << 31)) return PA_ERR_INVALID_ARG;
   if ((long long)num_tokens * num_kv_heads * (head_dim * 2 / 16) >= (1LL << 31))
     return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(slot_mapping, 8))
+      !aligned(slot_mapping, 8) || (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
     return PA_ERR_INVALID_ARG;
+  if (fp8)
+    return hip_status(pa::launch_kv_write_fp8(k, v, k_cache, v_cache, k_scale, v_scale,
+                                              slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                              block_size, num_blocks,
+                                              static_cast<hipStream_t>(stream)));
   return hip_status(pa::launch_kv_write(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                         num_kv_heads, head_dim, block_size, num_blocks,
                                         static_cast<hipStream_t>(stream)));

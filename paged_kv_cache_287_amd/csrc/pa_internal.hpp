@@ -101,6 +101,10 @@ hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int 
 hipError_t launch_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                            int head_dim, int block_size, int num_blocks, hipStream_t stream);
+hipError_t launch_kv_write_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                               float* k_scale, float* v_scale, const int64_t* slot_mapping,
+                               int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* block_mapping, int num_pairs, int num_kv_heads,
                               int head_dim, int block_size, int num_blocks, int elem_bytes,

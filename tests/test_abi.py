@@ -114,7 +114,8 @@ def test_decode_rejects_bad_arguments(over, expect):
 
 
 def kvw_args(**over):
-    a = dict(k=FAKE, v=FAKE, k_cache=FAKE, v_cache=FAKE, slot_mapping=FAKE, num_tokens=3,
+    a = dict(k=FAKE, v=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
+             slot_mapping=FAKE, num_tokens=3,
              num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10, kv_dtype=0, stream=None)
     a.update(over)
     return list(a.values())
@@ -126,7 +127,9 @@ def kvw_args(**over):
     (dict(num_tokens=-1), pa.PA_ERR_INVALID_ARG),
     (dict(num_blocks=0), pa.PA_ERR_INVALID_ARG),
     (dict(head_dim=80), pa.PA_ERR_UNSUPPORTED),
-    (dict(kv_dtype=1), pa.PA_ERR_UNSUPPORTED),  # E4M3 append is not provided
+    (dict(kv_dtype=1), pa.PA_ERR_INVALID_ARG),  # E4M3 append without scales
+    (dict(k_scale=FAKE, v_scale=FAKE), pa.PA_ERR_INVALID_ARG),  # fp16 append with scales
+    (dict(kv_dtype=1, k_scale=FAKE + 2, v_scale=FAKE), pa.PA_ERR_INVALID_ARG),  # misaligned scale
     (dict(num_blocks=1 << 28), pa.PA_ERR_INVALID_ARG),  # num_blocks * BS >= 2^31
     (dict(slot_mapping=FAKE + 4), pa.PA_ERR_INVALID_ARG),
     (dict(v_cache=FAKE + 8), pa.PA_ERR_INVALID_ARG),

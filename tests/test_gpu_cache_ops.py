@@ -159,3 +159,70 @@ def test_step_captured_in_a_graph_replays_exactly():
         assert (bits(out) == bits(eager)).all()
     counters = ws[: case.num_seqs * 8 * 4].view(torch.int32)
     assert int(counters.abs().sum()) == 0
+
+
+def _fp8_append_case(seed=600, num_seqs=12, hkv=4, d=128, bs=16):
+    """An E4M3 pool built by the tile quantizer, then appends: one token per sequence per step,
+    some rows scaled up so blocks must rescale, some steps opening fresh blocks."""
+    lens = np.random.default_rng(seed).integers(1, 60, size=num_seqs)
+    case = workloads.random_case(seed, lens, 2 * hkv, hkv, d, bs, kv_dtype="fp8_e4m3", pool_factor=3.0)
+    return case
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_append_bit_exact_over_pool_then_decode(d):
+    import paged_kv_cache_287_amd as pa
+
+    case = _fp8_append_case(d=d)
+    bm = workloads.BlockManager(case.num_blocks, case.block_size)
+    # rebuild the manager state from the case (tables, lengths), marking used blocks
+    bm._free = [b for b in range(case.num_blocks)
+                if b not in set(int(x) for row, L in zip(case.block_tables, case.context_lens)
+                                for x in row[: -(-int(L) // case.block_size)]) and b != case.pad_block][::-1]
+    for row, L in zip(case.block_tables, case.context_lens):
+        n = -(-int(L) // case.block_size)
+        bm.tables.append([int(x) for x in row[:n]])
+        bm.lens.append(int(L))
+        bm.refcount[row[:n]] = 1
+    kc, vc, ks, vs = case.k_cache.copy(), case.v_cache.copy(), case.k_scale.copy(), case.v_scale.copy()
+    gk, gv, gks, gvs = dev(kc), dev(vc), dev(ks), dev(vs)
+    rng = np.random.default_rng(601)
+    for step in range(20):
+        plan = bm.append_tokens(range(case.num_seqs))
+        grow = rng.choice([1.0, 1.0, 1.0, 6.0], size=(case.num_seqs, 1, 1))
+        nk = (rng.standard_normal((case.num_seqs, case.num_kv_heads, d)) * grow).astype(np.float16)
+        nv = (rng.standard_normal((case.num_seqs, case.num_kv_heads, d)) * grow).astype(np.float16)
+        kc, vc, ks, vs = oracle.kv_write_fp8(nk, nv, kc, vc, ks, vs, plan.slot_mapping)
+        pa.pa_kv_write(dev(nk), dev(nv), gk, gv, dev(plan.slot_mapping), k_scale=gks, v_scale=gvs)
+        torch.cuda.synchronize()
+        assert (bits(gk) == kc).all() and (bits(gv) == vc).all(), f"codes differ at step {step}"
+        assert (bits(gks) == host_bits(ks)).all() and (bits(gvs) == host_bits(vs)).all(), f"scales, step {step}"
+    log(f"[fp8 append] D={d}: 20 steps bit-exact")
+    tables = bm.block_tables(width=case.block_tables.shape[1] + 4, pad_id=case.pad_block)
+    lens = bm.context_lens()
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale, kv_dtype="fp8_e4m3", k_scale=ks, v_scale=vs)
+    out = torch.full_like(dev(case.q), float("nan"))
+    pa.pa_decode(out, dev(case.q), gk, gv, dev(tables), dev(lens), float(case.scale), k_scale=gks, v_scale=gvs)
+    torch.cuda.synchronize()
+    assert_attention_close(out, ref, f"decode after fp8 appends, D={d}")
+
+
+def test_fp8_append_rounds_ties_to_even():
+    import paged_kv_cache_287_amd as pa
+
+    # one fresh block per KV head-row: amax 448 gives scale 1, so x / s = x and every value is
+    # an exact midpoint between two E4M3 neighbours (representable in fp16)
+    vals = oracle.E4M3_TABLE[:0x7F]
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float16)
+    row = np.concatenate([[448.0], mids[:63], -mids[63:126]]).astype(np.float16)  # 1 + 63 + 63 = 127
+    row = np.concatenate([row, [-448.0]]).astype(np.float16)[:128]
+    k = np.stack([row, row[::-1]])[:, None, :].astype(np.float16)  # [T=2, Hkv=1, D=128]
+    kc = np.zeros((4, 1, 16, 128), np.uint8)
+    ks = np.zeros((4, 1), np.float32)
+    slots = np.array([0, 16], np.int64)
+    ek, ev, eks, evs = oracle.kv_write_fp8(k, k, kc, kc.copy(), ks, ks.copy(), slots)
+    gk, gv, gks, gvs = dev(kc), dev(kc.copy()), dev(ks), dev(ks.copy())
+    pa.pa_kv_write(dev(k), dev(k), gk, gv, dev(slots), k_scale=gks, v_scale=gvs)
+    torch.cuda.synchronize()
+    assert float(eks[0, 0]) == 1.0
+    assert (bits(gk) == ek).all() and (bits(gv) == ev).all()

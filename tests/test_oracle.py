@@ -359,3 +359,86 @@ def test_paged_waste_bound_from_pages():
     assert -(-ex["tokens"] // ex["slots_per_page"]) == ex["pages"]
     assert oracle.paged_waste_slots(ex["tokens"], ex["slots_per_page"]) == ex["idle_slots_without_sharing"]
     assert facts["default_block_size"]["tokens"] == 16
+
+
+# ------------------------------------------------------------------------------------------
+# E4M3 encoding and the 8-bit append policy
+# ------------------------------------------------------------------------------------------
+def test_e4m3_encoder_matches_torch_including_ties():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(50000) * 60, rng.standard_normal(20000) * 0.02,
+                        [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11]])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    vals = oracle.E4M3_TABLE[:0x7F]
+    ties = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    for arr in (x, ties, -ties):
+        ref = torch.from_numpy(arr).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(oracle.float_to_e4m3(arr), ref)
+    # round trip of every finite code
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(oracle.float_to_e4m3(oracle.e4m3_to_float(codes).astype(np.float32)), codes)
+
+
+def _fp8_pool(nb=8, hkv=2, bs=16, d=64):
+    codes = np.full((nb, hkv, bs, d), 0x7F, dtype=np.uint8)
+    scales = np.full((nb, hkv), np.nan, dtype=np.float32)
+    return codes, codes.copy(), scales, scales.copy()
+
+
+def test_fp8_append_first_token_equals_tile_quantizer():
+    rng = np.random.default_rng(8)
+    kc, vc, ks, vs = _fp8_pool()
+    k = (rng.standard_normal((1, 2, 64)) * 3).astype(np.float16)
+    v = rng.standard_normal((1, 2, 64)).astype(np.float16)
+    kc2, vc2, ks2, vs2 = oracle.kv_write_fp8(k, v, kc, vc, ks, vs, np.array([3 * 16], np.int64))
+    for h in range(2):
+        codes, s = workloads.quantize_tile(k[0, h])
+        assert np.array_equal(kc2[3, h, 0], codes) and ks2[3, h] == s
+        codes, s = workloads.quantize_tile(v[0, h])
+        assert np.array_equal(vc2[3, h, 0], codes) and vs2[3, h] == s
+    assert np.array_equal(kc2[[0, 1, 2, 4, 5, 6, 7]], kc[[0, 1, 2, 4, 5, 6, 7]])
+
+
+def test_fp8_append_without_growth_equals_whole_block_quantization():
+    # the largest token first: later appends never rescale, and the block equals quantizing
+    # the whole block at once with the same amax / 448 rule
+    rng = np.random.default_rng(9)
+    kc, vc, ks, vs = _fp8_pool()
+    rows = rng.standard_normal((10, 2, 64)).astype(np.float32)
+    rows[0] *= 8
+    rows = rows.astype(np.float16)
+    for t in range(10):
+        prev = kc.copy()
+        kc, vc, ks, vs = oracle.kv_write_fp8(rows[t:t + 1], rows[t:t + 1], kc, vc, ks, vs,
+                                             np.array([5 * 16 + t], np.int64))
+        assert np.array_equal(kc[5, :, :t], prev[5, :, :t])  # earlier codes untouched
+    for h in range(2):
+        codes, s = workloads.quantize_tile(rows[:, h])
+        assert np.array_equal(kc[5, h, :10], codes) and ks[5, h] == s
+
+
+def test_fp8_append_growth_rescales_and_keeps_the_bound():
+    # Each stored value is rounded once when written and once more every time its block's
+    # scale grows afterwards; one E4M3 rounding errs by at most 2^-4 of the value (normal
+    # range) or 2^-10 of the scale (subnormal range).
+    rng = np.random.default_rng(10)
+    kc, vc, ks, vs = _fp8_pool()
+    ks[2] = 1e30  # a stale scale from an earlier use of the block is ignored at offset 0
+    rows = (rng.standard_normal((16, 2, 64)) * np.geomspace(0.01, 50, 16)[:, None, None]).astype(np.float16)
+    rescales = np.zeros((16, 2), dtype=np.int64)  # later rescales seen by each stored token
+    for t in range(16):
+        before = ks[2].copy()
+        kc, vc, ks, vs = oracle.kv_write_fp8(rows[t:t + 1], rows[t:t + 1], kc, vc, ks, vs,
+                                             np.array([2 * 16 + t], np.int64))
+        if t > 0:
+            rescales[:t] += (ks[2] != before)[None, :]
+        x = rows[: t + 1].astype(np.float64)  # [t+1, 2, 64]
+        for h in range(2):
+            amax = np.abs(x[:, h]).max()
+            assert ks[2, h] >= np.float32(amax / 448) * (1 - 1e-7)
+            back = oracle.e4m3_to_float(kc[2, h, : t + 1]) * ks[2, h]
+            err = np.abs(back - x[:, h])
+            n = (1 + rescales[: t + 1, h])[:, None]
+            assert (err <= n * (2.0 ** -4 * 1.1 * np.abs(x[:, h]) + 2.0 ** -10 * ks[2, h])).all()
+    assert rescales.max() >= 5  # the growth did force repeated re-encoding
+    assert ks[2, 0] == np.float32(np.float32(np.abs(rows[:, 0].astype(np.float32)).max()) / np.float32(448))
