@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--probe-gib", type=float, default=4.0,
                     help="size of the streaming-read probe that measures attainable bandwidth (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--swap-blocks", type=int, default=1024,
+                    help="blocks swapped out to pinned host memory and back for the swap figure (0 = skip)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a captured HIP graph instead of launching it eagerly "
                          "(measured slower on MI355X: the graph adds a fence between its nodes)")
@@ -303,6 +305,39 @@ def main():
         attainable = buf.numel() / statistics.median(times) / 1e9
         del buf
 
+    swap = None
+    if args.swap_blocks > 0:
+        n = min(args.swap_blocks, case.num_blocks)
+        progress(f"swap of {n} blocks to pinned host memory and back")
+        hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=kc.dtype).pin_memory()
+        hv = torch.empty_like(hk).pin_memory()
+        hks = hvs = None
+        if ks is not None:
+            hks = torch.empty((n, case.num_kv_heads), dtype=torch.float32).pin_memory()
+            hvs = torch.empty_like(hks).pin_memory()
+        live = np.unique(np.concatenate([row[: -(-int(L) // case.block_size)]
+                                         for row, L in zip(case.block_tables, case.context_lens)]))
+        ids = torch.from_numpy(np.ascontiguousarray(live[:n])).int().cuda()
+        n = int(ids.numel())
+        out_map = torch.stack([ids, torch.arange(n, dtype=torch.int32, device="cuda")], 1).contiguous()
+        in_map = torch.stack([out_map[:, 1], out_map[:, 0]], 1).contiguous()
+        nbytes = 2 * n * int(np.prod(kc.shape[1:])) * kc.element_size()
+
+        def swap_out():
+            pa.pa_swap_blocks(kc, vc, hk, hv, out_map, src_k_scale=ks, src_v_scale=vs,
+                              dst_k_scale=hks, dst_v_scale=hvs)
+
+        def swap_in():
+            pa.pa_swap_blocks(hk, hv, kc, vc, in_map, src_k_scale=hks, src_v_scale=hvs,
+                              dst_k_scale=ks, dst_v_scale=vs)
+
+        swap_out(); swap_in()
+        t_out = timed(swap_out, 5)[1]
+        t_in = timed(swap_in, 5)[1]
+        swap = {"blocks": n, "bytes": nbytes, "out_gbs": nbytes / t_out / 1e9,
+                "in_gbs": nbytes / t_in / 1e9, "host": "pinned (hipHostMalloc via torch)"}
+        del hk, hv
+
     kvb = kv_bytes(case)
     seq_tokens = int(case.context_lens.sum())
     value = kvb / (ms_per_step * 1e-3) / 1e9
@@ -350,6 +385,7 @@ def main():
         "seq_tokens_per_s": seq_tokens / (ms_per_step * 1e-3),
         "kv_bytes_per_step": kvb,
         "flushed_decode": flushed,
+        "swap": swap,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -179,6 +179,31 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    void* stream);
 
 /*
+ * pa_swap_blocks — move whole blocks between two pools, e.g. out of the device pool into a
+ * pinned host pool and back (preemption by swap: "serving-paged-attention", section
+ * "그래도 넘칠 때 — 선점": a request's blocks go to CPU memory and return later, trading PCIe
+ * time for the recomputation).
+ *
+ * For each pair p with (src, dst) = block_mapping[p]: dst_k[dst] = src_k[src] and
+ * dst_v[dst] = src_v[src] over all KV heads (a block is Hkv*BS*D elements), and for E4M3 pools
+ * dst_*_scale[dst, :] = src_*_scale[src, :]. src ids index the source pool (src_num_blocks
+ * blocks), dst ids the destination pool (dst_num_blocks blocks); pairs with an id out of range
+ * are skipped. Either pool may be device memory or pinned host memory allocated with
+ * hipHostMalloc (reachable from the device through its host pointer); block_mapping is device
+ * memory. Both pools share Hkv, BS, D and dtype.
+ * Precondition (not checked): destinations are distinct and, when both pools are the same
+ * buffer, disjoint from the sources.
+ * Validated: pointers (all four scale pointers NULL for fp16, non-NULL for E4M3), 16-byte
+ * alignment of the pools, sizes, num_kv_heads <= 256.
+ */
+int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
+                   const float* src_v_scale, void* dst_k, void* dst_v, float* dst_k_scale,
+                   float* dst_v_scale, const int32_t* block_mapping, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t src_num_blocks, int32_t dst_num_blocks, int32_t kv_dtype,
+                   void* stream);
+
+/*
  * pa_stream_read_probe — measurement utility, not part of the decode path.
  *
  * Reads the first floor(bytes / 16) * 16 bytes of `buf` once with 16-byte loads spread over

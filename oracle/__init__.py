@@ -8,8 +8,8 @@ imports nothing from it.
 Modules:
 
 * :mod:`oracle.attention` — decode attention read through block tables (fp16 or E4M3 KV);
-* :mod:`oracle.cache_ops` — slot-mapped KV append (fp16, and E4M3 with its scale policy) and
-  copy-on-write block copies;
+* :mod:`oracle.cache_ops` — slot-mapped KV append (fp16, and E4M3 with its scale policy),
+  copy-on-write block copies and block swaps between pools;
 * :mod:`oracle.fp8` — OCP E4M3 decoding and round-to-nearest-even encoding from the format's
   definition;
 * :mod:`oracle.capacity` — the pages' KV-size and waste arithmetic.
@@ -19,7 +19,7 @@ printed numbers, closed forms, torch's independent attention routine, brute forc
 inputs, invariants). No function here is "parity unpinned".
 """
 from .attention import decode, gather_sequence  # noqa: F401
-from .cache_ops import copy_blocks, kv_write, kv_write_fp8  # noqa: F401
+from .cache_ops import copy_blocks, kv_write, kv_write_fp8, swap_blocks  # noqa: F401
 from .capacity import (  # noqa: F401
     kv_cache_bytes,
     max_concurrent_requests,

@@ -52,6 +52,23 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_mapping: np.ndar
     return kc, vc, ks, vs
 
 
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                block_mapping: np.ndarray, src_scales=None, dst_scales=None):
+    """Preemption by swap moves whole blocks to another pool and back ("serving-paged-
+    attention", section "그래도 넘칠 때 — 선점"): ``dst[d] = src[s]`` for every (s, d) pair,
+    with the per-(block, head) scales of an 8-bit pool. Returns new ``(dst_k, dst_v, dst_scales)``
+    (``dst_scales`` a (k, v) pair or None)."""
+    dk, dv = dst_k.copy(), dst_v.copy()
+    ds = None if dst_scales is None else (dst_scales[0].copy(), dst_scales[1].copy())
+    for s, d in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        dk[d] = src_k[s]
+        dv[d] = src_v[s]
+        if ds is not None:
+            ds[0][d] = src_scales[0][s]
+            ds[1][d] = src_scales[1][s]
+    return dk, dv, ds
+
+
 def kv_write_fp8(k: np.ndarray, v: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray,
                  k_scale: np.ndarray, v_scale: np.ndarray, slot_mapping: np.ndarray):
     """Slot-mapped append into an E4M3 cache with one fp32 scale per (block, KV head).

@@ -21,7 +21,7 @@ __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
     "decode_workspace_bytes", "decode_partition_tokens", "pa_decode", "pa_kv_write",
-    "pa_copy_blocks", "stream_read_probe",
+    "pa_copy_blocks", "pa_swap_blocks", "stream_read_probe",
 ]
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
@@ -44,6 +44,8 @@ EXPORTED_SYMBOLS = {
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "pa_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _p]),
     "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
 }
 
@@ -205,6 +207,33 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: 
                             _kv_dtype(k_cache), _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_copy_blocks")
+
+
+def pa_swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
+                   dst_v: torch.Tensor, block_mapping: torch.Tensor, *,
+                   src_k_scale: Optional[torch.Tensor] = None, src_v_scale: Optional[torch.Tensor] = None,
+                   dst_k_scale: Optional[torch.Tensor] = None, dst_v_scale: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Enqueue whole-block copies between two pools [NB, Hkv, BS, D] (device tensors, or pinned
+    host tensors made with ``pin_memory=True``) for every (src, dst) row of ``block_mapping``."""
+    for n, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous [NB, Hkv, BS, D] tensor")
+        if t.device.type != "cuda" and not t.is_pinned():
+            raise ValueError(f"{n} must be device memory or pinned host memory")
+        if t.dtype != src_k.dtype:
+            raise TypeError("all pools must share one dtype")
+    _check(block_mapping, "block_mapping", (torch.int32,), 2)
+    nb_s, hkv, bs, d = src_k.shape
+    nb_d = dst_k.shape[0]
+    if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape or dst_k.shape[1:] != src_k.shape[1:]:
+        raise ValueError("pool shapes differ")
+    st = lib.pa_swap_blocks(_ptr(src_k), _ptr(src_v), _ptr(src_k_scale), _ptr(src_v_scale),
+                            _ptr(dst_k), _ptr(dst_v), _ptr(dst_k_scale), _ptr(dst_v_scale),
+                            _ptr(block_mapping), block_mapping.shape[0], hkv, d, bs, nb_s, nb_d,
+                            _kv_dtype(src_k), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_swap_blocks")
 
 
 def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, *, stream=None) -> None:

@@ -140,7 +140,49 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
+// Swap of whole blocks between two pools (device memory, or pinned host memory mapped into the
+// device's address space): preemption by swap moves a request's blocks to host memory and later
+// back ("serving-paged-attention", section "그래도 넘칠 때 — 선점"). In the [NB, Hkv, BS, D]
+// layout a block of all KV heads is one contiguous run, so a workgroup per pair streams it
+// with 16-byte loads and stores; the per-(block, head) scales of an 8-bit cache move with it.
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v,
+    const float* __restrict__ src_ks, const float* __restrict__ src_vs, uint4* __restrict__ dst_k,
+    uint4* __restrict__ dst_v, float* __restrict__ dst_ks, float* __restrict__ dst_vs,
+    const int32_t* __restrict__ block_mapping, int num_kv_heads, int chunks_per_block,
+    int src_blocks, int dst_blocks) {
+  const int pair = blockIdx.x;
+  const int src = block_mapping[2 * pair];
+  const int dst = block_mapping[2 * pair + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;  // out of range: skipped
+  const size_t s0 = (size_t)src * chunks_per_block;
+  const size_t d0 = (size_t)dst * chunks_per_block;
+  for (int c = threadIdx.x; c < chunks_per_block; c += kCopyThreads) {
+    const uint4 kv = src_k[s0 + c];
+    const uint4 vv = src_v[s0 + c];
+    dst_k[d0 + c] = kv;
+    dst_v[d0 + c] = vv;
+  }
+  if (src_ks != nullptr && (int)threadIdx.x < num_kv_heads) {
+    dst_ks[(size_t)dst * num_kv_heads + threadIdx.x] = src_ks[(size_t)src * num_kv_heads + threadIdx.x];
+    dst_vs[(size_t)dst * num_kv_heads + threadIdx.x] = src_vs[(size_t)src * num_kv_heads + threadIdx.x];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, const float* src_ks,
+                              const float* src_vs, void* dst_k, void* dst_v, float* dst_ks,
+                              float* dst_vs, const int32_t* block_mapping, int num_pairs,
+                              int num_kv_heads, int head_dim, int block_size, int src_blocks,
+                              int dst_blocks, int elem_bytes, hipStream_t stream) {
+  const int chunks = num_kv_heads * block_size * head_dim * elem_bytes / 16;
+  swap_blocks_kernel<<<num_pairs, kCopyThreads, 0, stream>>>(
+      static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v), src_ks, src_vs,
+      static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), dst_ks, dst_vs, block_mapping,
+      num_kv_heads, chunks, src_blocks, dst_blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

@@ -196,6 +196,37 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                                            static_cast<hipStream_t>(stream)));
 }
 
+int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
+                   const float* src_v_scale, void* dst_k, void* dst_v, float* dst_k_scale,
+                   float* dst_v_scale, const int32_t* block_mapping, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t src_num_blocks, int32_t dst_num_blocks, int32_t kv_dtype,
+                   void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > pa::kThreads) return PA_ERR_UNSUPPORTED;
+  const bool fp8 = kv_dtype == PA_KV_FP8_E4M3;
+  const bool scales[4] = {src_k_scale != nullptr, src_v_scale != nullptr, dst_k_scale != nullptr,
+                          dst_v_scale != nullptr};
+  for (bool s : scales)
+    if (s != fp8) return PA_ERR_INVALID_ARG;
+  const long long block_bytes = (long long)num_kv_heads * block_size * head_dim * (fp8 ? 1 : 2);
+  if ((long long)src_num_blocks * block_bytes / 16 >= (1LL << 40) || block_bytes / 16 >= (1LL << 31))
+    return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) ||
+      !aligned(block_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_swap_blocks(src_k, src_v, src_k_scale, src_v_scale, dst_k, dst_v,
+                                           dst_k_scale, dst_v_scale, block_mapping, num_pairs,
+                                           num_kv_heads, head_dim, block_size, src_num_blocks,
+                                           dst_num_blocks, fp8 ? 1 : 2,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int pa_stream_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
   if (!buf || !sink || bytes < 16 || !aligned(buf, 16) || !aligned(sink, 4)) return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink),

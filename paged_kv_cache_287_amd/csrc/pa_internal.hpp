@@ -109,6 +109,11 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               const int32_t* block_mapping, int num_pairs, int num_kv_heads,
                               int head_dim, int block_size, int num_blocks, int elem_bytes,
                               hipStream_t stream);
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, const float* src_ks,
+                              const float* src_vs, void* dst_k, void* dst_v, float* dst_ks,
+                              float* dst_vs, const int32_t* block_mapping, int num_pairs,
+                              int num_kv_heads, int head_dim, int block_size, int src_blocks,
+                              int dst_blocks, int elem_bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace pa

@@ -170,3 +170,27 @@ def test_binding_rejects_host_tensors_before_calling_the_library():
         pa.pa_decode(q.clone(), q, torch.zeros(4, 2, 16, 128, dtype=torch.float16),
                      torch.zeros(4, 2, 16, 128, dtype=torch.float16),
                      torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32), 0.1)
+
+
+def swap_args(**over):
+    a = dict(src_k=FAKE, src_v=FAKE, src_ks=None, src_vs=None, dst_k=FAKE, dst_v=FAKE, dst_ks=None,
+             dst_vs=None, block_mapping=FAKE, num_pairs=2, num_kv_heads=8, head_dim=128,
+             block_size=16, src_num_blocks=10, dst_num_blocks=20, kv_dtype=0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(src_k=None), pa.PA_ERR_INVALID_ARG),
+    (dict(block_mapping=None), pa.PA_ERR_INVALID_ARG),
+    (dict(num_pairs=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(dst_num_blocks=0), pa.PA_ERR_INVALID_ARG),
+    (dict(head_dim=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=512), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1), pa.PA_ERR_INVALID_ARG),  # E4M3 without scales
+    (dict(kv_dtype=1, src_ks=FAKE, src_vs=FAKE, dst_ks=FAKE), pa.PA_ERR_INVALID_ARG),  # one missing
+    (dict(dst_k=FAKE + 8), pa.PA_ERR_INVALID_ARG),
+])
+def test_swap_rejects_bad_arguments(over, expect):
+    assert pa.lib.pa_swap_blocks(*swap_args(**over)) == expect
+    assert pa.lib.pa_swap_blocks(*swap_args(num_pairs=0, block_mapping=None)) == pa.PA_OK

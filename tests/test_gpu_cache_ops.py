@@ -226,3 +226,50 @@ def test_fp8_append_rounds_ties_to_even():
     torch.cuda.synchronize()
     assert float(eks[0, 0]) == 1.0
     assert (bits(gk) == ek).all() and (bits(gv) == ev).all()
+
+
+@pytest.mark.parametrize("kv_dtype", ["f16", "fp8_e4m3"])
+def test_swap_out_to_pinned_host_and_back(kv_dtype):
+    import paged_kv_cache_287_amd as pa
+
+    case = workloads.random_case(700, [300, 1000, 77, 513], 32, 8, 128, 16, kv_dtype=kv_dtype,
+                                 pool_factor=3.0)
+    d = case_to_device(case)
+    before = gpu_decode(d, case.scale, partition_tokens=256)
+    # swap out every block of sequences 1 and 3 into a pinned host pool
+    seqs = [1, 3]
+    ids = np.concatenate([case.block_tables[b, : -(-int(case.context_lens[b]) // 16)] for b in seqs])
+    n = len(ids)
+    shape = (n,) + case.k_cache.shape[1:]
+    tdt = torch.float16 if kv_dtype == "f16" else torch.uint8
+    hk = torch.zeros(shape, dtype=tdt).pin_memory()
+    hv = torch.zeros(shape, dtype=tdt).pin_memory()
+    hks = hvs = None
+    if kv_dtype != "f16":
+        hks = torch.zeros((n, case.num_kv_heads), dtype=torch.float32).pin_memory()
+        hvs = torch.zeros_like(hks).pin_memory()
+    out_map = np.stack([ids, np.arange(n)], 1).astype(np.int32)
+    log(f"[swap] {kv_dtype}: {n} blocks out to pinned host memory")
+    pa.pa_swap_blocks(d["k_cache"], d["v_cache"], hk, hv, dev(out_map), src_k_scale=d["k_scale"],
+                      src_v_scale=d["v_scale"], dst_k_scale=hks, dst_v_scale=hvs)
+    torch.cuda.synchronize()
+    assert (bits(hk) == host_bits(case.k_cache[ids])).all()
+    assert (bits(hv) == host_bits(case.v_cache[ids])).all()
+    if hks is not None:
+        assert (bits(hks) == host_bits(case.k_scale[ids])).all()
+    # clobber the old device blocks, swap back in at fresh ids, re-point the tables
+    d["k_cache"][torch.from_numpy(ids).long().cuda()] = 0
+    used = set(int(x) for r, L in zip(case.block_tables, case.context_lens) for x in r[: -(-int(L) // 16)])
+    free = np.array([i for i in range(case.num_blocks) if i not in used and i != case.pad_block][:n])
+    in_map = np.stack([np.arange(n), free], 1).astype(np.int32)
+    pa.pa_swap_blocks(hk, hv, d["k_cache"], d["v_cache"], dev(in_map), src_k_scale=hks, src_v_scale=hvs,
+                      dst_k_scale=d["k_scale"], dst_v_scale=d["v_scale"])
+    tables = case.block_tables.copy()
+    pos = 0
+    for b in seqs:
+        nb_ = -(-int(case.context_lens[b]) // 16)
+        tables[b, :nb_] = free[pos: pos + nb_]
+        pos += nb_
+    after = gpu_decode(d, case.scale, block_tables=dev(tables), partition_tokens=256)
+    torch.cuda.synchronize()
+    assert (bits(after) == bits(before)).all()

@@ -442,3 +442,26 @@ def test_fp8_append_growth_rescales_and_keeps_the_bound():
             assert (err <= n * (2.0 ** -4 * 1.1 * np.abs(x[:, h]) + 2.0 ** -10 * ks[2, h])).all()
     assert rescales.max() >= 5  # the growth did force repeated re-encoding
     assert ks[2, 0] == np.float32(np.float32(np.abs(rows[:, 0].astype(np.float32)).max()) / np.float32(448))
+
+
+def test_swap_round_trip_restores_blocks_and_attention():
+    # swap a sequence's blocks out to a host pool, then back in at other device ids: the
+    # blocks come back bit for bit and attention through the re-pointed table is unchanged
+    case = workloads.random_case(61, [40, 130, 7], 8, 2, 64, 16, pool_factor=3.0)
+    ref = run_oracle(case)
+    b = 1
+    n = -(-int(case.context_lens[b]) // 16)
+    old_ids = case.block_tables[b, :n].copy()
+    host_k = np.zeros((n,) + case.k_cache.shape[1:], np.float16)
+    host_v = np.zeros_like(host_k)
+    hk, hv, _ = oracle.swap_blocks(case.k_cache, case.v_cache, host_k, host_v,
+                                   np.stack([old_ids, np.arange(n)], 1))
+    used = set(int(x) for r, L in zip(case.block_tables, case.context_lens) for x in r[: -(-int(L) // 16)])
+    free = [i for i in range(case.num_blocks) if i not in used and i != case.pad_block][:n]
+    kc, vc, _ = oracle.swap_blocks(hk, hv, case.k_cache, case.v_cache, np.stack([np.arange(n), free], 1))
+    for i, (o, f) in enumerate(zip(old_ids, free)):
+        assert np.array_equal(kc[f].view(np.uint16), case.k_cache[o].view(np.uint16))
+    tables = case.block_tables.copy()
+    tables[b, :n] = free
+    out = oracle.decode(case.q, kc, vc, tables, case.context_lens, case.scale)
+    assert np.array_equal(out, ref)
