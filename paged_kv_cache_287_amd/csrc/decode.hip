@@ -33,14 +33,10 @@
 //     XCD's L2.
 //   * results depend only on logical token positions (fixed tile, row and merge order), so
 //     they are deterministic and independent of physical block placement.
-#include "pa_internal.hpp"
+#include "decode_common.hpp"
 
 namespace pa {
 namespace {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -57,8 +53,6 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
                                 c, false);
@@ -69,53 +63,6 @@ __device__ __forceinline__ float half_lo(uint32_t w) {
 }
 __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
-// Two OCP E4M3 codes (bytes 0-1, or 2-3 with hi) -> two fp16, exactly: every E4M3 value,
-// subnormals included, is representable in fp16, and the NaN code decodes to NaN. gfx950's
-// conversion uses the OCP encoding (checked against the format's definition for all 256 codes).
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-}
-
-// Partials of one partition are read by whichever workgroup finishes a sequence last, possibly on
-// another XCD (each XCD has its own L2). System-scope relaxed accesses compile to write-through
-// stores and cache-bypassing loads (sc0 sc1), which keeps that exchange coherent without
-// flushing any cache.
-__device__ __forceinline__ void publish(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ float fetch(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-template <int NWORDS>
-struct Chunk {
-  uint32_t w[NWORDS];
-};
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// NT = non-temporal: KV bytes are read once per call, so they are streamed past the caches
-// (measured on MI355X: ~7.0 TB/s for a non-temporal streaming read vs ~6.3 TB/s without).
-template <int NWORDS, bool NT = false>
-__device__ __forceinline__ Chunk<NWORDS> load_chunk(const uint8_t* ptr) {
-  Chunk<NWORDS> c;
-  if constexpr (NWORDS == 4) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(ptr);
-    const u32x4 v = NT ? __builtin_nontemporal_load(p) : *p;
-    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
-  } else if constexpr (NWORDS == 2) {
-    const u32x2* p = reinterpret_cast<const u32x2*>(ptr);
-    const u32x2 v = NT ? __builtin_nontemporal_load(p) : *p;
-    c.w[0] = v.x; c.w[1] = v.y;
-  } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(ptr);
-    c.w[0] = NT ? __builtin_nontemporal_load(p) : *p;
-  }
-  return c;
 }
 
 // Per-lane view of one token's elements as fp16 pairs (E/2 words).
@@ -343,85 +290,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     }
   };
 
-  if (nparts == 1) {
-    // the whole sequence fits one partition: normalise and write the output directly
-    for (int idx = tid; idx < GT * D; idx += kThreads) {
-      const int h = idx / D, d = idx - h * D;
-      float mx, ls, a;
-      local_merge(h, d, mx, ls, a);
-      p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(ls > 0.f ? a / ls : 0.f);
-    }
-    return;
-  }
-
-  // ---- several partitions: publish this one's (max, sum, value sum) ----------------------
-  for (int idx = tid; idx < GT * D; idx += kThreads) {
-    const int h = idx / D, d = idx - h * D;
-    float mx, ls, a;
-    local_merge(h, d, mx, ls, a);
-    const size_t slot = ((size_t)b * p.num_q_heads + h0 + h) * p.max_parts + part;
-    publish(p.ws_acc + slot * D + d, a);
-    if (d == 0) {
-      publish(p.ws_ml + slot * 2, mx);
-      publish(p.ws_ml + slot * 2 + 1, ls);
-    }
-  }
-  // Count arrivals once the partial is stored. The workgroup that arrives last merges every
-  // partition of this (sequence, head group) and resets the counter to zero, so no second
-  // kernel is needed and the counters are zero again for the next call. The partials go
-  // through write-through stores and come back through cache-bypassing loads (see publish /
-  // fetch); every wave waits for its stores to complete (s_waitcnt 0) before the barrier, so
-  // the counter only moves once the whole partial is in memory. No L2 write-back or
-  // invalidation is needed (those cost far more than the merge itself).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  __shared__ int s_last;
-  if (tid == 0) {
-    int32_t* ctr = p.counters + (size_t)b * p.num_kv_heads * p.head_groups + hg;
-    const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == nparts - 1;
-    if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  // exact merge: out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p
-  for (int idx = tid; idx < GT * D; idx += kThreads) {
-    const int h = idx / D, d = idx - h * D;
-    const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.max_parts;
-    const float* ml = p.ws_ml + row0 * 2;
-    const float* ac = p.ws_acc + row0 * D + d;
-    // partitions are taken kChunk at a time with all their loads in flight together, merged
-    // into a running (max, sum, value) exactly as the tiles were
-    constexpr int kChunk = 8;
-    float mx = kNegInf, ls = 0.f, a = 0.f;
-    for (int i0 = 0; i0 < nparts; i0 += kChunk) {
-      float mv[kChunk], lv[kChunk], av[kChunk];
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        const bool in = i0 + j < nparts;
-        const int i = in ? i0 + j : i0;
-        mv[j] = fetch(ml + 2 * i);
-        lv[j] = fetch(ml + 2 * i + 1);
-        av[j] = fetch(ac + (size_t)i * D);
-        if (!in) mv[j] = kNegInf;
-      }
-      float mc = mx;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
-      const float r = fexp2(mx - mc);  // mx = -inf only before the first chunk: r = 0
-      ls *= r;
-      a *= r;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        const float w = fexp2(mv[j] - mc);
-        ls = fmaf(w, lv[j], ls);
-        a = fmaf(w, av[j], a);
-      }
-      mx = mc;
-    }
-    p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(a / ls);
-  }
+  finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, h0, local_merge);
 }
 
 template <int D, int BS, int GT, bool KV8>

@@ -1,0 +1,313 @@
+// Paged decode attention for large query groups (G >= 16 query heads per KV head, e.g. MQA)
+// on gfx950 matrix cores.
+//
+// With G query heads sharing one KV head ("LLM 추론 확장, 품질·비용 절충 필수", attention-heads
+// paragraph: MQA lets every query head share a single KV head) the per-token work is G dot
+// products against each K row and G weighted sums of each V row: 32 flop per KV byte at G = 32,
+// above what the VALU can sustain at HBM speed. Stacking the G query rows makes QK^T and PV
+// dense 16-row tiles, so they run on MFMA:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = a 16-token K tile, loaded straight from the
+//     cache in the operand layout (lane l: token l%16, 8 consecutive dims of a 32-dim step);
+//     B = the query rows, held in registers. Lane l then owns query row l%16 and the scores of
+//     tokens 4(l/16)..4(l/16)+3, so the online softmax (running max / sum per row, as in the
+//     FlashAttention paragraph of the same talk summary) needs only two cross-row exchanges.
+//   * O^T += V^T P^T with v_mfma_f32_16x16x16_f16: B = P^T is exactly the probabilities each
+//     lane just computed (converted to fp16); A = V^T comes from the V tile staged through a
+//     padded per-wave LDS buffer (V is stored dim-contiguous, the operand wants 4 tokens of one
+//     dim per lane). The accumulator lane l holds row l%16, so rescaling by the running max is
+//     lane-local.
+// Everything else (partitioning, block-id walk, double-buffered non-temporal loads, fp8 scales,
+// merge through LDS, partial publish / last-arrival merge) follows the VALU kernel.
+#include "decode_common.hpp"
+
+namespace pa {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int D, int BS, int NT, bool KV8>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int R = 16 * NT;         // query rows of one KV head handled by a workgroup
+  constexpr int KK = D / 32;         // 32-dim steps of QK
+  constexpr int MT = D / 16;         // 16-dim slices of the output
+  constexpr int ESZ = KV8 ? 1 : 2;   // bytes per cached element
+  constexpr int ROW_BYTES = D * ESZ;
+  constexpr int TILE_BYTES = BS * ROW_BYTES;
+  constexpr int LANE_BYTES = 8 * ESZ;  // 8 elements per lane per step
+  constexpr int NWORDS = LANE_BYTES / 4;
+  constexpr int VRS = D + 8;         // staged V row stride in halves: rows stay 16-byte aligned
+                                     // and the 4 token groups of a read fall on different banks
+  static_assert(BS % kRows == 0, "block size");
+
+  const int hg = blockIdx.x;
+  const int b = blockIdx.y;
+  const int part = blockIdx.z;
+  const int kvh = hg / p.head_groups;
+  const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * R;
+  const int L = p.context_lens[b];
+  const int part_tokens = p.part_tokens;
+  const int wave_tokens = part_tokens / kWaves;
+  const int nparts = min(L > 0 ? (L + part_tokens - 1) / part_tokens : 1, p.max_parts);
+  if (part >= nparts) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;  // K/V token row of a load; query row of a score
+  const int lq = lane >> 4;  // 8-element group of a 32-dim step; 4-token group of a tile
+
+  // ---- query rows as the B operand: row h0 + 16 nt + lr, dims 32 kk + 8 lq .. +8 ------------
+  h8 qb[NT][KK];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qb[nt][kk] = *reinterpret_cast<const h8*>(
+          p.q + ((size_t)b * p.num_q_heads + h0 + 16 * nt + lr) * D + 32 * kk + 8 * lq);
+
+  // ---- block ids of this wave's tokens: lane j holds logical block wbase / BS + j ------------
+  const int wbase = part * part_tokens + wave * wave_tokens;
+  const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
+  int my_id = 0;
+  if (wbase < L) {
+    const int lb = min(wbase / BS + lane, nblk - 1);
+    my_id = p.block_tables[(size_t)b * p.max_blocks_per_seq + lb];
+    my_id = min(max(my_id, 0), p.num_blocks - 1);
+  }
+  // block of token (16 i + t) of tile i: uniform for BS >= 16; for BS = 8 the tile's second
+  // half lies in the next block
+  auto block_of = [&](int i, int t) -> int {
+    const int j0 = (kTileTokens * i) / BS;
+    if constexpr (BS >= kTileTokens) {
+      return __builtin_amdgcn_readlane(my_id, j0);
+    } else {
+      const int a = __builtin_amdgcn_readlane(my_id, j0);
+      const int c = __builtin_amdgcn_readlane(my_id, j0 + 1);
+      return t >= BS ? c : a;
+    }
+  };
+
+  const uint8_t* kbase = p.k_cache + (size_t)kvh * TILE_BYTES;
+  const uint8_t* vbase = p.v_cache + (size_t)kvh * TILE_BYTES;
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE_BYTES;
+
+  float m[NT], l[NT];
+  f4 o[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = kNegInf;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // LDS: a per-wave staging tile for V, reused after the loop for the workgroup merge
+  constexpr int kMergeFloats = kWaves * R * (D + 2);
+  static_assert(kWaves * kTileTokens * VRS * 2 <= kMergeFloats * 4, "staging fits the merge area");
+  __shared__ __align__(16) float smem[kMergeFloats];
+  _Float16* vst = reinterpret_cast<_Float16*>(smem) + wave * kTileTokens * VRS;
+
+  Chunk<NWORDS> ka[KK], va[KK], kb[KK], vb[KK];
+
+  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[KK], Chunk<NWORDS>(&vc)[KK]) {
+    const int id = block_of(i, lr);
+    const size_t off = (size_t)id * blk_stride +
+                       (size_t)(((kTileTokens * i + lr) % BS) * ROW_BYTES + lq * LANE_BYTES);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kc[kk] = load_chunk<NWORDS, true>(kbase + off + kk * 32 * ESZ);
+      vc[kk] = load_chunk<NWORDS, true>(vbase + off + kk * 32 * ESZ);
+    }
+  };
+
+  // 8 elements of a chunk as fp16 (E4M3 codes decode exactly)
+  auto to_h8 = [&](const Chunk<NWORDS>& c) -> h8 {
+    uint32_t w[4];
+    if constexpr (!KV8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = c.w[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        w[2 * i] = e4m3x2_to_f16x2<false>(c.w[i]);
+        w[2 * i + 1] = e4m3x2_to_f16x2<true>(c.w[i]);
+      }
+    }
+    return __builtin_bit_cast(h8, w);
+  };
+
+  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[KK], const Chunk<NWORDS>(&vc)[KK],
+                          bool masked) {
+    const int tok0 = wbase + kTileTokens * i;
+    // per-token multipliers: softmax scale (and the K / V block scales of an E4M3 cache) for
+    // this lane's four score tokens 4 lq + ii
+    float kmul = p.scale_log2, vmul = 1.f;
+    if constexpr (KV8) {
+      const int id = block_of(i, 4 * lq);
+      kmul *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
+      vmul = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+    }
+    h8 kA[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kA[kk] = to_h8(kc[kk]);
+    h4 pB[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qb[nt][kk], s, 0, 0, 0);
+      float sc[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const bool valid = !masked || (tok0 + 4 * lq + ii < L);
+        sc[ii] = valid ? s[ii] * kmul : kNegInf;
+      }
+      // online softmax for query row 16 nt + lr across the tile's 16 tokens
+      float tm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mn = fmaxf(m[nt], tm);
+      const float ms = mn == kNegInf ? 0.f : mn;
+      const float alpha = fexp2(m[nt] - ms);
+      float pw[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) pw[ii] = fexp2(sc[ii] - ms);
+      l[nt] = l[nt] * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+      m[nt] = mn;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+      pB[nt] = h4{(_Float16)(pw[0] * vmul), (_Float16)(pw[1] * vmul), (_Float16)(pw[2] * vmul),
+                  (_Float16)(pw[3] * vmul)};
+    }
+    // stage V (token lr, dims 32 kk + 8 lq .. +8) as fp16; tokens past the context are zeros so
+    // that stale or poisoned slots cannot reach the sums
+    const bool vvalid = !masked || (tok0 + lr < L);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      h8 vv = to_h8(vc[kk]);
+      if (!vvalid) vv = h8{0, 0, 0, 0, 0, 0, 0, 0};
+      *reinterpret_cast<h8*>(vst + lr * VRS + 32 * kk + 8 * lq) = vv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // O^T[dim][row] += V^T[dim][token] P^T[token][row], 16 dims at a time
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      h4 vA;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vA[j] = vst[(4 * lq + j) * VRS + 16 * mt + lr];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vA, pB[nt], o[nt][mt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // same double-buffered walk as the VALU kernel
+  const int avail = max(0, min(L - wbase, wave_tokens));
+  const int n_full = avail / kTileTokens;
+  const bool has_tail = (avail % kTileTokens) != 0;
+  const int n_tiles = n_full + (has_tail ? 1 : 0);
+  if (n_tiles > 0) issue_tile(0, ka, va);
+  int i = 0;
+  for (; i + 1 < n_full; i += 2) {
+    issue_tile(i + 1, kb, vb);
+    consume_tile(i, ka, va, false);
+    if (i + 2 < n_tiles) issue_tile(i + 2, ka, va);
+    consume_tile(i + 1, kb, vb, false);
+  }
+  if (i < n_full) {
+    if (has_tail) issue_tile(i + 1, kb, vb);
+    consume_tile(i, ka, va, false);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      ka[kk] = kb[kk];
+      va[kk] = vb[kk];
+    }
+    ++i;
+  }
+  if (has_tail) consume_tile(i, ka, va, true);
+
+  // row sums: the four lanes of a row held partial sums over their own tokens
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    l[nt] += __shfl_xor(l[nt], 16);
+    l[nt] += __shfl_xor(l[nt], 32);
+  }
+
+  // ---- merge the kWaves waves through LDS (the staging area is reused) ----------------------
+  __syncthreads();
+  float* s_acc = smem;                              // [kWaves][R][D]
+  float* s_ml = smem + kWaves * R * D;              // [kWaves][R][2]
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = 16 * nt + lr;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        s_acc[(wave * R + row) * D + 16 * mt + 4 * lq + ii] = o[nt][mt][ii];
+    if (lq == 0) {
+      s_ml[(wave * R + row) * 2] = m[nt];
+      s_ml[(wave * R + row) * 2 + 1] = l[nt];
+    }
+  }
+  __syncthreads();
+
+  auto local_merge = [&](int h, int d, float& mx, float& ls, float& a) {
+    mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_ml[(w * R + h) * 2]);
+    const float ms = mx == kNegInf ? 0.f : mx;
+    ls = 0.f;
+    a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fexp2(s_ml[(w * R + h) * 2] - ms);
+      ls = fmaf(wt, s_ml[(w * R + h) * 2 + 1], ls);
+      a = fmaf(wt, s_acc[(w * R + h) * D + d], a);
+    }
+  };
+  finish_partition<R, D, kThreads>(p, b, hg, part, nparts, h0, local_merge);
+}
+
+template <int D, int BS, int NT, bool KV8>
+hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  const dim3 grid(p.num_kv_heads * p.head_groups, num_seqs, p.max_parts);
+  decode_mfma_kernel<D, BS, NT, KV8><<<grid, kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int D, bool KV8, int NT>
+hipError_t dispatch_bs(const DecodeParams& p, int num_seqs, int bs, hipStream_t stream) {
+  switch (bs) {
+    case 8: return launch_one<D, 8, NT, KV8>(p, num_seqs, stream);
+    case 16: return launch_one<D, 16, NT, KV8>(p, num_seqs, stream);
+    case 32: return launch_one<D, 32, NT, KV8>(p, num_seqs, stream);
+    case 64: return launch_one<D, 64, NT, KV8>(p, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool KV8>
+hipError_t dispatch_rows(const DecodeParams& p, int num_seqs, int bs, int rows, hipStream_t stream) {
+  return rows == 32 ? dispatch_bs<D, KV8, 2>(p, num_seqs, bs, stream)
+                    : dispatch_bs<D, KV8, 1>(p, num_seqs, bs, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
+                              int rows, bool kv_fp8, hipStream_t stream) {
+  if (head_dim == 128)
+    return kv_fp8 ? dispatch_rows<128, true>(p, num_seqs, block_size, rows, stream)
+                  : dispatch_rows<128, false>(p, num_seqs, block_size, rows, stream);
+  if (head_dim == 64)
+    return kv_fp8 ? dispatch_rows<64, true>(p, num_seqs, block_size, rows, stream)
+                  : dispatch_rows<64, false>(p, num_seqs, block_size, rows, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

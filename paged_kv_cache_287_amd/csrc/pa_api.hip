@@ -26,7 +26,7 @@ bool resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int bloc
                        long long max_ctx, int partition_tokens, int* part_tokens, int* max_parts) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_ctx > (1LL << 30)) return false;
   const int group = num_q_heads / num_kv_heads;
-  const int units_per_seq = num_kv_heads * (group / pa::pick_head_tile(group));
+  const int units_per_seq = num_kv_heads * (group / pa::decode_rows(group));
   const int ctx = (int)(max_ctx > 0 ? max_ctx : 1);
   int pt = partition_tokens;
   if (pt == 0) pt = pa::auto_part_tokens(num_seqs, units_per_seq, ctx, block_size);
@@ -78,7 +78,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                             partition_tokens);
   if (pt == 0) return 0;
   const int group = num_q_heads / num_kv_heads;
-  const int hg_total = num_kv_heads * (group / pa::pick_head_tile(group));
+  const int hg_total = num_kv_heads * (group / pa::decode_rows(group));
   return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
                               (int)pa::ceil_div(max_context_len, pt)).total;
 }
@@ -115,7 +115,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                          partition_tokens, &part_tokens, &max_parts))
     return partition_tokens != 0 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
-  const int gt = pa::pick_head_tile(group);
+  const int gt = pa::decode_rows(group);
   const pa::WorkspaceLayout ws =
       pa::workspace_layout(num_seqs, num_q_heads, num_kv_heads * (group / gt), head_dim, max_parts);
   if (ws.total > 0 &&
@@ -144,6 +144,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   p.group = group;
   p.head_groups = group / gt;
   p.scale_log2 = scale * 1.4426950408889634f;
+  if (pa::decode_uses_mfma(group))
+    return hip_status(pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8,
+                                             static_cast<hipStream_t>(stream)));
   return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8,
                                       static_cast<hipStream_t>(stream)));
 }

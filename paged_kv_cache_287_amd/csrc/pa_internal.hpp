@@ -30,8 +30,12 @@ inline bool valid_part_tokens(int pt, int block_size) {
   return pt / kWaves <= kWave * block_size;
 }
 
-// Largest compiled query-head tile (GT) dividing the group size G.
-inline int pick_head_tile(int group) {
+// Query heads per workgroup. Groups of 16 or more query heads per KV head (MQA-like) stack 32 or
+// 16 of them into matrix-core tiles; smaller groups use the VALU kernel with the largest
+// compiled tile (8, 4, 2 or 1) dividing G.
+inline bool decode_uses_mfma(int group) { return group >= 16 && group % 16 == 0; }
+inline int decode_rows(int group) {
+  if (decode_uses_mfma(group)) return group % 32 == 0 ? 32 : 16;
   for (int gt : {8, 4, 2, 1})
     if (group % gt == 0) return gt;
   return 1;
@@ -98,6 +102,8 @@ struct DecodeParams {
 // Launchers: return hipSuccess or the launch error. Arguments are already validated.
 hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                          int head_tile, bool kv_fp8, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
+                              int rows, bool kv_fp8, hipStream_t stream);
 hipError_t launch_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                            int head_dim, int block_size, int num_blocks, hipStream_t stream);

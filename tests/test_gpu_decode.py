@@ -63,7 +63,8 @@ def test_ragged_lengths(d, bs, kv_dtype):
     run_case(case)
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (12, 4), (16, 2), (32, 1), (64, 2), (5, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (6, 2), (12, 4), (16, 2), (32, 1), (64, 2), (5, 1),
+                                    (16, 1), (48, 1), (64, 1)])
 def test_head_groupings(hq, hkv):
     case = workloads.random_case(200 + hq, [5, 300, 777], hq, hkv, 128, 16,
                                  name=f"groups_{hq}q_{hkv}kv")
@@ -184,3 +185,23 @@ def test_workspace_reuse_leaves_counters_zero():
     assert (bits(outs[0]) == bits(outs[3])).all() and (bits(outs[1]) == bits(outs[4])).all()
     counters = ws[: case.num_seqs * 8 * 4].view(torch.int32)
     assert int(counters.abs().sum()) == 0
+
+
+# ---- matrix-core path: 16 or more query heads per KV head -------------------------------------
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 64])
+@pytest.mark.parametrize("kv_dtype", ["f16", "fp8_e4m3"])
+@pytest.mark.parametrize("hq", [16, 32])
+def test_large_groups_ragged(d, bs, kv_dtype, hq):
+    case = workloads.random_case(800 + bs + d + hq, LENS, hq, 1, d, bs, kv_dtype=kv_dtype,
+                                 name=f"mfma_g{hq}_d{d}_bs{bs}_{kv_dtype}")
+    run_case(case)
+
+
+def test_large_groups_relabelling_and_determinism():
+    case = workloads.random_case(850, LENS, 32, 1, 128, 16)
+    a = gpu_decode(case_to_device(case), case.scale)
+    b = gpu_decode(case_to_device(_relabel(case, 3)), case.scale)
+    c = gpu_decode(case_to_device(case), case.scale)
+    torch.cuda.synchronize()
+    assert (bits(a) == bits(b)).all() and (bits(a) == bits(c)).all()
