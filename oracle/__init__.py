@@ -7,7 +7,8 @@ imports nothing from it.
 
 Modules:
 
-* :mod:`oracle.attention` — decode attention read through block tables (fp16 or E4M3 KV);
+* :mod:`oracle.attention` — decode attention and causal chunk (prefill) attention read through
+  block tables (fp16 or E4M3 KV);
 * :mod:`oracle.cache_ops` — slot-mapped KV append (fp16, and E4M3 with its scale policy),
   copy-on-write block copies and block swaps between pools;
 * :mod:`oracle.fp8` — OCP E4M3 decoding and round-to-nearest-even encoding from the format's
@@ -18,7 +19,7 @@ Every function is pinned by ``-m "not gpu"`` tests to something other than itsel
 printed numbers, closed forms, torch's independent attention routine, brute force on tiny
 inputs, invariants). No function here is "parity unpinned".
 """
-from .attention import decode, gather_sequence  # noqa: F401
+from .attention import decode, gather_sequence, prefill  # noqa: F401
 from .cache_ops import copy_blocks, kv_write, kv_write_fp8, swap_blocks  # noqa: F401
 from .capacity import (  # noqa: F401
     kv_cache_bytes,

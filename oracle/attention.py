@@ -86,3 +86,37 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables
             rows = slice(kvh * g, (kvh + 1) * g)
             out[i, rows] = attend(qb[rows], kk[:, kvh, :], vv[:, kvh, :], sigma)
     return out
+
+
+def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables: np.ndarray,
+            context_lens: np.ndarray, query_start: np.ndarray, scale: float, *,
+            kv_dtype: str = "f16", k_scale: Optional[np.ndarray] = None,
+            v_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Causal attention of a chunk of new tokens per sequence over its paged cache (float64).
+
+    Prefill builds the KV cache from the prompt with large matrix products (talk summary,
+    prefill/decode paragraphs); a chunk's keys and values are appended first, then its queries
+    attend. Sequence b has ``n = query_start[b+1] - query_start[b]`` query rows in ``q`` (rows
+    ``query_start[b]`` ..) which are the last n of its ``L = context_lens[b]`` tokens: query j
+    sits at position ``L - n + j`` and attends to positions ``0 .. L - n + j``. Returns
+    ``[T, Hq, D]``; a decode step is the case n = 1.
+    """
+    total, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    g = hq // hkv
+    sigma = float(np.float32(scale))
+    out = np.zeros((total, hq, d), dtype=np.float64)
+    for b in range(len(context_lens)):
+        qs, qe = int(query_start[b]), int(query_start[b + 1])
+        n, length = qe - qs, int(context_lens[b])
+        if n == 0:
+            continue
+        kk = gather_sequence(k_cache, block_tables[b], length, kv_dtype=kv_dtype, scales=k_scale)
+        vv = gather_sequence(v_cache, block_tables[b], length, kv_dtype=kv_dtype, scales=v_scale)
+        for j in range(n):
+            pos = length - n + j
+            qj = q[qs + j].astype(np.float64)
+            for kvh in range(hkv):
+                rows = slice(kvh * g, (kvh + 1) * g)
+                out[qs + j, rows] = attend(qj[rows], kk[: pos + 1, kvh, :], vv[: pos + 1, kvh, :], sigma)
+    return out

@@ -465,3 +465,30 @@ def test_swap_round_trip_restores_blocks_and_attention():
     tables[b, :n] = free
     out = oracle.decode(case.q, kc, vc, tables, case.context_lens, case.scale)
     assert np.array_equal(out, ref)
+
+
+# ------------------------------------------------------------------------------------------
+# paged prefill (causal chunk attention)
+# ------------------------------------------------------------------------------------------
+def test_prefill_equals_causal_sdpa_and_decode_on_last_token():
+    case = workloads.random_case(71, [40, 130, 17], 8, 2, 64, 16)
+    n = [13, 130, 1]  # chunk lengths: partial, whole prompt, a single (decode) token
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    rng = np.random.default_rng(72)
+    q = rng.standard_normal((qs[-1], 8, 64)).astype(np.float16)
+    out = oracle.prefill(q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, qs,
+                         case.scale)
+    for b in range(3):
+        L = int(case.context_lens[b])
+        kt = torch.from_numpy(case.logical_k[b].astype(np.float64)).permute(1, 0, 2).repeat_interleave(4, 0)
+        vt = torch.from_numpy(case.logical_v[b].astype(np.float64)).permute(1, 0, 2).repeat_interleave(4, 0)
+        qt = torch.from_numpy(q[qs[b]:qs[b + 1]].astype(np.float64)).permute(1, 0, 2)  # [H, n, D]
+        pos = torch.arange(L - n[b], L)[:, None]
+        mask = torch.arange(L)[None, :] <= pos  # [n, L] causal with the chunk at the end
+        ref = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], attn_mask=mask,
+                                                               scale=float(np.float32(case.scale)))
+        assert np.max(np.abs(out[qs[b]:qs[b + 1]] - ref[0].permute(1, 0, 2).numpy())) < 1e-12
+    # the last query of each chunk sees the whole context: it is a decode step
+    last = q[qs[1:] - 1]
+    dec = oracle.decode(last, case.k_cache, case.v_cache, case.block_tables, case.context_lens, case.scale)
+    assert np.array_equal(out[qs[1:] - 1], dec)
