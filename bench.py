@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of an MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8b_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_287_amd", "csrc", f)
                   for f in ("decode.hip", "pa_internal.hpp")]
@@ -50,7 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="8b",
-                    help="8b | tiny | prefix | sweep_bs{8,16,32,64} | variant_hkv{32,8,1}_{f16,fp8_e4m3}")
+                    help="8b | tiny | prefix | sweep_bs{8,16,32,64} | variant_hkv{32,8,1}_{f16,fp8_e4m3}"
+                         " | prefill_8b (chunked prefill: its own JSON line in TFLOP/s)")
     ap.add_argument("--flushed-calls", type=int, default=50,
                     help="pa_decode calls timed one by one after evicting the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,6 +158,137 @@ def cpu_baseline(case, budget_s: float):
             "seq_tokens_per_s": tok_done / dt}
 
 
+def prefill_flops(pc) -> int:
+    """Algorithmic flops of one causal chunk attention: a query at position p multiplies with
+    p + 1 keys and p + 1 values, 2 * D flops each, for every query head."""
+    c = pc.cache
+    total = 0
+    for b in range(c.num_seqs):
+        n, L = int(pc.chunk_lens[b]), int(c.context_lens[b])
+        total += n * (L - n) + n * (n + 1) // 2  # sum over j < n of (L - n + j + 1)
+    return 4 * c.head_dim * c.num_q_heads * total
+
+
+def prefill_cpu_baseline(pc, budget_s: float):
+    """Time the float64 oracle on single rows of the same workload (each row is a one-row chunk
+    at its own context length) until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    c = pc.cache
+    rng = np.random.default_rng(0)
+    flops, rows = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = int(rng.integers(0, c.num_seqs))
+        n, L = int(pc.chunk_lens[b]), int(c.context_lens[b])
+        j = int(rng.integers(0, n))
+        row = int(pc.query_start[b]) + j
+        oracle.prefill(pc.q[row: row + 1], c.k_cache, c.v_cache, c.block_tables[b: b + 1],
+                       np.array([L - n + j + 1], dtype=np.int32), np.array([0, 1], dtype=np.int32),
+                       c.scale)
+        flops += 4 * c.head_dim * c.num_q_heads * (L - n + j + 1)
+        rows += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} random query rows (all heads) of the same workload, each as a "
+                      f"one-row chunk, {dt:.1f} s, float64 numpy"}
+
+
+def main_prefill(args):
+    """Chunked prefill: one step is the chunk's append (pa_kv_write of every chunk token) and
+    the causal attention of the chunk over the cache (pa_prefill)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_287_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    progress(f"generating workload {args.workload}")
+    pc = workloads.prefill_8b()
+    c = pc.cache
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.float16:
+            return torch.from_numpy(x.view(np.uint16)).cuda().view(torch.float16)
+        return torch.from_numpy(x).cuda()
+
+    parts = [pc.chunk_kv(b) for b in range(c.num_seqs)]
+    g_nk = dev(np.concatenate([p[0] for p in parts]))
+    g_nv = dev(np.concatenate([p[1] for p in parts]))
+    g_slots = dev(np.concatenate([p[2] for p in parts]).astype(np.int64))
+    q, kc, vc = dev(pc.q), dev(c.k_cache), dev(c.v_cache)
+    tables, lens, qstart = dev(c.block_tables), dev(c.context_lens), dev(pc.query_start)
+    out = torch.empty_like(q)
+    max_q, max_ctx = int(pc.chunk_lens.max()), int(c.context_lens.max())
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        pa.pa_prefill(out, q, kc, vc, tables, lens, qstart, float(c.scale), max_query_len=max_q,
+                      max_context_len=max_ctx)
+
+    def step():
+        pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots)
+        prefill()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n, e0.elapsed_time(e1) * 1e-3 / n
+
+    progress(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    progress(f"timing {args.steps} steps")
+    wall_step, event_step = timed(step, args.steps)
+    progress(f"timing {args.steps} prefill calls")
+    _, event_call = timed(prefill, args.steps)
+    flops = prefill_flops(pc)
+    achieved = flops / event_call / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = prefill_cpu_baseline(pc, args.cpu_seconds)
+    line = {
+        "metric": "paged chunked prefill: causal attention TFLOP/s, 8B-shaped, 1 GPU",
+        "value": flops / wall_step / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_step * 1e3,
+        "event_ms_per_step": event_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) fp16 q/K/V, scattered blocks, NaN-poisoned unused slots)",
+        "config": {"workload": f"paged chunked prefill {pc.name}: {c.num_seqs} seqs, chunk "
+                               f"{max_q} tokens at context {max_ctx}, {c.num_q_heads}q/"
+                               f"{c.num_kv_heads}kv heads, head_dim {c.head_dim}, block_size "
+                               f"{c.block_size}, {c.kv_dtype} KV",
+                   "step": "kv_write(chunk) + prefill"},
+        "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "pa_prefill (prefill_kernel)", "avg_call_us": event_call * 1e6,
+                     "timing": "HIP events around the timed back-to-back pa_prefill calls"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +296,8 @@ def main():
               "(the decode path shards by sequence or KV head with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("prefill"):
+        return main_prefill(args)
     import numpy as np
     import torch
 
@@ -350,7 +485,7 @@ def main():
             traffic = tr.get("hbm_bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+                "kernel": "pa_decode (decode_partition_kernel, cross-partition merge fused)",
                 "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3,
                 "timing": "HIP events around the timed back-to-back pa_decode calls"}
     cpu = None

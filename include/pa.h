@@ -137,6 +137,49 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * pa_prefill — causal attention of a chunk of new tokens per sequence over its paged KV cache
+ * (prefill, or one chunk of a chunked prefill).
+ *
+ * Prefill turns the prompt into KV-cache entries with large matrix products and is bound by
+ * arithmetic, while decode is bound by reading the cache ("LLM 추론 확장, 품질·비용 절충 필수",
+ * prefill and decode paragraphs). The chunk's keys and values are appended first (pa_kv_write);
+ * then, for sequence b with n = query_start[b+1] - query_start[b] query rows and
+ * L = context_lens[b] tokens in the cache (the chunk being the last n of them), every query
+ * head h (KV head g = h / G) and chunk token j < n at position p = L - n + j:
+ *     out[query_start[b] + j, h, :] = softmax(scale * K_b[0..p] q[query_start[b] + j, h])
+ *                                     V_b[0..p]
+ * with K_b, V_b read through the block table as in pa_decode (fp32 accumulation, fp16 out;
+ * E4M3 values are decode(code) * scale[block, g]). Scores and probabilities go through fp16
+ * matrix-core products, the probabilities rounded to fp16 before the product with V.
+ * A decode step is the case n = 1.
+ *
+ *   q, out           [num_tokens, Hq, D] fp16, the chunks of all sequences back to back.
+ *   query_start      [num_seqs + 1] int32 device array: first row of each sequence's chunk
+ *                    in q / out, then num_tokens.
+ *   max_query_len    host-side upper bound on every n (sizes the grid).
+ *   max_context_len  host-side upper bound on context_lens[]; at most max_blocks_per_seq *
+ *                    block_size and at most 4096 * block_size (the kernel keeps a sequence's
+ *                    block ids on chip).
+ * Preconditions (not checked): query_start non-decreasing from 0 to num_tokens;
+ * n <= max_query_len; n <= context_lens[b] <= max_context_len; block ids of the first
+ * ceil(L / BS) table entries in [0, num_blocks); out does not alias any input. Violations give
+ * wrong values but no access outside the buffers: row ranges are clamped into [0, num_tokens),
+ * n to max_query_len, L to max_context_len, block ids into [0, num_blocks); rows at a position
+ * below 0 are written as zeros.
+ * Validated: non-NULL pointers (scales as in pa_decode), 16-byte alignment of q, out and the
+ * caches; 4-byte alignment of the int arrays; sizes; Hq % Hkv == 0; supported head_dim,
+ * block_size and dtype; the grid (max_query_len * G / 128 * Hkv * num_seqs workgroups) < 2^31.
+ * num_tokens == 0 returns PA_OK without launching. Needs no workspace; deterministic.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+               int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+               int32_t max_query_len, int32_t max_context_len, float scale, int32_t kv_dtype,
+               void* stream);
+
+/*
  * pa_kv_write — slot-mapped append of new keys and values.
  *
  * For each token t < num_tokens with slot = slot_mapping[t] >= 0, writes

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
-    "decode_workspace_bytes", "decode_partition_tokens", "pa_decode", "pa_kv_write",
+    "decode_workspace_bytes", "decode_partition_tokens", "pa_decode", "pa_prefill", "pa_kv_write",
     "pa_copy_blocks", "pa_swap_blocks", "stream_read_probe",
 ]
 
@@ -41,6 +41,8 @@ EXPORTED_SYMBOLS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p]),
     "pa_copy_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
@@ -163,6 +165,49 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        _ptr(workspace), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode")
+    return out
+
+
+def pa_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+               scale: float, *, max_query_len: int, max_context_len: int = 0,
+               k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Enqueue causal chunk attention over the paged cache; writes ``out`` [T, Hq, D] fp16.
+
+    ``query_start`` [S + 1] int32 (device) gives each sequence's first row in ``q`` / ``out``;
+    ``max_query_len`` bounds every chunk length and ``max_context_len`` (0 = the table's width
+    times the block size) every context length; both are host integers that size the grid.
+    """
+    _check(q, "q", (torch.float16,), 3)
+    _check(out, "out", (torch.float16,), 3)
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(block_tables, "block_tables", (torch.int32,), 2)
+    _check(context_lens, "context_lens", (torch.int32,), 1)
+    _check(query_start, "query_start", (torch.int32,), 1)
+    kvt = _kv_dtype(k_cache)
+    if kvt == PA_KV_FP8_E4M3:
+        for n, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{n} is required for an 8-bit cache")
+            _check(s, n, (torch.float32,), 2)
+    num_tokens, num_q_heads, head_dim = q.shape
+    nb, num_kv_heads, block_size, d2 = k_cache.shape
+    num_seqs = context_lens.shape[0]
+    if out.shape != q.shape or d2 != head_dim or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if block_tables.shape[0] != num_seqs or query_start.shape[0] != num_seqs + 1:
+        raise ValueError("block_tables needs one row and query_start one entry per sequence (+1)")
+    mbps = block_tables.shape[1]
+    st = lib.pa_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                        _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), _ptr(query_start),
+                        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, nb,
+                        mbps, int(max_query_len),
+                        int(max_context_len) if max_context_len > 0 else mbps * block_size,
+                        float(scale), kvt, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_prefill")
     return out
 
 

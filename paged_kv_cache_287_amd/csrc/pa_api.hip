@@ -151,6 +151,62 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                                       static_cast<hipStream_t>(stream)));
 }
 
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+               int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+               int32_t max_query_len, int32_t max_context_len, float scale, int32_t kv_dtype,
+               void* stream) {
+  if (num_seqs <= 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || max_query_len < 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!known_dtype(kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const bool fp8 = kv_dtype == PA_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return PA_ERR_INVALID_ARG;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size)
+    return PA_ERR_INVALID_ARG;
+  if ((long long)max_context_len > (long long)pa::kPrefillMaxBlocks * block_size)
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (max_query_len == 0) return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
+      (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4))))
+    return PA_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  const long long q_tiles = pa::ceil_div((long long)max_query_len * group, pa::kPrefillRows);
+  if (q_tiles * num_kv_heads * num_seqs >= (1LL << 31)) return PA_ERR_INVALID_ARG;
+
+  pa::PrefillParams p{};
+  p.out = static_cast<_Float16*>(out);
+  p.q = static_cast<const _Float16*>(q);
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.num_tokens = num_tokens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.max_query_len = max_query_len;
+  p.max_context_len = max_context_len;
+  p.group = group;
+  p.q_tiles = (int)q_tiles;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pa::launch_prefill(p, num_seqs, head_dim, block_size, fp8,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int pa_kv_write(const void* k, const void* v, void* k_cache, void* v_cache, float* k_scale,
                 float* v_scale, const int64_t* slot_mapping, int32_t num_tokens,
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,

@@ -24,6 +24,9 @@ constexpr int kMaxPartTokens = 4096;
 // Compute units of an MI355X / MI350X (gfx950): the automatic partition choice aims to give the
 // grid enough workgroups to fill them.
 constexpr int kNumCUs = 256;
+// Accelerator complex dies of an MI355X: consecutive workgroup ids are dealt round-robin over
+// them, and each has its own L2.
+constexpr int kNumXcds = 8;
 
 inline bool valid_part_tokens(int pt, int block_size) {
   if (pt < kMinPartTokens || pt > kMaxPartTokens || (pt & (pt - 1)) != 0) return false;
@@ -99,11 +102,42 @@ struct DecodeParams {
   float scale_log2;     // softmax scale * log2(e)
 };
 
+// ---- prefill geometry ------------------------------------------------------------------
+// A prefill workgroup owns kPrefillRows query rows (chunk token x query head of one KV head) and
+// holds the block ids of its attended range in LDS, so a sequence may span at most
+// kPrefillMaxBlocks blocks.
+constexpr int kPrefillRows = 128;
+constexpr int kPrefillMaxBlocks = 4096;
+
+struct PrefillParams {
+  _Float16* out;
+  const _Float16* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [S + 1] first query row of each sequence, then the total
+  int32_t num_tokens;          // rows of q and out
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t max_query_len;
+  int32_t max_context_len;
+  int32_t group;
+  int32_t q_tiles;             // ceil(max_query_len * group / kPrefillRows)
+  float scale_log2;
+};
+
 // Launchers: return hipSuccess or the launch error. Arguments are already validated.
 hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                          int head_tile, bool kv_fp8, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                               int rows, bool kv_fp8, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,
+                          bool kv_fp8, hipStream_t stream);
 hipError_t launch_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                            int head_dim, int block_size, int num_blocks, hipStream_t stream);

@@ -1,0 +1,329 @@
+// Paged prefill for gfx950: causal attention of a chunk of new tokens over each sequence's paged
+// KV cache, on matrix cores.
+//
+// Prefill is the compute-bound phase: the prompt is processed with large matrix products, while
+// decode is bound by reading the cache ("LLM 추론 확장, 품질·비용 절충 필수", prefill and decode
+// paragraphs). A chunk's keys and values are appended to the cache first (pa_kv_write); query j
+// of a chunk of n then sits at position L - n + j and attends to positions 0 .. L - n + j, read
+// through the block table ("serving-paged-attention", section "블록으로 쪼개고 표로 잇는다").
+//
+// Work decomposition. The query rows of one (sequence, KV head) are the chunk's tokens times the
+// G query heads of that KV head, flattened as row = j * G + (h mod G). A workgroup of four waves
+// owns 128 consecutive rows; each wave owns 32 of them (two 16-row MFMA tiles) for the whole
+// attended range, so no cross-wave merge is needed. The workgroup walks the attended tokens in
+// 64-token tiles; every tile of K and V is read from the cache once per workgroup, converted to
+// fp16 if the cache is 8-bit, and staged in LDS for all four waves:
+//   * K as [token][d] rows: a wave reads its MFMA A operand (16 tokens x 32 dims) straight out;
+//   * V transposed, as [d][token] rows, with the tokens of each 32-token half permuted so that a
+//     lane's eight contraction slots are one 16-byte read (see vt_col).
+// Per tile and 16-row tile a wave forms S^T = K Q^T with v_mfma_f32_16x16x32_f16 (a lane ends up
+// with four consecutive tokens of one row), updates that row's online softmax in log2 units, and
+// accumulates O^T += V^T P^T, again with 16x16x32, where P^T is taken as-is from the lanes that
+// computed it. Loads of the next tile are in flight while the current one is computed.
+#include "decode_common.hpp"
+
+namespace pa {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaveRows = 32;                        // query rows per wave (two 16-row tiles)
+constexpr int kTileTok = 64;                         // attended tokens per LDS tile
+static_assert(kPrefillRows == kWaves * kWaveRows, "rows per workgroup");
+
+// Column of tile token t (0..63) in the transposed V tile. Within each half of 32 tokens, tokens
+// 4c..4c+3 go to columns 8c..8c+3 and tokens 16+4c..16+4c+3 to columns 8c+4..8c+7: exactly the
+// tokens whose scores lane group c holds after the two 16-token S^T products of that half, so
+// those eight scores and the matching eight V^T values meet in the same contraction slots.
+__device__ __forceinline__ int vt_col(int t) {
+  const int half = t & 32, u = t & 31;
+  return half + ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
+}
+
+template <int NWORDS>
+__device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
+  uint32_t w[4];
+  if constexpr (NWORDS == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = c.w[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      w[2 * i] = e4m3x2_to_f16x2<false>(c.w[i]);
+      w[2 * i + 1] = e4m3x2_to_f16x2<true>(c.w[i]);
+    }
+  }
+  return __builtin_bit_cast(h8, w);
+}
+
+template <int D, int BS, bool KV8>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
+  constexpr int NT = kWaveRows / 16;
+  constexpr int KK = D / 32;              // 32-dim steps of S^T = K Q^T
+  constexpr int MT = D / 16;              // 16-dim tiles of O^T
+  constexpr int ESZ = KV8 ? 1 : 2;
+  constexpr int ROW_BYTES = D * ESZ;
+  constexpr int TILE_BYTES = BS * ROW_BYTES;  // one block of one KV head
+  constexpr int NWORDS = 2 * ESZ;         // 32-bit words per 8-element chunk
+  constexpr int DCH = D / 8;              // 8-element chunks per token row
+  constexpr int TPT = kTileTok * DCH / kThreads;  // consecutive tokens staged per thread (4 or 2)
+  constexpr int KRS = D + 8;              // LDS row stride of K (halves)
+  constexpr int VRS = kTileTok + 8;       // LDS row stride of V^T (halves)
+  static_assert(TPT == 4 || TPT == 2, "staging shape");
+
+  __shared__ __align__(16) _Float16 k_lds[kTileTok * KRS];
+  __shared__ __align__(16) _Float16 vt_lds[D * VRS];
+  __shared__ int32_t ids[kPrefillMaxBlocks];
+
+  // ---- which (sequence, KV head, row tile): consecutive ids on one XCD share a KV range ------
+  int wid = blockIdx.x;
+  const int per_xcd = gridDim.x / kNumXcds;
+  if (wid < per_xcd * kNumXcds) wid = (wid % kNumXcds) * per_xcd + wid / kNumXcds;
+  const int qt = wid % p.q_tiles;
+  const int kvh = (wid / p.q_tiles) % p.num_kv_heads;
+  const int b = wid / (p.q_tiles * p.num_kv_heads);
+
+  const int T = p.num_tokens;
+  const int qs = min(max(p.query_start[b], 0), T);
+  const int qe = min(max(p.query_start[b + 1], qs), T);
+  const int n = min(qe - qs, p.max_query_len);
+  const int G = p.group;
+  const int nrows = n * G;
+  const int row0 = qt * kPrefillRows;
+  if (row0 >= nrows) return;  // uniform over the workgroup
+  const int L = min(max(p.context_lens[b], 0), p.max_context_len);
+  const int base = L - n;     // position of the chunk's first token
+  const int kv_end = max(0, min(L, base + (min(row0 + kPrefillRows, nrows) - 1) / G + 1));
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+
+  // ---- block ids of the attended range ------------------------------------------------------
+  const int nblk = (kv_end + BS - 1) / BS;
+  for (int i = tid; i < nblk; i += kThreads) {
+    const int id = p.block_tables[(size_t)b * p.max_blocks_per_seq + i];
+    ids[i] = min(max(id, 0), p.num_blocks - 1);
+  }
+
+  // ---- this wave's query rows as the B operand of S^T = K Q^T -------------------------------
+  const int wrow0 = row0 + wave * kWaveRows;
+  h8 qb[NT][KK];
+  int pos[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = wrow0 + 16 * nt + lr;
+    const bool ok = r < nrows;
+    const int j = ok ? r / G : 0;
+    const int h = kvh * G + (ok ? r - j * G : 0);
+    pos[nt] = ok ? base + j : -1;
+    const _Float16* qrow = p.q + ((size_t)(qs + j) * p.num_q_heads + h) * D + 8 * lq;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qb[nt][kk] = ok ? *reinterpret_cast<const h8*>(qrow + 32 * kk) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  // positions of the wave's first and last valid rows (rows are in token order)
+  const int wpos_lo = base + wrow0 / G;
+  const int wpos_hi = wrow0 < nrows ? base + (min(wrow0 + kWaveRows, nrows) - 1) / G : -1;
+
+  float m[NT], l[NT];
+  f4 o[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = kNegInf;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- staging: thread -> (TPT consecutive tokens, one 8-element chunk of d) ------------------
+  const int sch = tid % DCH;
+  const int st0 = (tid / DCH) * TPT;
+  const uint8_t* kbase = p.k_cache + (size_t)kvh * TILE_BYTES + sch * 8 * ESZ;
+  const uint8_t* vbase = p.v_cache + (size_t)kvh * TILE_BYTES + sch * 8 * ESZ;
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE_BYTES;
+  Chunk<NWORDS> kr[TPT], vr[TPT];
+
+  auto issue = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = min(tile * kTileTok + st0 + u, kv_end - 1);
+      const size_t off = (size_t)ids[t / BS] * blk_stride + (size_t)(t % BS) * ROW_BYTES;
+      kr[u] = load_chunk<NWORDS>(kbase + off);
+      vr[u] = load_chunk<NWORDS>(vbase + off);
+    }
+  };
+
+  auto stage = [&]() {
+    h8 vv[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      *reinterpret_cast<h8*>(k_lds + (st0 + u) * KRS + 8 * sch) = to_h8(kr[u]);
+      vv[u] = to_h8(vr[u]);
+    }
+    const int col = vt_col(st0);  // st0 .. st0 + TPT - 1 land in consecutive columns
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16* dst = vt_lds + (8 * sch + e) * VRS + col;
+      if constexpr (TPT == 4)
+        *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
+      else
+        *reinterpret_cast<h2*>(dst) = h2{vv[0][e], vv[1][e]};
+    }
+  };
+
+  auto compute = [&](int tile) {
+    const int tok0 = tile * kTileTok;
+    if (tok0 > wpos_hi) return;  // every token of the tile is in this wave's causal future
+    const bool masked = tok0 + kTileTok - 1 > wpos_lo;
+    float kmul[4], vmul[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kmul[s] = p.scale_log2;
+      vmul[s] = 1.f;
+      if constexpr (KV8) {
+        // a lane's four tokens 16s + 4lq .. +3 share one block (block sizes are multiples of 4)
+        const int id = ids[min(tok0 + 16 * s + 4 * lq, kv_end - 1) / BS];
+        kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
+        vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+      }
+    }
+    // S^T for the four 16-token sub-tiles and both row tiles
+    f4 sacc[NT][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8 kA[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kA[kk] = *reinterpret_cast<const h8*>(k_lds + (16 * s + lr) * KRS + 32 * kk + 8 * lq);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qb[nt][kk], acc, 0, 0, 0);
+        sacc[nt][s] = acc;
+      }
+    }
+    // online softmax per row (lane lr's row; its 16 tokens of the tile are spread over lq)
+    h8 pB[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float sv[4][4];
+      float tm = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int t = tok0 + 16 * s + 4 * lq + ii;
+          const bool valid = !masked || t <= pos[nt];
+          sv[s][ii] = valid ? sacc[nt][s][ii] * kmul[s] : kNegInf;
+          tm = fmaxf(tm, sv[s][ii]);
+        }
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mn = fmaxf(m[nt], tm);
+      const float ms = mn == kNegInf ? 0.f : mn;
+      const float alpha = fexp2(m[nt] - ms);
+      float pw[4][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          pw[s][ii] = fexp2(sv[s][ii] - ms);
+          ps += pw[s][ii];
+        }
+      l[nt] = l[nt] * alpha + ps;
+      m[nt] = mn;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int s0 = 2 * ks, s1 = 2 * ks + 1;
+        pB[nt][ks] = h8{(_Float16)(pw[s0][0] * vmul[s0]), (_Float16)(pw[s0][1] * vmul[s0]),
+                        (_Float16)(pw[s0][2] * vmul[s0]), (_Float16)(pw[s0][3] * vmul[s0]),
+                        (_Float16)(pw[s1][0] * vmul[s1]), (_Float16)(pw[s1][1] * vmul[s1]),
+                        (_Float16)(pw[s1][2] * vmul[s1]), (_Float16)(pw[s1][3] * vmul[s1])};
+      }
+    }
+    // O^T += V^T P^T, 32 tokens per product
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const h8 vA = *reinterpret_cast<const h8*>(vt_lds + (16 * mt + lr) * VRS + 32 * ks + 8 * lq);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vA, pB[nt][ks], o[nt][mt], 0, 0, 0);
+      }
+  };
+
+  __syncthreads();  // ids visible
+  const int tiles = (kv_end + kTileTok - 1) / kTileTok;
+  if (tiles > 0) issue(0);
+  for (int i = 0; i < tiles; ++i) {
+    __syncthreads();  // every wave is done reading the previous tile
+    stage();
+    __syncthreads();
+    if (i + 1 < tiles) issue(i + 1);
+    compute(i);
+  }
+
+  // ---- normalise and write this wave's rows ------------------------------------------------
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float lt = l[nt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int r = wrow0 + 16 * nt + lr;
+    if (r >= nrows) continue;
+    const int j = r / G;
+    const int h = kvh * G + (r - j * G);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    _Float16* orow = p.out + ((size_t)(qs + j) * p.num_q_heads + h) * D + 4 * lq;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<h4*>(orow + 16 * mt) =
+          h4{(_Float16)(o[nt][mt][0] * inv), (_Float16)(o[nt][mt][1] * inv),
+             (_Float16)(o[nt][mt][2] * inv), (_Float16)(o[nt][mt][3] * inv)};
+  }
+}
+
+template <int D, int BS, bool KV8>
+hipError_t launch_one(const PrefillParams& p, long long workgroups, hipStream_t stream) {
+  prefill_kernel<D, BS, KV8><<<dim3((unsigned)workgroups), kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int D, bool KV8>
+hipError_t dispatch_bs(const PrefillParams& p, long long wgs, int bs, hipStream_t stream) {
+  switch (bs) {
+    case 8: return launch_one<D, 8, KV8>(p, wgs, stream);
+    case 16: return launch_one<D, 16, KV8>(p, wgs, stream);
+    case 32: return launch_one<D, 32, KV8>(p, wgs, stream);
+    case 64: return launch_one<D, 64, KV8>(p, wgs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,
+                          bool kv_fp8, hipStream_t stream) {
+  const long long wgs = (long long)p.q_tiles * p.num_kv_heads * num_seqs;
+  if (head_dim == 128)
+    return kv_fp8 ? dispatch_bs<128, true>(p, wgs, block_size, stream)
+                  : dispatch_bs<128, false>(p, wgs, block_size, stream);
+  if (head_dim == 64)
+    return kv_fp8 ? dispatch_bs<64, true>(p, wgs, block_size, stream)
+                  : dispatch_bs<64, false>(p, wgs, block_size, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -194,3 +194,41 @@ def swap_args(**over):
 def test_swap_rejects_bad_arguments(over, expect):
     assert pa.lib.pa_swap_blocks(*swap_args(**over)) == expect
     assert pa.lib.pa_swap_blocks(*swap_args(num_pairs=0, block_mapping=None)) == pa.PA_OK
+
+
+def prefill_args(**over):
+    a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
+             block_tables=FAKE, context_lens=FAKE, query_start=FAKE, num_seqs=4, num_tokens=40,
+             num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10,
+             max_blocks_per_seq=4, max_query_len=16, max_context_len=64, scale=0.125, kv_dtype=0,
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(out=None), pa.PA_ERR_INVALID_ARG),
+    (dict(query_start=None), pa.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=0), pa.PA_ERR_INVALID_ARG),
+    (dict(num_tokens=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(max_query_len=0), pa.PA_ERR_INVALID_ARG),  # rows to compute but no query length
+    (dict(num_q_heads=6, num_kv_heads=4), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), pa.PA_ERR_INVALID_ARG),
+    (dict(head_dim=256), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=128), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1), pa.PA_ERR_INVALID_ARG),  # E4M3 without scales
+    (dict(k_scale=FAKE, v_scale=FAKE), pa.PA_ERR_INVALID_ARG),  # fp16 with scales
+    (dict(out=FAKE + 8), pa.PA_ERR_INVALID_ARG),  # misaligned
+    (dict(query_start=FAKE + 2), pa.PA_ERR_INVALID_ARG),
+    (dict(max_context_len=65), pa.PA_ERR_INVALID_ARG),  # longer than the table allows
+    # a sequence's block ids must fit on chip: at most 4096 blocks
+    (dict(max_blocks_per_seq=5000, max_context_len=4097 * 16), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=65535, num_kv_heads=1, num_q_heads=32, max_query_len=1 << 20),
+     pa.PA_ERR_INVALID_ARG),  # grid of 2^31 workgroups or more
+])
+def test_prefill_rejects_bad_arguments(over, expect):
+    assert pa.lib.pa_prefill(*prefill_args(**over)) == expect
+
+
+def test_prefill_with_no_rows_returns_ok_without_launching():
+    assert pa.lib.pa_prefill(*prefill_args(num_tokens=0, q=None, out=None)) == pa.PA_OK

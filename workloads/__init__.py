@@ -4,10 +4,13 @@ from .block_manager import AppendPlan, BlockManager, PoolExhausted, check_plan  
 from .configs import (  # noqa: F401
     SEEDS,
     DecodeCase,
+    PrefillCase,
     StepInputs,
     by_name,
     eight_b,
     normal_f16,
+    prefill_8b,
+    prefill_case,
     random_case,
     shared_prefix,
     softmax_scale,

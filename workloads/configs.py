@@ -34,7 +34,8 @@ from .quant import quantize_pool
 F16_NAN = np.uint16(0x7E00)
 
 # fixed seeds per workload
-SEEDS = {"tiny": 1, "8b": 2, "prefix": 3, "prefix_fork": 31, "sweep": 4, "variants": 5}
+SEEDS = {"tiny": 1, "8b": 2, "prefix": 3, "prefix_fork": 31, "sweep": 4, "variants": 5,
+         "prefill": 6}
 
 
 @dataclass
@@ -314,6 +315,55 @@ def variant(num_kv_heads: int, kv_dtype: str = "f16", num_seqs: int = 64, ctx: i
         case.v_cache, case.v_scale = quantize_pool(case.v_cache, live)
         case.kv_dtype = "fp8_e4m3"
     return case
+
+
+# --------------------------------------------------------------------------------------------
+# Prefill (a chunk of new tokens per sequence attending causally over its cache)
+# --------------------------------------------------------------------------------------------
+@dataclass
+class PrefillCase:
+    """A paged cache that already holds every sequence's chunk (the chunk is the last
+    ``chunk_lens[b]`` of its ``context_lens[b]`` tokens) plus the chunk queries back to back."""
+
+    name: str
+    cache: DecodeCase  # pools, tables, context lengths, scales; its q is unused
+    q: np.ndarray  # [T, Hq, D] fp16
+    query_start: np.ndarray  # [S + 1] int32
+    chunk_lens: np.ndarray  # [S] int32
+
+    @property
+    def num_tokens(self) -> int:
+        return self.q.shape[0]
+
+    def chunk_kv(self, b: int):
+        """The chunk's own keys and values [n, Hkv, D] (fp16 draws) and their slots [n]."""
+        L, n = int(self.cache.context_lens[b]), int(self.chunk_lens[b])
+        t = np.arange(L - n, L)
+        bs = self.cache.block_size
+        slots = self.cache.block_tables[b][t // bs].astype(np.int64) * bs + t % bs
+        return self.cache.logical_k[b][L - n:], self.cache.logical_v[b][L - n:], slots
+
+
+def prefill_case(seed, ctx_lens, chunk_lens, hq, hkv, d, bs, *, kv_dtype="f16",
+                 name="prefill") -> PrefillCase:
+    """Seeded prefill case: the cache of :func:`random_case` for the full context lengths, then
+    the chunk queries (one fp16 normal draw of ``[sum(chunk_lens), Hq, D]``)."""
+    ctx = [int(x) for x in ctx_lens]
+    chunks = np.asarray([int(x) for x in chunk_lens], dtype=np.int32)
+    assert len(ctx) == len(chunks) and all(0 <= n <= L for n, L in zip(chunks, ctx))
+    cache = random_case(seed, ctx, hq, hkv, d, bs, kv_dtype=kv_dtype, name=name)
+    rng = np.random.default_rng([int(np.sum(np.atleast_1d(seed))), 7])
+    q = normal_f16(rng, (int(chunks.sum()), hq, d))
+    query_start = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    return PrefillCase(name=name, cache=cache, q=q, query_start=query_start, chunk_lens=chunks)
+
+
+def prefill_8b(num_seqs: int = 16, ctx: int = 4096, chunk: int = 1024) -> PrefillCase:
+    """Chunked prefill in the 8B head shape: 16 sequences whose first 3,072 tokens are cached
+    and whose next 1,024-token chunk attends causally (context 4,096 after the chunk's
+    append), 32 q / 8 KV heads, D 128, BS 16, fp16."""
+    return prefill_case(SEEDS["prefill"], [ctx] * num_seqs, [chunk] * num_seqs, 32, 8, 128, 16,
+                        name="prefill_8b")
 
 
 def by_name(name: str) -> DecodeCase:
