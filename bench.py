@@ -69,6 +69,9 @@ def parse():
                          "known traffic that hardware byte counters are scaled against")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="split-context partition size passed to pa_decode (0 = library's choice)")
+    ap.add_argument("--decode", choices=["auto", "plain", "shared_prefix"], default="auto",
+                    help="decode entry point: shared_prefix reads each group's shared blocks once "
+                         "(auto: whenever the workload has prefix groups)")
     return ap.parse_args()
 
 
@@ -330,12 +333,26 @@ def main():
                                              args.partition_tokens)
     ws_bytes = pa.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                          case.head_dim, case.block_size, max_ctx, kvt, part_tokens)
+    shared = case.group_start is not None if args.decode == "auto" else args.decode == "shared_prefix"
+    if shared:
+        assert case.group_start is not None, "this workload has no shared-prefix groups"
+        ws_bytes = pa.shared_prefix_workspace_bytes(case.num_seqs, case.num_q_heads,
+                                                    case.num_kv_heads, case.head_dim,
+                                                    case.block_size, max_ctx, kvt, part_tokens)
+        g_gs, g_gpb = dev(case.group_start), dev(case.group_prefix_blocks)
+        max_group = int(np.diff(case.group_start).max())
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def decode():
-        pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
-                     max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws)
+        if shared:
+            pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, g_gs, g_gpb, float(case.scale),
+                                       max_group_seqs=max_group, k_scale=ks, v_scale=vs,
+                                       max_context_len=max_ctx, partition_tokens=part_tokens,
+                                       workspace=ws)
+        else:
+            pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
+                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws)
 
     def step():
         if g_pairs.shape[0]:
@@ -485,7 +502,9 @@ def main():
             traffic = tr.get("hbm_bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": "pa_decode (decode_partition_kernel, cross-partition merge fused)",
+                "kernel": ("pa_decode_shared_prefix (prefix pass prefill_kernel<PREFIX> + decode "
+                           "partition kernel, merge fused)") if shared else
+                          "pa_decode (decode partition kernel, cross-partition merge fused)",
                 "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3,
                 "timing": "HIP events around the timed back-to-back pa_decode calls"}
     cpu = None
@@ -513,7 +532,8 @@ def main():
                    "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
                    "block_size": case.block_size, "kv_dtype": case.kv_dtype,
                    "step": "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
-                   "partition_tokens": part_tokens},
+                   "partition_tokens": part_tokens,
+                   "decode": "shared_prefix" if shared else "plain"},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attainable_read_gbs": attainable,
         "frac_of_attainable": None if attainable is None else value / attainable,

@@ -137,6 +137,58 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * pa_decode_shared_prefix — pa_decode for batches in which groups of sequences share leading
+ * blocks (one system prompt behind many requests, or the siblings of parallel sampling), with
+ * the shared blocks read once per KV head for the whole group.
+ *
+ * Sharing a prefix makes block tables point at the same physical blocks ("serving-paged-
+ * attention", section "공유는 표를 베끼는 일이 된다": 100 requests behind one 512-token system
+ * prompt). Plain decode still reads those blocks once per sequence. Here the call runs in two
+ * passes on `stream`:
+ *   1. prefix pass: for each group g (sequences group_start[g] .. group_start[g+1]-1) and KV
+ *      head, the first group_prefix_blocks[g] blocks of the group's first member's table are
+ *      attended by the G query rows of every member at once, as one matrix-core product, giving
+ *      each (member, query head) an unnormalised partial (running max, running sum, weighted
+ *      value sum) over the prefix tokens;
+ *   2. decode pass: each sequence's remaining tokens [prefix, L) are attended exactly as in
+ *      pa_decode, and the workgroup that finishes a sequence merges the prefix partial with the
+ *      partition partials, exactly (talk summary, FlashAttention paragraph: partial softmax
+ *      states combine without approximation).
+ * The output is out[b, h, :] of pa_decode for the same inputs, up to rounding (the prefix
+ * products round the probabilities to fp16 before the product with V).
+ *
+ *   group_start          [num_groups + 1] int32, device: increasing sequence indices from 0 to
+ *                        num_seqs; a sequence that shares nothing is a group of its own (or
+ *                        has group_prefix_blocks 0).
+ *   group_prefix_blocks  [num_groups] int32, device: full blocks shared by every member of the
+ *                        group, taken from the first member's table (0 = none).
+ *   max_group_seqs       host bound on every group's size (sizes the prefix pass's grid).
+ *   workspace            >= pa_decode_shared_prefix_workspace_bytes(...) bytes, zero-filled
+ *                        before its first use, as for pa_decode (always needed here).
+ * Other arguments as for pa_decode.
+ * Preconditions (not checked), beyond pa_decode's: every member's first group_prefix_blocks[g]
+ * table entries equal the first member's, and group_prefix_blocks[g] * block_size <= the
+ * member's context length. Violations give wrong values, never an access outside the buffers.
+ * Validated: as pa_decode, plus non-NULL 4-byte aligned group arrays, num_groups >= 1,
+ * 1 <= max_group_seqs <= num_seqs, and the prefix pass's grid (ceil(max_group_seqs * G / 128)
+ * * Hkv * num_groups workgroups) < 2^31.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t max_context_len,
+                                               int32_t kv_dtype, int32_t partition_tokens);
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* group_start, const int32_t* group_prefix_blocks,
+                            int32_t num_groups, int32_t max_group_seqs, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, int32_t partition_tokens, float scale,
+                            int32_t kv_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * pa_prefill — causal attention of a chunk of new tokens per sequence over its paged KV cache
  * (prefill, or one chunk of a chunked prefill).
  *

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
-    "decode_workspace_bytes", "decode_partition_tokens", "pa_decode", "pa_prefill", "pa_kv_write",
+    "decode_workspace_bytes", "decode_partition_tokens", "pa_decode",
+    "shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_prefill", "pa_kv_write",
     "pa_copy_blocks", "pa_swap_blocks", "stream_read_probe",
 ]
 
@@ -41,6 +42,10 @@ EXPORTED_SYMBOLS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _f32, _i32, _p, _sz, _p]),
     "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -165,6 +170,71 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        _ptr(workspace), ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode")
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                  head_dim: int, block_size: int, max_context_len: int,
+                                  kv_dtype: int = PA_KV_F16, partition_tokens: int = 0) -> int:
+    """Workspace bytes for pa_decode_shared_prefix (allocate zero-filled: it holds counters)."""
+    return int(lib.pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                           head_dim, block_size, max_context_len,
+                                                           kv_dtype, partition_tokens))
+
+
+def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, group_start: torch.Tensor,
+                            group_prefix_blocks: torch.Tensor, scale: float, *,
+                            max_group_seqs: int, k_scale: Optional[torch.Tensor] = None,
+                            v_scale: Optional[torch.Tensor] = None, max_context_len: int = 0,
+                            partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Enqueue decode attention whose shared prefix blocks are read once per group and KV head;
+    writes ``out`` [S, Hq, D] fp16 and returns it.
+
+    ``group_start`` [NG + 1] and ``group_prefix_blocks`` [NG] are int32 device tensors;
+    ``max_group_seqs`` (host) bounds every group's size.
+    """
+    _check(q, "q", (torch.float16,), 3)
+    _check(out, "out", (torch.float16,), 3)
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(block_tables, "block_tables", (torch.int32,), 2)
+    _check(context_lens, "context_lens", (torch.int32,), 1)
+    _check(group_start, "group_start", (torch.int32,), 1)
+    _check(group_prefix_blocks, "group_prefix_blocks", (torch.int32,), 1)
+    kvt = _kv_dtype(k_cache)
+    if kvt == PA_KV_FP8_E4M3:
+        for n, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{n} is required for an 8-bit cache")
+            _check(s, n, (torch.float32,), 2)
+    num_seqs, num_q_heads, head_dim = q.shape
+    nb, num_kv_heads, block_size, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != head_dim or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    num_groups = group_prefix_blocks.shape[0]
+    if group_start.shape[0] != num_groups + 1:
+        raise ValueError("group_start must have one entry per group plus one")
+    mbps = block_tables.shape[1]
+    need = shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                         max_context_len if max_context_len > 0 else mbps * block_size,
+                                         kvt, partition_tokens)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_shared_prefix(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                                     _ptr(group_start), _ptr(group_prefix_blocks), num_groups,
+                                     int(max_group_seqs), num_seqs, num_q_heads, num_kv_heads,
+                                     head_dim, block_size, nb, mbps, max_context_len,
+                                     partition_tokens, float(scale), kvt, _ptr(workspace),
+                                     ws_bytes, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_shared_prefix")
     return out
 
 

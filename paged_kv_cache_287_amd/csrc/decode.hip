@@ -99,12 +99,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   const int part = blockIdx.z;
   const int kvh = hg / p.head_groups;
   const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * GT;
-  const int L = p.context_lens[b];
+  const SeqRange sr = seq_range<BS>(p, b);
+  const int L = sr.L;
   // partitions beyond the grid's (context longer than the host bound) are dropped, never
   // written outside the workspace
   const int part_tokens = p.part_tokens;
   const int wave_tokens = part_tokens / kWaves;
-  const int nparts = min(L > 0 ? (L + part_tokens - 1) / part_tokens : 1, p.max_parts);
+  const int span = L - sr.start;
+  const int nparts = min(span > 0 ? (span + part_tokens - 1) / part_tokens : 1, p.max_parts);
   if (part >= nparts) return;
 
   const int tid = threadIdx.x;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   }
 
   // ---- block ids of this wave's tokens: lane j holds logical block lb0 + j ---------------
-  const int wbase = part * part_tokens + wave * wave_tokens;
+  const int wbase = sr.start + part * part_tokens + wave * wave_tokens;
   const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
   int my_id = 0;
   if (wbase < L) {
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     }
   };
 
-  finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, h0, local_merge);
+  finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, local_merge);
 }
 
 template <int D, int BS, int GT, bool KV8>

@@ -59,16 +59,49 @@ __device__ __forceinline__ Chunk<NWORDS> load_chunk(const uint8_t* ptr) {
   return c;
 }
 
+// Context range [start, L) of sequence b covered by this call's partitions, and the number of
+// partial slots (0 or 1) that an earlier pass already filled for it. Plain decode covers the
+// whole context. With shared-prefix groups, a member of a group with a non-empty prefix starts
+// after the prefix blocks, whose partial the prefix pass stored in slot 0.
+struct SeqRange {
+  int L, start, extra;
+};
+template <int BS>
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
+  SeqRange r{p.context_lens[b], 0, 0};
+  if (p.group_start != nullptr) {
+    // last group whose first sequence is <= b
+    int lo = 0, hi = p.num_groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.group_start[mid] <= b) lo = mid;
+      else hi = mid - 1;
+    }
+    const bool member = p.group_start[lo] <= b && b < p.group_start[lo + 1];
+    // the prefix pass keeps a group's block ids on chip, so it covers at most
+    // kPrefillMaxBlocks of them; any shared blocks beyond are decoded per sequence
+    const int pb = member ? min(min(p.group_prefix_blocks[lo], p.max_blocks_per_seq),
+                                kPrefillMaxBlocks)
+                          : 0;
+    if (pb > 0) {
+      r.start = min(pb * BS, max(r.L, 0));
+      r.extra = 1;
+    }
+  }
+  return r;
+}
+
 // End of one (sequence, head group, partition) workgroup. merge(h, d, mx, ls, a) returns the
 // workgroup's combined running max, running sum and weighted value sum for element d of its
-// query row h (R rows, head dim D). With one partition the normalised output is written
-// directly; otherwise the partial is published and the workgroup that arrives last merges all
-// partitions exactly and resets the arrival counter to zero.
+// query row h (R rows, head dim D). With one partition and no earlier partial the normalised
+// output is written directly; otherwise the partial is published (after the `extra` slots an
+// earlier pass filled) and the workgroup that arrives last merges all slots exactly and resets
+// the arrival counter to zero.
 template <int R, int D, int NTHREADS, typename Merge>
 __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, int hg, int part,
-                                                 int nparts, int h0, Merge&& merge) {
+                                                 int nparts, int extra, int h0, Merge&& merge) {
   const int tid = threadIdx.x;
-  if (nparts == 1) {
+  if (nparts == 1 && extra == 0) {
     // the whole sequence fits one partition: normalise and write the output directly
     for (int idx = tid; idx < R * D; idx += NTHREADS) {
       const int h = idx / D, d = idx - h * D;
@@ -84,7 +117,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
     const int h = idx / D, d = idx - h * D;
     float mx, ls, a;
     merge(h, d, mx, ls, a);
-    const size_t slot = ((size_t)b * p.num_q_heads + h0 + h) * p.max_parts + part;
+    const size_t slot = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots + extra + part;
     publish(p.ws_acc + slot * D + d, a);
     if (d == 0) {
       publish(p.ws_ml + slot * 2, mx);
@@ -113,18 +146,19 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
   // exact merge: out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p
   for (int idx = tid; idx < R * D; idx += NTHREADS) {
     const int h = idx / D, d = idx - h * D;
-    const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.max_parts;
+    const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
     const float* ml = p.ws_ml + row0 * 2;
     const float* ac = p.ws_acc + row0 * D + d;
     // partitions are taken kChunk at a time with all their loads in flight together, merged
     // into a running (max, sum, value) exactly as the tiles were
     constexpr int kChunk = 8;
     float mx = kNegInf, ls = 0.f, a = 0.f;
-    for (int i0 = 0; i0 < nparts; i0 += kChunk) {
+    const int nslots = nparts + extra;
+    for (int i0 = 0; i0 < nslots; i0 += kChunk) {
       float mv[kChunk], lv[kChunk], av[kChunk];
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
-        const bool in = i0 + j < nparts;
+        const bool in = i0 + j < nslots;
         const int i = in ? i0 + j : i0;
         mv[j] = fetch(ml + 2 * i);
         lv[j] = fetch(ml + 2 * i + 1);

@@ -46,10 +46,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   const int part = blockIdx.z;
   const int kvh = hg / p.head_groups;
   const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * R;
-  const int L = p.context_lens[b];
+  const SeqRange sr = seq_range<BS>(p, b);
+  const int L = sr.L;
   const int part_tokens = p.part_tokens;
   const int wave_tokens = part_tokens / kWaves;
-  const int nparts = min(L > 0 ? (L + part_tokens - 1) / part_tokens : 1, p.max_parts);
+  const int span = L - sr.start;
+  const int nparts = min(span > 0 ? (span + part_tokens - 1) / part_tokens : 1, p.max_parts);
   if (part >= nparts) return;
 
   const int tid = threadIdx.x;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
           p.q + ((size_t)b * p.num_q_heads + h0 + 16 * nt + lr) * D + 32 * kk + 8 * lq);
 
   // ---- block ids of this wave's tokens: lane j holds logical block wbase / BS + j ------------
-  const int wbase = part * part_tokens + wave * wave_tokens;
+  const int wbase = sr.start + part * part_tokens + wave * wave_tokens;
   const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
   int my_id = 0;
   if (wbase < L) {
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       a = fmaf(wt, s_acc[(w * R + h) * D + d], a);
     }
   };
-  finish_partition<R, D, kThreads>(p, b, hg, part, nparts, h0, local_merge);
+  finish_partition<R, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, local_merge);
 }
 
 template <int D, int BS, int NT, bool KV8>

@@ -2,6 +2,8 @@
 // Nothing here allocates, frees or synchronises; all buffers belong to the caller.
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/pa.h"
 #include "pa_internal.hpp"
 
@@ -83,13 +85,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                               (int)pa::ceil_div(max_context_len, pt)).total;
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const float* k_scale, const float* v_scale, const int32_t* block_tables,
-              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-              int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_tokens,
-              float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes_given,
-              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of pa_decode and pa_decode_shared_prefix (groups == nullptr for plain decode).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                const int32_t* context_lens, const int32_t* group_start,
+                const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_seqs,
+                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                int32_t max_context_len, int32_t partition_tokens, float scale, int32_t kv_dtype,
+                void* workspace, size_t workspace_bytes_given, void* stream) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -106,6 +114,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
       !aligned(v_scale, 4))))
     return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535) return PA_ERR_INVALID_ARG;
+  const bool groups = group_start != nullptr;
+  if (groups) {
+    if (!group_prefix_blocks || !aligned(group_start, 4) || !aligned(group_prefix_blocks, 4) ||
+        num_groups <= 0 || max_group_seqs <= 0 || max_group_seqs > num_seqs)
+      return PA_ERR_INVALID_ARG;
+  }
   const long long max_ctx = max_context_len > 0 ? (long long)max_context_len
                                                 : (long long)max_blocks_per_seq * block_size;
   if (max_ctx > (long long)max_blocks_per_seq * block_size || max_ctx > (1LL << 30))
@@ -116,8 +130,15 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     return partition_tokens != 0 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
   const int gt = pa::decode_rows(group);
-  const pa::WorkspaceLayout ws =
-      pa::workspace_layout(num_seqs, num_q_heads, num_kv_heads * (group / gt), head_dim, max_parts);
+  const int part_slots = max_parts + (groups ? 1 : 0);
+  long long prefix_tiles = 0;
+  if (groups) {
+    prefix_tiles = pa::ceil_div((long long)max_group_seqs * group, pa::kPrefillRows);
+    if (prefix_tiles * num_kv_heads * num_groups >= (1LL << 31)) return PA_ERR_INVALID_ARG;
+  }
+  const pa::WorkspaceLayout ws = pa::workspace_layout(num_seqs, num_q_heads,
+                                                      num_kv_heads * (group / gt), head_dim,
+                                                      part_slots);
   if (ws.total > 0 &&
       (workspace == nullptr || workspace_bytes_given < ws.total || !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
@@ -135,6 +156,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   p.counters = ws.total ? reinterpret_cast<int32_t*>(wsb + ws.counters_off) : nullptr;
   p.ws_ml = ws.total ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
   p.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc_off) : nullptr;
+  p.group_start = group_start;
+  p.group_prefix_blocks = group_prefix_blocks;
+  p.num_groups = groups ? num_groups : 0;
+  p.part_slots = part_slots;
   p.part_tokens = part_tokens;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -144,11 +169,89 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   p.group = group;
   p.head_groups = group / gt;
   p.scale_log2 = scale * 1.4426950408889634f;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (groups) {
+    // prefix pass: every group's shared blocks once per KV head, for all member queries
+    pa::PrefillParams f{};
+    f.q = p.q;
+    f.k_cache = p.k_cache;
+    f.v_cache = p.v_cache;
+    f.k_scale = k_scale;
+    f.v_scale = v_scale;
+    f.block_tables = block_tables;
+    f.context_lens = context_lens;
+    f.query_start = group_start;
+    f.num_tokens = num_seqs;
+    f.num_q_heads = num_q_heads;
+    f.num_kv_heads = num_kv_heads;
+    f.max_blocks_per_seq = max_blocks_per_seq;
+    f.num_blocks = num_blocks;
+    f.max_query_len = max_group_seqs;
+    f.max_context_len = (int)(std::min<long long>(max_ctx / block_size, pa::kPrefillMaxBlocks) *
+                              block_size);
+    f.group = group;
+    f.q_tiles = (int)prefix_tiles;
+    f.scale_log2 = p.scale_log2;
+    f.group_prefix_blocks = group_prefix_blocks;
+    f.ws_ml = p.ws_ml;
+    f.ws_acc = p.ws_acc;
+    f.part_slots = part_slots;
+    const int rc = hip_status(pa::launch_prefix_pass(f, num_groups, head_dim, block_size, fp8, st));
+    if (rc != PA_OK) return rc;
+  }
   if (pa::decode_uses_mfma(group))
-    return hip_status(pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8,
-                                             static_cast<hipStream_t>(stream)));
-  return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8,
-                                      static_cast<hipStream_t>(stream)));
+    return hip_status(pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8, st));
+  return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+              int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_tokens,
+              float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes_given,
+              void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     nullptr, nullptr, 0, 0, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                     partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t max_context_len,
+                                               int32_t kv_dtype, int32_t partition_tokens) {
+  const int pt = pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            block_size, max_context_len, kv_dtype,
+                                            partition_tokens);
+  if (pt == 0) return 0;
+  const int group = num_q_heads / num_kv_heads;
+  const int hg_total = num_kv_heads * (group / pa::decode_rows(group));
+  return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
+                              (int)pa::ceil_div(max_context_len, pt) + 1).total;
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* group_start, const int32_t* group_prefix_blocks,
+                            int32_t num_groups, int32_t max_group_seqs, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, int32_t partition_tokens, float scale,
+                            int32_t kv_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!group_start) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     group_start, group_prefix_blocks, num_groups, max_group_seqs, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, partition_tokens, scale, kv_dtype,
+                     workspace, workspace_bytes, stream);
 }
 
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -89,8 +89,15 @@ struct DecodeParams {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t* counters;  // [S, HG_total] arrival counters; zero before and after every call
-  float* ws_ml;       // [S, Hq, max_parts, 2] (running max in log2 units, running sum)
-  float* ws_acc;      // [S, Hq, max_parts, D] unnormalised weighted value sums
+  float* ws_ml;       // [S, Hq, part_slots, 2] (running max in log2 units, running sum)
+  float* ws_acc;      // [S, Hq, part_slots, D] unnormalised weighted value sums
+  // Shared-prefix groups (null for plain decode): sequences [group_start[g], group_start[g+1])
+  // share their first group_prefix_blocks[g] table entries, whose partial state the prefix
+  // pass has already stored in slot 0; the partitions then cover the rest of each context.
+  const int32_t* group_start;
+  const int32_t* group_prefix_blocks;
+  int32_t num_groups;
+  int32_t part_slots;   // partial slots per (sequence, query head): max_parts (+1 with groups)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
@@ -129,6 +136,14 @@ struct PrefillParams {
   int32_t group;
   int32_t q_tiles;             // ceil(max_query_len * group / kPrefillRows)
   float scale_log2;
+  // Prefix pass of shared-prefix decode: the "sequences" are groups, query_start is the group
+  // ranges over decode sequences, group_prefix_blocks[g] the shared leading blocks (read from
+  // the first member's table row), and the unnormalised partial of each (member, query head)
+  // goes to slot 0 of the decode workspace instead of a normalised output.
+  const int32_t* group_prefix_blocks;
+  float* ws_ml;
+  float* ws_acc;
+  int32_t part_slots;
 };
 
 // Launchers: return hipSuccess or the launch error. Arguments are already validated.
@@ -138,6 +153,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim,
                               int rows, bool kv_fp8, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,
                           bool kv_fp8, hipStream_t stream);
+hipError_t launch_prefix_pass(const PrefillParams& p, int num_groups, int head_dim, int block_size,
+                              bool kv_fp8, hipStream_t stream);
 hipError_t launch_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                            int head_dim, int block_size, int num_blocks, hipStream_t stream);

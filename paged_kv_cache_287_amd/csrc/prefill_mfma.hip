@@ -43,6 +43,15 @@ __device__ __forceinline__ int vt_col(int t) {
   return half + ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
 }
 
+// Bank swizzle of the transposed V tile: in row d, the 4-column unit k is stored at unit
+// k ^ (2 * ((d >> 4) & 7)). A staging write instruction has 16 lanes writing the same unit of
+// rows 8c + e (c = 0..15); the unpadded row stride would put pairs of those rows on the same
+// banks, the swizzle spreads them over all 64. The XOR keeps even unit pairs together, so a
+// reader's 16-byte operand (units 2i, 2i + 1 of one row) stays contiguous.
+__device__ __forceinline__ int vt_swz(int d, int col) {
+  return col ^ (((d >> 4) & 7) << 3);
+}
+
 template <int NWORDS>
 __device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
   uint32_t w[4];
@@ -59,7 +68,10 @@ __device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
   return __builtin_bit_cast(h8, w);
 }
 
-template <int D, int BS, bool KV8>
+// PREFIX selects the prefix pass of shared-prefix decode: the "sequences" are groups of decode
+// sequences that share leading blocks, each member contributes its G query rows, every row sees
+// all prefix tokens, and the unnormalised (max, sum, value sum) goes to the decode workspace.
+template <int D, int BS, bool KV8, bool PREFIX>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   constexpr int NT = kWaveRows / 16;
   constexpr int KK = D / 32;              // 32-dim steps of S^T = K Q^T
@@ -94,9 +106,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int nrows = n * G;
   const int row0 = qt * kPrefillRows;
   if (row0 >= nrows) return;  // uniform over the workgroup
-  const int L = min(max(p.context_lens[b], 0), p.max_context_len);
-  const int base = L - n;     // position of the chunk's first token
-  const int kv_end = max(0, min(L, base + (min(row0 + kPrefillRows, nrows) - 1) / G + 1));
+  int base, kv_end;
+  if constexpr (PREFIX) {
+    const int pb = min(min(p.group_prefix_blocks[b], p.max_blocks_per_seq), kPrefillMaxBlocks);
+    if (pb <= 0) return;  // no shared prefix: the decode pass covers these sequences alone
+    kv_end = min(pb * BS, p.max_context_len);
+    base = kv_end - 1;    // every row sees the whole prefix
+  } else {
+    const int L = min(max(p.context_lens[b], 0), p.max_context_len);
+    base = L - n;         // position of the chunk's first token
+    kv_end = max(0, min(L, base + (min(row0 + kPrefillRows, nrows) - 1) / G + 1));
+  }
+  // table row: the sequence's own, or (prefix pass) the group's first member's
+  const int32_t* table = p.block_tables + (size_t)(PREFIX ? qs : b) * p.max_blocks_per_seq;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,8 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // ---- block ids of the attended range ------------------------------------------------------
   const int nblk = (kv_end + BS - 1) / BS;
   for (int i = tid; i < nblk; i += kThreads) {
-    const int id = p.block_tables[(size_t)b * p.max_blocks_per_seq + i];
-    ids[i] = min(max(id, 0), p.num_blocks - 1);
+    ids[i] = min(max(table[i], 0), p.num_blocks - 1);
   }
 
   // ---- this wave's query rows as the B operand of S^T = K Q^T -------------------------------
@@ -121,15 +142,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const bool ok = r < nrows;
     const int j = ok ? r / G : 0;
     const int h = kvh * G + (ok ? r - j * G : 0);
-    pos[nt] = ok ? base + j : -1;
+    pos[nt] = ok ? (PREFIX ? base : base + j) : -1;
     const _Float16* qrow = p.q + ((size_t)(qs + j) * p.num_q_heads + h) * D + 8 * lq;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qb[nt][kk] = ok ? *reinterpret_cast<const h8*>(qrow + 32 * kk) : h8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   // positions of the wave's first and last valid rows (rows are in token order)
-  const int wpos_lo = base + wrow0 / G;
-  const int wpos_hi = wrow0 < nrows ? base + (min(wrow0 + kWaveRows, nrows) - 1) / G : -1;
+  const int wpos_lo = PREFIX ? base : base + wrow0 / G;
+  const int wpos_hi =
+      wrow0 < nrows ? (PREFIX ? base : base + (min(wrow0 + kWaveRows, nrows) - 1) / G) : -1;
 
   float m[NT], l[NT];
   f4 o[NT][MT];
@@ -169,7 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int col = vt_col(st0);  // st0 .. st0 + TPT - 1 land in consecutive columns
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      _Float16* dst = vt_lds + (8 * sch + e) * VRS + col;
+      const int d = 8 * sch + e;
+      _Float16* dst = vt_lds + d * VRS + vt_swz(d, col);
       if constexpr (TPT == 4)
         *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
       else
@@ -257,7 +280,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const h8 vA = *reinterpret_cast<const h8*>(vt_lds + (16 * mt + lr) * VRS + 32 * ks + 8 * lq);
+        const int d = 16 * mt + lr;
+        const h8 vA = *reinterpret_cast<const h8*>(vt_lds + d * VRS + vt_swz(d, 32 * ks + 8 * lq));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vA, pB[nt][ks], o[nt][mt], 0, 0, 0);
@@ -285,6 +309,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     if (r >= nrows) continue;
     const int j = r / G;
     const int h = kvh * G + (r - j * G);
+    if constexpr (PREFIX) {
+      // slot 0 of (member qs + j, head h), stored the way decode partials are (write-through),
+      // for the decode pass that follows on the same stream to merge
+      const size_t slot = ((size_t)(qs + j) * p.num_q_heads + h) * p.part_slots;
+      float* acc = p.ws_acc + slot * D + 4 * lq;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) publish(acc + 16 * mt + ii, o[nt][mt][ii]);
+      if (lq == 0) {
+        publish(p.ws_ml + slot * 2, m[nt]);
+        publish(p.ws_ml + slot * 2 + 1, lt);
+      }
+      continue;
+    }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     _Float16* orow = p.out + ((size_t)(qs + j) * p.num_q_heads + h) * D + 4 * lq;
 #pragma unroll
@@ -295,20 +334,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int BS, bool KV8>
+template <int D, int BS, bool KV8, bool PREFIX>
 hipError_t launch_one(const PrefillParams& p, long long workgroups, hipStream_t stream) {
-  prefill_kernel<D, BS, KV8><<<dim3((unsigned)workgroups), kThreads, 0, stream>>>(p);
+  prefill_kernel<D, BS, KV8, PREFIX><<<dim3((unsigned)workgroups), kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool PREFIX>
 hipError_t dispatch_bs(const PrefillParams& p, long long wgs, int bs, hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_one<D, 8, KV8>(p, wgs, stream);
-    case 16: return launch_one<D, 16, KV8>(p, wgs, stream);
-    case 32: return launch_one<D, 32, KV8>(p, wgs, stream);
-    case 64: return launch_one<D, 64, KV8>(p, wgs, stream);
+    case 8: return launch_one<D, 8, KV8, PREFIX>(p, wgs, stream);
+    case 16: return launch_one<D, 16, KV8, PREFIX>(p, wgs, stream);
+    case 32: return launch_one<D, 32, KV8, PREFIX>(p, wgs, stream);
+    case 64: return launch_one<D, 64, KV8, PREFIX>(p, wgs, stream);
   }
+  return hipErrorInvalidValue;
+}
+
+template <bool PREFIX>
+hipError_t dispatch(const PrefillParams& p, int num_units, int head_dim, int block_size,
+                    bool kv_fp8, hipStream_t stream) {
+  const long long wgs = (long long)p.q_tiles * p.num_kv_heads * num_units;
+  if (head_dim == 128)
+    return kv_fp8 ? dispatch_bs<128, true, PREFIX>(p, wgs, block_size, stream)
+                  : dispatch_bs<128, false, PREFIX>(p, wgs, block_size, stream);
+  if (head_dim == 64)
+    return kv_fp8 ? dispatch_bs<64, true, PREFIX>(p, wgs, block_size, stream)
+                  : dispatch_bs<64, false, PREFIX>(p, wgs, block_size, stream);
   return hipErrorInvalidValue;
 }
 
@@ -316,14 +368,12 @@ hipError_t dispatch_bs(const PrefillParams& p, long long wgs, int bs, hipStream_
 
 hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,
                           bool kv_fp8, hipStream_t stream) {
-  const long long wgs = (long long)p.q_tiles * p.num_kv_heads * num_seqs;
-  if (head_dim == 128)
-    return kv_fp8 ? dispatch_bs<128, true>(p, wgs, block_size, stream)
-                  : dispatch_bs<128, false>(p, wgs, block_size, stream);
-  if (head_dim == 64)
-    return kv_fp8 ? dispatch_bs<64, true>(p, wgs, block_size, stream)
-                  : dispatch_bs<64, false>(p, wgs, block_size, stream);
-  return hipErrorInvalidValue;
+  return dispatch<false>(p, num_seqs, head_dim, block_size, kv_fp8, stream);
+}
+
+hipError_t launch_prefix_pass(const PrefillParams& p, int num_groups, int head_dim, int block_size,
+                              bool kv_fp8, hipStream_t stream) {
+  return dispatch<true>(p, num_groups, head_dim, block_size, kv_fp8, stream);
 }
 
 }  // namespace pa

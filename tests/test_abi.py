@@ -232,3 +232,41 @@ def test_prefill_rejects_bad_arguments(over, expect):
 
 def test_prefill_with_no_rows_returns_ok_without_launching():
     assert pa.lib.pa_prefill(*prefill_args(num_tokens=0, q=None, out=None)) == pa.PA_OK
+
+
+def shared_args(**over):
+    a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
+             block_tables=FAKE, context_lens=FAKE, group_start=FAKE, group_prefix_blocks=FAKE,
+             num_groups=2, max_group_seqs=3, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+             head_dim=128, block_size=16, num_blocks=10, max_blocks_per_seq=4, max_context_len=0,
+             partition_tokens=0, scale=0.125, kv_dtype=0, workspace=None, workspace_bytes=0,
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(group_start=None), pa.PA_ERR_INVALID_ARG),
+    (dict(group_prefix_blocks=None), pa.PA_ERR_INVALID_ARG),
+    (dict(group_start=FAKE + 2), pa.PA_ERR_INVALID_ARG),
+    (dict(num_groups=0), pa.PA_ERR_INVALID_ARG),
+    (dict(max_group_seqs=0), pa.PA_ERR_INVALID_ARG),
+    (dict(max_group_seqs=5), pa.PA_ERR_INVALID_ARG),  # more members than sequences
+    (dict(q=None), pa.PA_ERR_INVALID_ARG),
+    (dict(head_dim=80), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1), pa.PA_ERR_INVALID_ARG),  # E4M3 without scales
+    # the prefix partial always goes through the workspace, even for one partition
+    (dict(), pa.PA_ERR_WORKSPACE),
+    (dict(workspace=FAKE, workspace_bytes=64), pa.PA_ERR_WORKSPACE),
+])
+def test_shared_prefix_rejects_bad_arguments(over, expect):
+    assert pa.lib.pa_decode_shared_prefix(*shared_args(**over)) == expect
+
+
+def test_shared_prefix_workspace_has_one_more_slot_per_row():
+    plain = pa.decode_workspace_bytes(64, 32, 8, 128, 16, 4096)
+    shared = pa.shared_prefix_workspace_bytes(64, 32, 8, 128, 16, 4096)
+    # one extra (max, sum) pair and one extra D-float row per (sequence, query head)
+    assert shared - plain >= 64 * 32 * (2 + 128) * 4
+    assert pa.shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 64) > 0
+    assert pa.decode_workspace_bytes(4, 8, 2, 128, 16, 64) == 0

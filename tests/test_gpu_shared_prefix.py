@@ -1,0 +1,115 @@
+"""GPU parity of pa_decode_shared_prefix (prefix blocks read once per group and KV head, then
+the private tails, merged exactly) against the float64 decode oracle: the shared-prefix and fork
+workloads after their copy-on-write + append step, ragged multi-group batches over head
+groupings, head dims, block sizes and KV dtypes, empty tails, explicit partition sizes,
+determinism and workspace reuse.
+
+The oracle is plain decode: sharing only changes which bytes are read once, not the result.
+Tolerance as for decode: |out - ref| <= 2e-3 + 2e-3 |ref| elementwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_helpers import (assert_attention_close, bits, case_to_device, dev, gen, gpu_decode,
+                            log, oracle_decode)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_shared(case, d, *, partition_tokens=0, workspace=None, max_context_len=0):
+    import paged_kv_cache_287_amd as pa
+
+    gs = case.group_start
+    out = torch.full_like(d["q"], float("nan"))
+    pa.pa_decode_shared_prefix(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                               d["context_lens"], dev(gs), dev(case.group_prefix_blocks),
+                               float(case.scale), max_group_seqs=int(np.diff(gs).max()),
+                               k_scale=d["k_scale"], v_scale=d["v_scale"],
+                               max_context_len=max_context_len or int(case.context_lens.max()),
+                               partition_tokens=partition_tokens, workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def apply_step(case):
+    """The workload's copy-on-write + append step on the device, and the oracle's pool after it."""
+    import paged_kv_cache_287_amd as pa
+
+    st = case.step
+    d = case_to_device(case)
+    pa.pa_copy_blocks(d["k_cache"], d["v_cache"], dev(st.block_mapping.reshape(-1, 2)))
+    pa.pa_kv_write(dev(st.new_k), dev(st.new_v), d["k_cache"], d["v_cache"], dev(st.slot_mapping))
+    kc, vc, _, _ = oracle.copy_blocks(case.k_cache, case.v_cache, st.block_mapping)
+    ek, ev = oracle.kv_write(st.new_k, st.new_v, kc, vc, st.slot_mapping)
+    return d, ek, ev
+
+
+@pytest.mark.parametrize("fork", [False, True])
+def test_shared_prefix_workloads_after_their_step(fork):
+    case = gen(workloads.shared_prefix, fork)
+    log(f"[shared] {case.name}: S={case.num_seqs} groups={len(case.group_prefix_blocks)} "
+        f"prefix blocks={case.group_prefix_blocks.tolist()}")
+    d, ek, ev = apply_step(case)
+    out = gpu_shared(case, d)
+    ref = oracle_decode(case, k_cache=ek, v_cache=ev)
+    assert_attention_close(out, ref, f"shared-prefix decode {case.name}")
+    plain = gpu_decode(d, case.scale)
+    assert_attention_close(plain, ref, f"plain decode {case.name}")
+
+
+GROUPS = [(3, 64, (0, 40)), (1, 0, (1, 20)), (40, 256, (1, 300)), (1, 128, (0, 0)),
+          (5, 32, (100, 700))]
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (16, 2), (12, 2), (32, 1), (16, 1)])
+def test_ragged_groups_head_layouts(hq, hkv):
+    case = workloads.prefix_groups(40 + hq + hkv, GROUPS, hq, hkv, 128, 16)
+    log(f"[shared] G={hq // hkv} S={case.num_seqs}")
+    out = gpu_shared(case, case_to_device(case))
+    assert_attention_close(out, oracle_decode(case), f"shared-prefix G{hq // hkv}")
+
+
+@pytest.mark.parametrize("d,bs,kv", [(128, 8, "f16"), (128, 64, "f16"), (64, 16, "f16"),
+                                     (128, 16, "fp8_e4m3"), (64, 32, "fp8_e4m3"),
+                                     (128, 8, "fp8_e4m3")])
+def test_ragged_groups_dims_block_sizes_dtypes(d, bs, kv):
+    groups = [(3, 8 * bs, (0, 40)), (1, 0, (1, 20)), (30, 4 * bs, (1, 300)), (2, 2 * bs, (0, 0))]
+    case = workloads.prefix_groups(60 + d + bs, groups, 32, 8, d, bs, kv_dtype=kv)
+    out = gpu_shared(case, case_to_device(case))
+    assert_attention_close(out, oracle_decode(case), f"shared-prefix D{d} BS{bs} {kv}")
+
+
+def test_mqa_group_larger_than_one_workgroup():
+    """160 members x 32 query heads = 5,120 rows: 40 row tiles of the prefix pass per KV head,
+    and the matrix-core decode pass for the tails."""
+    case = workloads.prefix_groups(77, [(160, 512, (1, 200)), (4, 0, (1, 50))], 32, 1, 128, 16)
+    out = gpu_shared(case, case_to_device(case))
+    assert_attention_close(out, oracle_decode(case), "shared-prefix MQA 160 members")
+
+
+@pytest.mark.parametrize("pt", [256, 1024])
+def test_explicit_partition_sizes(pt):
+    case = workloads.prefix_groups(88, [(20, 1024, (1, 3000)), (3, 0, (500, 2000))], 32, 8, 128, 16)
+    out = gpu_shared(case, case_to_device(case), partition_tokens=pt)
+    assert_attention_close(out, oracle_decode(case), f"shared-prefix pt={pt}")
+
+
+def test_deterministic_and_workspace_reuse():
+    """Bit-identical on reruns with one workspace (its counters return to zero), and a smaller
+    call through the same workspace afterwards is still correct."""
+    import paged_kv_cache_287_amd as pa
+
+    case = workloads.prefix_groups(99, GROUPS, 32, 8, 128, 16)
+    d = case_to_device(case)
+    need = pa.shared_prefix_workspace_bytes(case.num_seqs, 32, 8, 128, 16,
+                                            int(case.context_lens.max()))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    a = gpu_shared(case, d, workspace=ws)
+    b = gpu_shared(case, d, workspace=ws)
+    assert np.array_equal(bits(a), bits(b))
+    small = workloads.prefix_groups(100, [(4, 64, (1, 30))], 32, 8, 128, 16)
+    out = gpu_shared(small, case_to_device(small), workspace=ws)
+    assert_attention_close(out, oracle_decode(small), "shared-prefix after reuse")

@@ -11,6 +11,7 @@ from .configs import (  # noqa: F401
     normal_f16,
     prefill_8b,
     prefill_case,
+    prefix_groups,
     random_case,
     shared_prefix,
     softmax_scale,

@@ -69,6 +69,10 @@ class DecodeCase:
     logical_k: Optional[List[np.ndarray]] = field(default=None, repr=False)
     logical_v: Optional[List[np.ndarray]] = field(default=None, repr=False)
     step: Optional[StepInputs] = None
+    # shared-prefix groups: sequences [group_start[g], group_start[g+1]) share their first
+    # group_prefix_blocks[g] table entries (None when the workload has no such structure)
+    group_start: Optional[np.ndarray] = None
+    group_prefix_blocks: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -271,6 +275,42 @@ def shared_prefix(fork: bool = False, num_seqs: int = 100, prefix_len: int = 512
                         block_mapping=plan.block_mapping, pre_block_tables=pre_tables,
                         pre_context_lens=pre_lens))
     case.prefix_blocks = prefix_blocks  # type: ignore[attr-defined]
+    case.group_start = np.array([0, n], dtype=np.int32)
+    case.group_prefix_blocks = np.array([n_pref], dtype=np.int32)
+    return case
+
+
+def prefix_groups(seed, groups, hq, hkv, d, bs, *, kv_dtype="f16",
+                  name="prefix_groups") -> DecodeCase:
+    """Sequences in groups behind shared prefixes ("serving-paged-attention", section "공유는
+    표를 베끼는 일이 된다"). ``groups`` lists ``(members, prefix_tokens, (tail_lo, tail_hi))``:
+    the group's members alias one prefix of ``prefix_tokens`` tokens (a multiple of the block
+    size; 0 = nothing shared) and each has a private tail of U{tail_lo..tail_hi} tokens.
+
+    Draw order: tail lengths, then per group the prefix K/V and each member's tail K/V, then the
+    block permutation's use as blocks are taken in group order."""
+    rng = np.random.default_rng(seed)
+    tails = [rng.integers(lo, hi, endpoint=True, size=m) for m, _, (lo, hi) in groups]
+    live = 1 + sum(pt // bs + sum(-(-int(t) // bs) + 1 for t in tl)
+                   for (_, pt, _), tl in zip(groups, tails))
+    nb = int(math.ceil(1.25 * live)) + 1
+    bm = BlockManager(nb, bs, free_order=rng.permutation(nb))
+    lk, lv = [], []
+    gstart, gblocks = [0], []
+    for (m, pt, _), tl in zip(groups, tails):
+        assert pt % bs == 0
+        pblocks = bm.reserve(pt // bs) if pt else []
+        pk = normal_f16(rng, (pt, hkv, d))
+        pv = normal_f16(rng, (pt, hkv, d))
+        for t in tl:
+            bm.new_sequence(pt + int(t), prefix=pblocks)
+            lk.append(np.concatenate([pk, normal_f16(rng, (int(t), hkv, d))]))
+            lv.append(np.concatenate([pv, normal_f16(rng, (int(t), hkv, d))]))
+        gstart.append(gstart[-1] + m)
+        gblocks.append(pt // bs)
+    case = _finish(name, seed, rng, bm, lk, lv, hq, d, kv_dtype)
+    case.group_start = np.array(gstart, dtype=np.int32)
+    case.group_prefix_blocks = np.array(gblocks, dtype=np.int32)
     return case
 
 
