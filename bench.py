@@ -341,13 +341,15 @@ def main():
                                                     case.block_size, max_ctx, kvt, part_tokens)
         g_gs, g_gpb = dev(case.group_start), dev(case.group_prefix_blocks)
         max_group = int(np.diff(case.group_start).max())
+        max_prefix = max(1, int(case.group_prefix_blocks.max()))
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def decode():
         if shared:
             pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, g_gs, g_gpb, float(case.scale),
-                                       max_group_seqs=max_group, k_scale=ks, v_scale=vs,
+                                       max_group_seqs=max_group,
+                                       max_prefix_blocks=max_prefix, k_scale=ks, v_scale=vs,
                                        max_context_len=max_ctx, partition_tokens=part_tokens,
                                        workspace=ws)
         else:

@@ -147,9 +147,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * passes on `stream`:
  *   1. prefix pass: for each group g (sequences group_start[g] .. group_start[g+1]-1) and KV
  *      head, the first group_prefix_blocks[g] blocks of the group's first member's table are
- *      attended by the G query rows of every member at once, as one matrix-core product, giving
- *      each (member, query head) an unnormalised partial (running max, running sum, weighted
- *      value sum) over the prefix tokens;
+ *      attended by the G query rows of every member at once, as matrix-core products, giving
+ *      each (member, query head) unnormalised partials (running max, running sum, weighted
+ *      value sum), one per slice of the prefix tokens;
  *   2. decode pass: each sequence's remaining tokens [prefix, L) are attended exactly as in
  *      pa_decode, and the workgroup that finishes a sequence merges the prefix partial with the
  *      partition partials, exactly (talk summary, FlashAttention paragraph: partial softmax
@@ -163,6 +163,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   group_prefix_blocks  [num_groups] int32, device: full blocks shared by every member of the
  *                        group, taken from the first member's table (0 = none).
  *   max_group_seqs       host bound on every group's size (sizes the prefix pass's grid).
+ *   max_prefix_blocks    host bound on group_prefix_blocks[] (>= 1). The prefix pass covers at
+ *                        most min(max_prefix_blocks, max_blocks_per_seq, 4096,
+ *                        max_context_len / block_size) blocks of a group; shared blocks beyond
+ *                        that are attended per sequence, which gives the same result. The
+ *                        prefix is cut into at most 4 slices of at least 128 tokens, one
+ *                        workgroup each, so that short prefixes still spread over the GPU.
  *   workspace            >= pa_decode_shared_prefix_workspace_bytes(...) bytes, zero-filled
  *                        before its first use, as for pa_decode (always needed here).
  * Other arguments as for pa_decode.
@@ -170,8 +176,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * table entries equal the first member's, and group_prefix_blocks[g] * block_size <= the
  * member's context length. Violations give wrong values, never an access outside the buffers.
  * Validated: as pa_decode, plus non-NULL 4-byte aligned group arrays, num_groups >= 1,
- * 1 <= max_group_seqs <= num_seqs, and the prefix pass's grid (ceil(max_group_seqs * G / 128)
- * * Hkv * num_groups workgroups) < 2^31.
+ * 1 <= max_group_seqs <= num_seqs, max_prefix_blocks >= 1, and the prefix pass's grid
+ * (ceil(max_group_seqs * G / 128) * Hkv * num_groups * slices workgroups) < 2^31.
  */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                int32_t num_kv_heads, int32_t head_dim,
@@ -181,7 +187,8 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                             const float* k_scale, const float* v_scale,
                             const int32_t* block_tables, const int32_t* context_lens,
                             const int32_t* group_start, const int32_t* group_prefix_blocks,
-                            int32_t num_groups, int32_t max_group_seqs, int32_t num_seqs,
+                            int32_t num_groups, int32_t max_group_seqs,
+                            int32_t max_prefix_blocks, int32_t num_seqs,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                             int32_t max_context_len, int32_t partition_tokens, float scale,

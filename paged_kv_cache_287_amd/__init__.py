@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = {
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                               _i32, _f32, _i32, _p, _sz, _p]),
+                                               _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -186,7 +186,7 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
                             v_cache: torch.Tensor, block_tables: torch.Tensor,
                             context_lens: torch.Tensor, group_start: torch.Tensor,
                             group_prefix_blocks: torch.Tensor, scale: float, *,
-                            max_group_seqs: int, k_scale: Optional[torch.Tensor] = None,
+                            max_group_seqs: int, max_prefix_blocks: int, k_scale: Optional[torch.Tensor] = None,
                             v_scale: Optional[torch.Tensor] = None, max_context_len: int = 0,
                             partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
                             stream=None) -> torch.Tensor:
@@ -194,7 +194,7 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     writes ``out`` [S, Hq, D] fp16 and returns it.
 
     ``group_start`` [NG + 1] and ``group_prefix_blocks`` [NG] are int32 device tensors;
-    ``max_group_seqs`` (host) bounds every group's size.
+    ``max_group_seqs`` and ``max_prefix_blocks`` (host) bound every group's size and prefix.
     """
     _check(q, "q", (torch.float16,), 3)
     _check(out, "out", (torch.float16,), 3)
@@ -229,7 +229,7 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     st = lib.pa_decode_shared_prefix(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                      _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
                                      _ptr(group_start), _ptr(group_prefix_blocks), num_groups,
-                                     int(max_group_seqs), num_seqs, num_q_heads, num_kv_heads,
+                                     int(max_group_seqs), int(max_prefix_blocks), num_seqs, num_q_heads, num_kv_heads,
                                      head_dim, block_size, nb, mbps, max_context_len,
                                      partition_tokens, float(scale), kvt, _ptr(workspace),
                                      ws_bytes, _stream(stream))

@@ -60,9 +60,10 @@ __device__ __forceinline__ Chunk<NWORDS> load_chunk(const uint8_t* ptr) {
 }
 
 // Context range [start, L) of sequence b covered by this call's partitions, and the number of
-// partial slots (0 or 1) that an earlier pass already filled for it. Plain decode covers the
-// whole context. With shared-prefix groups, a member of a group with a non-empty prefix starts
-// after the prefix blocks, whose partial the prefix pass stored in slot 0.
+// partial slots that an earlier pass already filled for it. Plain decode covers the whole
+// context. With shared-prefix groups, a member of a group with a non-empty prefix starts after
+// the prefix blocks, whose partials the prefix pass stored in slots 0 .. extra - 1 (one per
+// slice of prefix_split tokens).
 struct SeqRange {
   int L, start, extra;
 };
@@ -78,14 +79,12 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
       else hi = mid - 1;
     }
     const bool member = p.group_start[lo] <= b && b < p.group_start[lo + 1];
-    // the prefix pass keeps a group's block ids on chip, so it covers at most
-    // kPrefillMaxBlocks of them; any shared blocks beyond are decoded per sequence
-    const int pb = member ? min(min(p.group_prefix_blocks[lo], p.max_blocks_per_seq),
-                                kPrefillMaxBlocks)
-                          : 0;
+    // the same clamp as the prefix pass (at most max_prefix_blocks, itself within the table
+    // and the prefix pass's on-chip id list); shared blocks beyond it are decoded per sequence
+    const int pb = member ? min(p.group_prefix_blocks[lo], p.max_prefix_blocks) : 0;
     if (pb > 0) {
       r.start = min(pb * BS, max(r.L, 0));
-      r.extra = 1;
+      r.extra = (pb * BS + p.prefix_split - 1) / p.prefix_split;
     }
   }
   return r;

@@ -94,7 +94,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 const float* k_scale, const float* v_scale, const int32_t* block_tables,
                 const int32_t* context_lens, const int32_t* group_start,
                 const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_seqs,
-                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t max_prefix_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                 int32_t max_context_len, int32_t partition_tokens, float scale, int32_t kv_dtype,
                 void* workspace, size_t workspace_bytes_given, void* stream) {
@@ -117,7 +117,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const bool groups = group_start != nullptr;
   if (groups) {
     if (!group_prefix_blocks || !aligned(group_start, 4) || !aligned(group_prefix_blocks, 4) ||
-        num_groups <= 0 || max_group_seqs <= 0 || max_group_seqs > num_seqs)
+        num_groups <= 0 || max_group_seqs <= 0 || max_group_seqs > num_seqs ||
+        max_prefix_blocks <= 0)
       return PA_ERR_INVALID_ARG;
   }
   const long long max_ctx = max_context_len > 0 ? (long long)max_context_len
@@ -130,12 +131,21 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return partition_tokens != 0 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
   const int gt = pa::decode_rows(group);
-  const int part_slots = max_parts + (groups ? 1 : 0);
+  // prefix blocks beyond the clamp (table width, on-chip id list, host bound on contexts) are
+  // simply decoded per sequence, so the clamp never changes the result
+  int prefix_blocks = 0, prefix_split = 0, prefix_slices = 0;
   long long prefix_tiles = 0;
   if (groups) {
+    prefix_blocks = (int)std::min<long long>(
+        std::min<long long>(max_prefix_blocks, max_blocks_per_seq),
+        std::min<long long>(pa::kPrefillMaxBlocks, max_ctx / block_size));
+    prefix_split = pa::prefix_split_tokens(prefix_blocks * block_size);
+    prefix_slices = (int)pa::ceil_div((long long)prefix_blocks * block_size, prefix_split);
     prefix_tiles = pa::ceil_div((long long)max_group_seqs * group, pa::kPrefillRows);
-    if (prefix_tiles * num_kv_heads * num_groups >= (1LL << 31)) return PA_ERR_INVALID_ARG;
+    if (prefix_tiles * num_kv_heads * num_groups * std::max(prefix_slices, 1) >= (1LL << 31))
+      return PA_ERR_INVALID_ARG;
   }
+  const int part_slots = max_parts + prefix_slices;
   const pa::WorkspaceLayout ws = pa::workspace_layout(num_seqs, num_q_heads,
                                                       num_kv_heads * (group / gt), head_dim,
                                                       part_slots);
@@ -159,6 +169,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.group_start = group_start;
   p.group_prefix_blocks = group_prefix_blocks;
   p.num_groups = groups ? num_groups : 0;
+  p.max_prefix_blocks = prefix_blocks;
+  p.prefix_split = prefix_split > 0 ? prefix_split : pa::kPrefixMinSplit;
   p.part_slots = part_slots;
   p.part_tokens = part_tokens;
   p.num_q_heads = num_q_heads;
@@ -171,7 +183,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.scale_log2 = scale * 1.4426950408889634f;
   const hipStream_t st = static_cast<hipStream_t>(stream);
 
-  if (groups) {
+  if (groups && prefix_blocks > 0) {
     // prefix pass: every group's shared blocks once per KV head, for all member queries
     pa::PrefillParams f{};
     f.q = p.q;
@@ -197,6 +209,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     f.ws_ml = p.ws_ml;
     f.ws_acc = p.ws_acc;
     f.part_slots = part_slots;
+    f.max_prefix_blocks = prefix_blocks;
+    f.prefix_split = prefix_split;
+    f.prefix_slices = prefix_slices;
     const int rc = hip_status(pa::launch_prefix_pass(f, num_groups, head_dim, block_size, fp8, st));
     if (rc != PA_OK) return rc;
   }
@@ -217,7 +232,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes_given,
               void* stream) {
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     nullptr, nullptr, 0, 0, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads, head_dim,
                      block_size, num_blocks, max_blocks_per_seq, max_context_len,
                      partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
 }
@@ -233,14 +248,15 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
   const int group = num_q_heads / num_kv_heads;
   const int hg_total = num_kv_heads * (group / pa::decode_rows(group));
   return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
-                              (int)pa::ceil_div(max_context_len, pt) + 1).total;
+                              (int)pa::ceil_div(max_context_len, pt) + pa::kMaxPrefixSlices).total;
 }
 
 int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const float* k_scale, const float* v_scale,
                             const int32_t* block_tables, const int32_t* context_lens,
                             const int32_t* group_start, const int32_t* group_prefix_blocks,
-                            int32_t num_groups, int32_t max_group_seqs, int32_t num_seqs,
+                            int32_t num_groups, int32_t max_group_seqs,
+                            int32_t max_prefix_blocks, int32_t num_seqs,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                             int32_t max_context_len, int32_t partition_tokens, float scale,
@@ -248,7 +264,8 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                             void* stream) {
   if (!group_start) return PA_ERR_INVALID_ARG;
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     group_start, group_prefix_blocks, num_groups, max_group_seqs, num_seqs,
+                     group_start, group_prefix_blocks, num_groups, max_group_seqs,
+                     max_prefix_blocks, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, partition_tokens, scale, kv_dtype,
                      workspace, workspace_bytes, stream);

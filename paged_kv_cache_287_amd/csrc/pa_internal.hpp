@@ -97,7 +97,9 @@ struct DecodeParams {
   const int32_t* group_start;
   const int32_t* group_prefix_blocks;
   int32_t num_groups;
-  int32_t part_slots;   // partial slots per (sequence, query head): max_parts (+1 with groups)
+  int32_t max_prefix_blocks;  // clamp on group_prefix_blocks (<= table width, kPrefillMaxBlocks)
+  int32_t prefix_split;       // prefix tokens per prefix-pass slice (multiple of 64)
+  int32_t part_slots;  // partial slots per (sequence, query head): max_parts (+ kMaxPrefixSlices)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
@@ -115,6 +117,16 @@ struct DecodeParams {
 // kPrefillMaxBlocks blocks.
 constexpr int kPrefillRows = 128;
 constexpr int kPrefillMaxBlocks = 4096;
+// Shared-prefix decode cuts each group's prefix into at most kMaxPrefixSlices slices of at least
+// kPrefixMinSplit tokens: enough workgroups to spread a short prefix over the GPU, and a bounded
+// number of extra partial states for the merge to read.
+constexpr int kMaxPrefixSlices = 4;
+constexpr int kPrefixMinSplit = 128;
+inline int prefix_split_tokens(int max_prefix_tokens) {
+  int split = kPrefixMinSplit;
+  while ((long long)split * kMaxPrefixSlices < max_prefix_tokens) split *= 2;
+  return split;
+}
 
 struct PrefillParams {
   _Float16* out;
@@ -144,6 +156,9 @@ struct PrefillParams {
   float* ws_ml;
   float* ws_acc;
   int32_t part_slots;
+  int32_t max_prefix_blocks;
+  int32_t prefix_split;
+  int32_t prefix_slices;  // grid slices per group: ceil(max_prefix_blocks * BS / prefix_split)
 };
 
 // Launchers: return hipSuccess or the launch error. Arguments are already validated.

@@ -29,6 +29,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaveRows = 32;                        // query rows per wave (two 16-row tiles)
 constexpr int kTileTok = 64;                         // attended tokens per LDS tile
@@ -70,7 +71,8 @@ __device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
 
 // PREFIX selects the prefix pass of shared-prefix decode: the "sequences" are groups of decode
 // sequences that share leading blocks, each member contributes its G query rows, every row sees
-// all prefix tokens, and the unnormalised (max, sum, value sum) goes to the decode workspace.
+// all prefix tokens, and the prefix is cut into slices of prefix_split tokens, one workgroup
+// each, whose unnormalised (max, sum, value sum) go to slots 0.. of the decode workspace.
 template <int D, int BS, bool KV8, bool PREFIX>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   constexpr int NT = kWaveRows / 16;
@@ -96,7 +98,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   if (wid < per_xcd * kNumXcds) wid = (wid % kNumXcds) * per_xcd + wid / kNumXcds;
   const int qt = wid % p.q_tiles;
   const int kvh = (wid / p.q_tiles) % p.num_kv_heads;
-  const int b = wid / (p.q_tiles * p.num_kv_heads);
+  const int unit = wid / (p.q_tiles * p.num_kv_heads);
+  // prefix pass: a unit is (group, slice of prefix_split tokens of its prefix)
+  const int b = PREFIX ? unit / p.prefix_slices : unit;
+  const int slice = PREFIX ? unit - b * p.prefix_slices : 0;
 
   const int T = p.num_tokens;
   const int qs = min(max(p.query_start[b], 0), T);
@@ -106,12 +111,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int nrows = n * G;
   const int row0 = qt * kPrefillRows;
   if (row0 >= nrows) return;  // uniform over the workgroup
-  int base, kv_end;
+  int base, kv_begin = 0, kv_end;
   if constexpr (PREFIX) {
-    const int pb = min(min(p.group_prefix_blocks[b], p.max_blocks_per_seq), kPrefillMaxBlocks);
-    if (pb <= 0) return;  // no shared prefix: the decode pass covers these sequences alone
-    kv_end = min(pb * BS, p.max_context_len);
-    base = kv_end - 1;    // every row sees the whole prefix
+    // the decode pass derives the same clamp and slice count from the same inputs
+    const int total = min(p.group_prefix_blocks[b], p.max_prefix_blocks) * BS;
+    kv_begin = slice * p.prefix_split;
+    if (kv_begin >= total) return;  // no prefix, or fewer slices than the grid allows for
+    kv_end = min(total, kv_begin + p.prefix_split);
+    base = total - 1;     // every row sees the whole prefix
   } else {
     const int L = min(max(p.context_lens[b], 0), p.max_context_len);
     base = L - n;         // position of the chunk's first token
@@ -127,9 +134,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const int lq = lane >> 4;
 
   // ---- block ids of the attended range ------------------------------------------------------
-  const int nblk = (kv_end + BS - 1) / BS;
+  // (kv_begin is a multiple of the 64-token tile, hence of the block size)
+  const int blk0 = kv_begin / BS;
+  const int nblk = (kv_end + BS - 1) / BS - blk0;
   for (int i = tid; i < nblk; i += kThreads) {
-    ids[i] = min(max(table[i], 0), p.num_blocks - 1);
+    ids[i] = min(max(table[blk0 + i], 0), p.num_blocks - 1);
   }
 
   // ---- this wave's query rows as the B operand of S^T = K Q^T -------------------------------
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int t = min(tile * kTileTok + st0 + u, kv_end - 1);
-      const size_t off = (size_t)ids[t / BS] * blk_stride + (size_t)(t % BS) * ROW_BYTES;
+      const size_t off = (size_t)ids[t / BS - blk0] * blk_stride + (size_t)(t % BS) * ROW_BYTES;
       kr[u] = load_chunk<NWORDS>(kbase + off);
       vr[u] = load_chunk<NWORDS>(vbase + off);
     }
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       vmul[s] = 1.f;
       if constexpr (KV8) {
         // a lane's four tokens 16s + 4lq .. +3 share one block (block sizes are multiples of 4)
-        const int id = ids[min(tok0 + 16 * s + 4 * lq, kv_end - 1) / BS];
+        const int id = ids[min(tok0 + 16 * s + 4 * lq, kv_end - 1) / BS - blk0];
         kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
         vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
       }
@@ -289,13 +298,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   };
 
   __syncthreads();  // ids visible
-  const int tiles = (kv_end + kTileTok - 1) / kTileTok;
-  if (tiles > 0) issue(0);
-  for (int i = 0; i < tiles; ++i) {
+  const int tile_lo = kv_begin / kTileTok;
+  const int tile_hi = (kv_end + kTileTok - 1) / kTileTok;
+  if (tile_lo < tile_hi) issue(tile_lo);
+  for (int i = tile_lo; i < tile_hi; ++i) {
     __syncthreads();  // every wave is done reading the previous tile
     stage();
     __syncthreads();
-    if (i + 1 < tiles) issue(i + 1);
+    if (i + 1 < tile_hi) issue(i + 1);
     compute(i);
   }
 
@@ -310,18 +320,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     const int j = r / G;
     const int h = kvh * G + (r - j * G);
     if constexpr (PREFIX) {
-      // slot 0 of (member qs + j, head h), stored the way decode partials are (write-through),
-      // for the decode pass that follows on the same stream to merge
-      const size_t slot = ((size_t)(qs + j) * p.num_q_heads + h) * p.part_slots;
+      // slot `slice` of (member qs + j, head h), for the decode pass that follows on the same
+      // stream to merge; the kernel boundary makes these plain stores visible to it
+      const size_t slot = ((size_t)(qs + j) * p.num_q_heads + h) * p.part_slots + slice;
       float* acc = p.ws_acc + slot * D + 4 * lq;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) publish(acc + 16 * mt + ii, o[nt][mt][ii]);
-      if (lq == 0) {
-        publish(p.ws_ml + slot * 2, m[nt]);
-        publish(p.ws_ml + slot * 2 + 1, lt);
-      }
+      for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f4*>(acc + 16 * mt) = o[nt][mt];
+      if (lq == 0) *reinterpret_cast<f2*>(p.ws_ml + slot * 2) = f2{m[nt], lt};
       continue;
     }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -373,7 +378,7 @@ hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, in
 
 hipError_t launch_prefix_pass(const PrefillParams& p, int num_groups, int head_dim, int block_size,
                               bool kv_fp8, hipStream_t stream) {
-  return dispatch<true>(p, num_groups, head_dim, block_size, kv_fp8, stream);
+  return dispatch<true>(p, num_groups * p.prefix_slices, head_dim, block_size, kv_fp8, stream);
 }
 
 }  // namespace pa

@@ -237,7 +237,7 @@ def test_prefill_with_no_rows_returns_ok_without_launching():
 def shared_args(**over):
     a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
              block_tables=FAKE, context_lens=FAKE, group_start=FAKE, group_prefix_blocks=FAKE,
-             num_groups=2, max_group_seqs=3, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+             num_groups=2, max_group_seqs=3, max_prefix_blocks=2, num_seqs=4, num_q_heads=8, num_kv_heads=2,
              head_dim=128, block_size=16, num_blocks=10, max_blocks_per_seq=4, max_context_len=0,
              partition_tokens=0, scale=0.125, kv_dtype=0, workspace=None, workspace_bytes=0,
              stream=None)
@@ -252,6 +252,7 @@ def shared_args(**over):
     (dict(num_groups=0), pa.PA_ERR_INVALID_ARG),
     (dict(max_group_seqs=0), pa.PA_ERR_INVALID_ARG),
     (dict(max_group_seqs=5), pa.PA_ERR_INVALID_ARG),  # more members than sequences
+    (dict(max_prefix_blocks=0), pa.PA_ERR_INVALID_ARG),
     (dict(q=None), pa.PA_ERR_INVALID_ARG),
     (dict(head_dim=80), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=1), pa.PA_ERR_INVALID_ARG),  # E4M3 without scales

@@ -19,7 +19,8 @@ from parity_helpers import (assert_attention_close, bits, case_to_device, dev, g
 pytestmark = pytest.mark.gpu
 
 
-def gpu_shared(case, d, *, partition_tokens=0, workspace=None, max_context_len=0):
+def gpu_shared(case, d, *, partition_tokens=0, workspace=None, max_context_len=0,
+               max_prefix_blocks=None):
     import paged_kv_cache_287_amd as pa
 
     gs = case.group_start
@@ -27,6 +28,8 @@ def gpu_shared(case, d, *, partition_tokens=0, workspace=None, max_context_len=0
     pa.pa_decode_shared_prefix(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                                d["context_lens"], dev(gs), dev(case.group_prefix_blocks),
                                float(case.scale), max_group_seqs=int(np.diff(gs).max()),
+                               max_prefix_blocks=max_prefix_blocks or
+                               max(1, int(case.group_prefix_blocks.max())),
                                k_scale=d["k_scale"], v_scale=d["v_scale"],
                                max_context_len=max_context_len or int(case.context_lens.max()),
                                partition_tokens=partition_tokens, workspace=workspace)
@@ -113,3 +116,16 @@ def test_deterministic_and_workspace_reuse():
     small = workloads.prefix_groups(100, [(4, 64, (1, 30))], 32, 8, 128, 16)
     out = gpu_shared(small, case_to_device(small), workspace=ws)
     assert_attention_close(out, oracle_decode(small), "shared-prefix after reuse")
+
+
+def test_long_prefix_in_several_slices_and_a_clamping_bound():
+    """A 2,048-token prefix is cut into 4 slices of 512 tokens, each its own partial; with a host
+    bound of 40 blocks the prefix pass covers only 640 tokens and the rest of the shared blocks
+    is decoded per sequence, which gives the same result."""
+    case = workloads.prefix_groups(111, [(6, 2048, (1, 100)), (2, 1024, (0, 10)), (1, 0, (5, 9))],
+                                   32, 8, 128, 16)
+    d = case_to_device(case)
+    ref = oracle_decode(case)
+    assert_attention_close(gpu_shared(case, d), ref, "shared-prefix 2048-token prefix")
+    assert_attention_close(gpu_shared(case, d, max_prefix_blocks=40), ref,
+                           "shared-prefix clamped to 40 blocks")
