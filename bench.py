@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of an MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8b_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_287_amd", "csrc", f)
-                  for f in ("decode.hip", "pa_internal.hpp")]
+                  for f in ("decode.hip", "decode_common.hpp", "pa_internal.hpp")]
 
 
 def progress(msg: str) -> None:
@@ -248,6 +248,15 @@ def main_prefill(args):
         e1.record(stream)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / n, e0.elapsed_time(e1) * 1e-3 / n
+
+    if args.calibrate:
+        progress("calibration copy: 3 x 256 MiB read + 256 MiB written")
+        src = torch.ones(2 ** 28, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     progress(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
