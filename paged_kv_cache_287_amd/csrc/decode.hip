@@ -11,8 +11,8 @@
 //   summary, prefill/decode paragraphs), so the kernel is organised around HBM traffic.
 //
 // Mapping onto CDNA4:
-//   * workgroup = (KV head [x GT query heads], sequence, 512-token context partition), 4 waves;
-//     each wave owns 128 consecutive tokens, walked in 16-token tiles.
+//   * workgroup = (KV head [x GT query heads], sequence, context partition), 4 waves; the
+//     partition's tokens are split evenly over the waves in 16-token tiles.
 //   * within a wave, each 16-lane row holds one token per step; lane `col` of the row holds
 //     elements [col*E, col*E+E) of that token (E = D/16). One step of the wave therefore loads
 //     4 consecutive token rows of a block: for D = 128 fp16 that is 1 KiB of contiguous memory
@@ -96,7 +96,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 
   const int hg = blockIdx.x;
   const int b = blockIdx.y;
-  const int part = blockIdx.z;
+  // partitions are dispatched last first: only long contexts have high partition indices, so
+  // their full workgroups start early instead of forming the tail of the grid
+  const int part = p.max_parts - 1 - (int)blockIdx.z;
   const int kvh = hg / p.head_groups;
   const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * GT;
   const SeqRange sr = seq_range<BS>(p, b);
@@ -104,7 +106,6 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   // partitions beyond the grid's (context longer than the host bound) are dropped, never
   // written outside the workspace
   const int part_tokens = p.part_tokens;
-  const int wave_tokens = part_tokens / kWaves;
   const int span = L - sr.start;
   const int nparts = min(span > 0 ? (span + part_tokens - 1) / part_tokens : 1, p.max_parts);
   if (part >= nparts) return;
@@ -127,7 +128,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   }
 
   // ---- block ids of this wave's tokens: lane j holds logical block lb0 + j ---------------
-  const int wbase = sr.start + part * part_tokens + wave * wave_tokens;
+  // The partition's tokens [p0, p0 + pn) are split evenly over the waves in whole tiles, so a
+  // short partition (the end of a context) keeps every wave busy. A full partition gives each
+  // wave part_tokens / 4 tokens. p0 is a multiple of the block size and share of the tile, so a
+  // tile never straddles a block of 16 tokens or more (and covers two whole blocks of 8), and
+  // a wave's range spans at most 64 blocks.
+  const int p0 = sr.start + part * part_tokens;
+  const int pn = max(0, min(L - p0, part_tokens));
+  const int share = (pn + kWaves * kTileTokens - 1) / (kWaves * kTileTokens) * kTileTokens;
+  const int wbase = p0 + wave * share;
+  const int woff = wbase % BS;  // lane j holds logical block wbase / BS + j
   const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
   int my_id = 0;
   if (wbase < L) {
@@ -156,8 +166,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int t = kTileTokens * i + kRows * s;  // first token of the step, wave-relative
-      const int id = __builtin_amdgcn_readlane(my_id, t / BS);
-      const size_t off = (size_t)id * blk_stride + (size_t)((t % BS) * ROW_BYTES + lane_off);
+      const int id = __builtin_amdgcn_readlane(my_id, (woff + t) / BS);
+      const size_t off = (size_t)id * blk_stride + (size_t)(((woff + t) % BS) * ROW_BYTES + lane_off);
       kc[s] = load_chunk<NWORDS, true>(kbase + off);
       vc[s] = load_chunk<NWORDS, true>(vbase + off);
     }
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
       vmul[s] = 1.f;
       if constexpr (KV8) {
         const int t = kTileTokens * i + kRows * s;
-        const int id = __builtin_amdgcn_readlane(my_id, t / BS);
+        const int id = __builtin_amdgcn_readlane(my_id, (woff + t) / BS);
         kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
         vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
       }
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   // Tiles [0, n_full) are complete; tile n_full is the masked tail when the context ends
   // inside this wave's range. Two register buffers alternate so the next tile's loads are in
   // flight while the current one is consumed.
-  const int avail = max(0, min(L - wbase, wave_tokens));
+  const int avail = max(0, min(p0 + pn - wbase, share));
   const int n_full = avail / kTileTokens;
   const bool has_tail = (avail % kTileTokens) != 0;
   const int n_tiles = n_full + (has_tail ? 1 : 0);

@@ -43,13 +43,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 
   const int hg = blockIdx.x;
   const int b = blockIdx.y;
-  const int part = blockIdx.z;
+  // partitions are dispatched last first: only long contexts have high partition indices, so
+  // their full workgroups start early instead of forming the tail of the grid
+  const int part = p.max_parts - 1 - (int)blockIdx.z;
   const int kvh = hg / p.head_groups;
   const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * R;
   const SeqRange sr = seq_range<BS>(p, b);
   const int L = sr.L;
   const int part_tokens = p.part_tokens;
-  const int wave_tokens = part_tokens / kWaves;
   const int span = L - sr.start;
   const int nparts = min(span > 0 ? (span + part_tokens - 1) / part_tokens : 1, p.max_parts);
   if (part >= nparts) return;
@@ -70,7 +71,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
           p.q + ((size_t)b * p.num_q_heads + h0 + 16 * nt + lr) * D + 32 * kk + 8 * lq);
 
   // ---- block ids of this wave's tokens: lane j holds logical block wbase / BS + j ------------
-  const int wbase = sr.start + part * part_tokens + wave * wave_tokens;
+  // The partition's tokens [p0, p0 + pn) are split evenly over the waves in whole tiles, so a
+  // short partition (the end of a context) keeps every wave busy. A full partition gives each
+  // wave part_tokens / 4 tokens. p0 is a multiple of the block size and share of the tile, so a
+  // tile never straddles a block of 16 tokens or more (and covers two whole blocks of 8), and
+  // a wave's range spans at most 64 blocks.
+  const int p0 = sr.start + part * part_tokens;
+  const int pn = max(0, min(L - p0, part_tokens));
+  const int share = (pn + kWaves * kTileTokens - 1) / (kWaves * kTileTokens) * kTileTokens;
+  const int wbase = p0 + wave * share;
+  const int woff = wbase % BS;  // lane j holds logical block wbase / BS + j
   const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
   int my_id = 0;
   if (wbase < L) {
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   // block of token (16 i + t) of tile i: uniform for BS >= 16; for BS = 8 the tile's second
   // half lies in the next block
   auto block_of = [&](int i, int t) -> int {
-    const int j0 = (kTileTokens * i) / BS;
+    const int j0 = (woff + kTileTokens * i) / BS;
     if constexpr (BS >= kTileTokens) {
       return __builtin_amdgcn_readlane(my_id, j0);
     } else {
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[KK], Chunk<NWORDS>(&vc)[KK]) {
     const int id = block_of(i, lr);
     const size_t off = (size_t)id * blk_stride +
-                       (size_t)(((kTileTokens * i + lr) % BS) * ROW_BYTES + lq * LANE_BYTES);
+                       (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES + lq * LANE_BYTES);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       kc[kk] = load_chunk<NWORDS, true>(kbase + off + kk * 32 * ESZ);
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   };
 
   // same double-buffered walk as the VALU kernel
-  const int avail = max(0, min(L - wbase, wave_tokens));
+  const int avail = max(0, min(p0 + pn - wbase, share));
   const int n_full = avail / kTileTokens;
   const bool has_tail = (avail % kTileTokens) != 0;
   const int n_tiles = n_full + (has_tail ? 1 : 0);

@@ -35,7 +35,9 @@ inline bool valid_part_tokens(int pt, int block_size) {
 
 // Query heads per workgroup. Groups of 16 or more query heads per KV head (MQA-like) stack 32 or
 // 16 of them into matrix-core tiles; smaller groups use the VALU kernel with the largest
-// compiled tile (8, 4, 2 or 1) dividing G.
+// compiled tile (8, 4, 2 or 1) dividing G. (Padding 4 or 8 rows into a 16-row matrix-core tile
+// was measured slower than the VALU kernel for fp16 and for E4M3 caches: the transposed V
+// operand costs more LDS reads than the dot products it replaces.)
 inline bool decode_uses_mfma(int group) { return group >= 16 && group % 16 == 0; }
 inline int decode_rows(int group) {
   if (decode_uses_mfma(group)) return group % 32 == 0 ? 32 : 16;
