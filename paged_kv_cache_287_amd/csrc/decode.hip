@@ -23,7 +23,10 @@
 //   * each row keeps its own online-softmax state (max, sum) per query head and a partial
 //     output of E floats per lane and head; rows and waves are merged once, through LDS, at the
 //     end of the partition. Scores are kept in log2 units (scale * log2 e folded in) so the
-//     exponentials are single v_exp_f32 instructions.
+//     exponentials are single v_exp_f32 instructions. The running maximum only moves when a
+//     score passes it by more than 8 (log2 units), which skips the rescaling of most tiles.
+//   * P.V: a lane's tokens of two steps are paired element by element, so one v_dot2 per
+//     element and head adds two tokens' contributions (probabilities rounded to fp16).
 //   * the block ids a wave needs are fetched once, one per lane, and read back with
 //     v_readlane, so the table walk costs no memory latency inside the tile loop; the next
 //     tile's K and V loads are issued before the current tile is consumed.
@@ -58,12 +61,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                 c, false);
 }
 
-__device__ __forceinline__ float half_lo(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-}
-__device__ __forceinline__ float half_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
 
 // Per-lane view of one token's elements as fp16 pairs (E/2 words).
 template <int E, bool KV8>
@@ -80,6 +77,10 @@ __device__ __forceinline__ void to_half_pairs(const Chunk<(KV8 ? E : 2 * E) / 4>
     }
   }
 }
+
+// Largest step of a row's score above the running-max reference before l and acc are
+// rescaled (log2 units): probabilities stay below 256.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D, int BS, int GT, bool KV8>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
@@ -207,38 +208,57 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
         sc[s][h] = valid ? x : kNegInf;
       }
     }
-    // online softmax: new running max, rescale, exponentiate this tile's scores
+    // Online softmax. The running maximum m is only the reference point of l and acc (both are
+    // sums of 2^(s - m) terms), so it moves, and l and acc are rescaled, only when some row's
+    // score exceeds it by more than kRescaleSlack; probabilities then stay below 2^kRescaleSlack.
+    // The decision is wave-uniform and the result is the same softmax up to rounding.
     float pw[kSteps][GT];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       const float mt = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
-      const float mn = fmaxf(m[h], mt);
-      const float ms = (masked && mn == kNegInf) ? 0.f : mn;
-      const float alpha = fexp2(m[h] - ms);
+      if (__builtin_amdgcn_ballot_w64(mt > m[h] + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m[h], mt);
+        const float alpha = fexp2(m[h] - (mn == kNegInf ? 0.f : mn));
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+        m[h] = mn;
+      }
+      const float ms = m[h] == kNegInf ? 0.f : m[h];
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) pw[s][h] = fexp2(sc[s][h] - ms);
-      l[h] = l[h] * alpha + ((pw[0][h] + pw[1][h]) + (pw[2][h] + pw[3][h]));
-      m[h] = mn;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+      l[h] += (pw[0][h] + pw[1][h]) + (pw[2][h] + pw[3][h]);
     }
-    // weighted value sum
+    // Weighted value sum as fp16 dot products over token pairs: the lane's tokens of steps 2j
+    // and 2j + 1 are paired element by element (byte permutes), the two probabilities rounded
+    // to fp16, and one v_dot2 per element and head adds both tokens.
+    uint32_t vh[kSteps][NH2];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      uint32_t vh[NH2];
-      to_half_pairs<E, KV8>(vc[s], vh);
+      to_half_pairs<E, KV8>(vc[s], vh[s]);
       if (masked) {
         const bool valid = tok0 + kRows * s + row < L;
 #pragma unroll
-        for (int w = 0; w < NH2; ++w) vh[w] = valid ? vh[w] : 0u;
+        for (int w = 0; w < NH2; ++w) vh[s][w] = valid ? vh[s][w] : 0u;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSteps / 2; ++j) {
+      uint32_t lo[NH2], hi[NH2];
+#pragma unroll
+      for (int w = 0; w < NH2; ++w) {
+        lo[w] = __builtin_amdgcn_perm(vh[2 * j + 1][w], vh[2 * j][w], 0x05040100u);
+        hi[w] = __builtin_amdgcn_perm(vh[2 * j + 1][w], vh[2 * j][w], 0x07060302u);
       }
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float pv = KV8 ? pw[s][h] * vmul[s] : pw[s][h];
+        const float p0 = KV8 ? pw[2 * j][h] * vmul[2 * j] : pw[2 * j][h];
+        const float p1 = KV8 ? pw[2 * j + 1][h] * vmul[2 * j + 1] : pw[2 * j + 1][h];
+        const uint32_t pp = __builtin_bit_cast(uint32_t, half2_t{(_Float16)p0, (_Float16)p1});
 #pragma unroll
         for (int w = 0; w < NH2; ++w) {
-          acc[h][2 * w] = fmaf(pv, half_lo(vh[w]), acc[h][2 * w]);
-          acc[h][2 * w + 1] = fmaf(pv, half_hi(vh[w]), acc[h][2 * w + 1]);
+          acc[h][2 * w] = dot2(lo[w], pp, acc[h][2 * w]);
+          acc[h][2 * w + 1] = dot2(hi[w], pp, acc[h][2 * w + 1]);
         }
       }
     }
