@@ -32,6 +32,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaveRows = 32;                        // query rows per wave (two 16-row tiles)
+constexpr float kRescaleSlack = 8.f;                 // log2 units
 constexpr int kTileTok = 64;                         // attended tokens per LDS tile
 static_assert(kPrefillRows == kWaves * kWaveRows, "rows per workgroup");
 
@@ -180,13 +181,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   const size_t blk_stride = (size_t)p.num_kv_heads * TILE_BYTES;
   Chunk<NWORDS> kr[TPT], vr[TPT];
 
+  // A thread's TPT tokens start at a multiple of 4, so they share one block (block sizes are
+  // multiples of 8): one id lookup per tile. Tokens past kv_end re-read the last token before
+  // it (in bounds; masked later).
   auto issue = [&](int tile) {
+    const int t0 = tile * kTileTok + st0;
+    const int tc = min(t0, kv_end - 1);
+    const int last = max(0, kv_end - 1 - t0);
+    const size_t off = (size_t)ids[tc / BS - blk0] * blk_stride + (size_t)(tc % BS) * ROW_BYTES;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-      const int t = min(tile * kTileTok + st0 + u, kv_end - 1);
-      const size_t off = (size_t)ids[t / BS - blk0] * blk_stride + (size_t)(t % BS) * ROW_BYTES;
-      kr[u] = load_chunk<NWORDS>(kbase + off);
-      vr[u] = load_chunk<NWORDS>(vbase + off);
+      const size_t o = off + (size_t)min(u, last) * ROW_BYTES;
+      kr[u] = load_chunk<NWORDS>(kbase + o);
+      vr[u] = load_chunk<NWORDS>(vbase + o);
     }
   };
 
@@ -209,10 +216,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  auto compute = [&](int tile) {
+  // masked: the tile reaches some row's causal limit (a uniform branch around the selects)
+  auto compute = [&](int tile, bool masked) {
     const int tok0 = tile * kTileTok;
-    if (tok0 > wpos_hi) return;  // every token of the tile is in this wave's causal future
-    const bool masked = tok0 + kTileTok - 1 > wpos_lo;
     float kmul[4], vmul[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -247,21 +253,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float sv[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sv[s][ii] = sacc[nt][s][ii] * kmul[s];
+      if (masked) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            if (tok0 + 16 * s + 4 * lq + ii > pos[nt]) sv[s][ii] = kNegInf;
+      }
       float tm = kNegInf;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int t = tok0 + 16 * s + 4 * lq + ii;
-          const bool valid = !masked || t <= pos[nt];
-          sv[s][ii] = valid ? sacc[nt][s][ii] * kmul[s] : kNegInf;
-          tm = fmaxf(tm, sv[s][ii]);
-        }
+        for (int ii = 0; ii < 4; ++ii) tm = fmaxf(tm, sv[s][ii]);
       tm = fmaxf(tm, __shfl_xor(tm, 16));
       tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mn = fmaxf(m[nt], tm);
-      const float ms = mn == kNegInf ? 0.f : mn;
-      const float alpha = fexp2(m[nt] - ms);
+      // the running max is the reference of l and o; it moves (with a rescale) only when a
+      // score passes it by more than kRescaleSlack (wave-uniform decision), so most tiles skip
+      // the rescale; probabilities stay below 2^kRescaleSlack
+      if (__builtin_amdgcn_ballot_w64(tm > m[nt] + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m[nt], tm);
+        const float alpha = fexp2(m[nt] - (mn == kNegInf ? 0.f : mn));
+        l[nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+        m[nt] = mn;
+      }
+      const float ms = m[nt] == kNegInf ? 0.f : m[nt];
       float pw[4][4];
       float ps = 0.f;
 #pragma unroll
@@ -271,10 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
           pw[s][ii] = fexp2(sv[s][ii] - ms);
           ps += pw[s][ii];
         }
-      l[nt] = l[nt] * alpha + ps;
-      m[nt] = mn;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+      l[nt] += ps;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int s0 = 2 * ks, s1 = 2 * ks + 1;
@@ -306,7 +324,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     stage();
     __syncthreads();
     if (i + 1 < tile_hi) issue(i + 1);
-    compute(i);
+    const int tok0 = i * kTileTok;
+    if (tok0 > wpos_hi) continue;  // every token of the tile is in this wave's causal future
+    compute(i, tok0 + kTileTok - 1 > wpos_lo);
   }
 
   // ---- normalise and write this wave's rows ------------------------------------------------
