@@ -143,6 +143,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   }
 
   // ---- this wave's query rows as the B operand of S^T = K Q^T -------------------------------
+  // A negative softmax scale is applied as |scale| with the query negated (exact in fp16), so
+  // the per-score multiplier is positive and the row max can be taken before scaling.
+  const float qscale = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   const int wrow0 = row0 + wave * kWaveRows;
   h8 qb[NT][KK];
   int pos[NT];
@@ -155,8 +159,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     pos[nt] = ok ? (PREFIX ? base : base + j) : -1;
     const _Float16* qrow = p.q + ((size_t)(qs + j) * p.num_q_heads + h) * D + 8 * lq;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qb[nt][kk] = ok ? *reinterpret_cast<const h8*>(qrow + 32 * kk) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk) : u32x4{0, 0, 0, 0};
+      w ^= qsign;
+      qb[nt][kk] = __builtin_bit_cast(h8, w);
+    }
   }
   // positions of the wave's first and last valid rows (rows are in token order)
   const int wpos_lo = PREFIX ? base : base + wrow0 / G;
@@ -164,14 +171,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
       wrow0 < nrows ? (PREFIX ? base : base + (min(wrow0 + kWaveRows, nrows) - 1) / G) : -1;
 
   float m[NT], l[NT];
-  f4 o[NT][MT];
+  f4 o[NT][MT], osum[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = kNegInf;
     l[nt] = 0.f;
+    osum[nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
   }
+  // A operand whose row 0 is all ones (lanes lr == 0 hold row 0's eight slots)
+  const _Float16 one = lr == 0 ? (_Float16)1.f : (_Float16)0.f;
+  const h8 ones = h8{one, one, one, one, one, one, one, one};
 
   // ---- staging: thread -> (TPT consecutive tokens, one 8-element chunk of d) ------------------
   const int sch = tid % DCH;
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     float kmul[4], vmul[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      kmul[s] = p.scale_log2;
+      kmul[s] = qscale;
       vmul[s] = 1.f;
       if constexpr (KV8) {
         // a lane's four tokens 16s + 4lq .. +3 share one block (block sizes are multiples of 4)
@@ -252,11 +263,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
     h8 pB[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      // raw scores; the multiplier goes into the exponent's fma (and, with one multiplier for
+      // the whole tile, after the max)
       float sv[4][4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sv[s][ii] = sacc[nt][s][ii] * kmul[s];
+        for (int ii = 0; ii < 4; ++ii) sv[s][ii] = sacc[nt][s][ii];
       if (masked) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -268,7 +281,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) tm = fmaxf(tm, sv[s][ii]);
+        for (int ii = 0; ii < 4; ++ii) tm = fmaxf(tm, KV8 ? sv[s][ii] * kmul[s] : sv[s][ii]);
+      if constexpr (!KV8) tm *= qscale;
       tm = fmaxf(tm, __shfl_xor(tm, 16));
       tm = fmaxf(tm, __shfl_xor(tm, 32));
       // the running max is the reference of l and o; it moves (with a rescale) only when a
@@ -278,21 +292,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         const float mn = fmaxf(m[nt], tm);
         const float alpha = fexp2(m[nt] - (mn == kNegInf ? 0.f : mn));
         l[nt] *= alpha;
+        if constexpr (!KV8) osum[nt] *= alpha;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
         m[nt] = mn;
       }
-      const float ms = m[nt] == kNegInf ? 0.f : m[nt];
+      const float nms = m[nt] == kNegInf ? 0.f : -m[nt];
       float pw[4][4];
-      float ps = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          pw[s][ii] = fexp2(sv[s][ii] - ms);
-          ps += pw[s][ii];
-        }
-      l[nt] += ps;
+        for (int ii = 0; ii < 4; ++ii) pw[s][ii] = fexp2(fmaf(sv[s][ii], kmul[s], nms));
+      if constexpr (KV8) {
+        // the probabilities going to the matrix cores carry the V scale, so the row sums are
+        // taken here; without it they come out of the P.V product (osum)
+        float ps = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) ps += pw[s][ii];
+        l[nt] += ps;
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int s0 = 2 * ks, s1 = 2 * ks + 1;
@@ -302,9 +322,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
                         (_Float16)(pw[s1][2] * vmul[s1]), (_Float16)(pw[s1][3] * vmul[s1])};
       }
     }
-    // O^T += V^T P^T, 32 tokens per product
+    // O^T += V^T P^T, 32 tokens per product; for an fp16 cache one more product with an
+    // all-ones row in place of V^T accumulates the row sums of P (osum, element 0 of lanes
+    // lq == 0), on the matrix cores instead of 32 adds per tile
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int d = 16 * mt + lr;
@@ -313,6 +335,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
         for (int nt = 0; nt < NT; ++nt)
           o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vA, pB[nt][ks], o[nt][mt], 0, 0, 0);
       }
+      if constexpr (!KV8) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          osum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pB[nt][ks], osum[nt], 0, 0, 0);
+      }
+    }
   };
 
   __syncthreads();  // ids visible
@@ -332,9 +360,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
   // ---- normalise and write this wave's rows ------------------------------------------------
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float lt = l[nt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    float lt;
+    if constexpr (KV8) {
+      lt = l[nt];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+    } else {
+      lt = __shfl(osum[nt][0], lr);  // row lr's sum sits in lane lr (lq == 0), element 0
+    }
     const int r = wrow0 + 16 * nt + lr;
     if (r >= nrows) continue;
     const int j = r / G;

@@ -196,3 +196,12 @@ def test_prefill_longest_supported_context():
                              np.array([0, 1], dtype=np.int32), c.scale)
         err = np.abs(out[row] - ref[0])
         assert (err <= 2e-3 + 2e-3 * np.abs(ref[0])).all(), (b, j, float(err.max()))
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+def test_prefill_negative_scale(kv):
+    """A negative softmax scale is legal input; the kernel applies |scale| to negated queries."""
+    pc = w.prefill_case(900, CTX, CHUNK, 32, 8, 128, 16, kv_dtype=kv)
+    pc.cache.scale = np.float32(-0.07)
+    out = gpu_prefill(pc)
+    assert_attention_close(out, oracle_prefill(pc), f"prefill scale<0 {kv}")

@@ -129,3 +129,10 @@ def test_long_prefix_in_several_slices_and_a_clamping_bound():
     assert_attention_close(gpu_shared(case, d), ref, "shared-prefix 2048-token prefix")
     assert_attention_close(gpu_shared(case, d, max_prefix_blocks=40), ref,
                            "shared-prefix clamped to 40 blocks")
+
+
+def test_negative_scale():
+    case = workloads.prefix_groups(120, GROUPS, 32, 8, 128, 16)
+    case.scale = np.float32(-0.05)
+    out = gpu_shared(case, case_to_device(case))
+    assert_attention_close(out, oracle_decode(case), "shared-prefix scale<0")
