@@ -142,43 +142,94 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
   __syncthreads();
   if (!s_last) return;
 
-  // exact merge: out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p
-  for (int idx = tid; idx < R * D; idx += NTHREADS) {
-    const int h = idx / D, d = idx - h * D;
-    const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
-    const float* ml = p.ws_ml + row0 * 2;
-    const float* ac = p.ws_acc + row0 * D + d;
-    // partitions are taken kChunk at a time with all their loads in flight together, merged
-    // into a running (max, sum, value) exactly as the tiles were
-    constexpr int kChunk = 8;
-    float mx = kNegInf, ls = 0.f, a = 0.f;
-    const int nslots = nparts + extra;
-    for (int i0 = 0; i0 < nslots; i0 += kChunk) {
-      float mv[kChunk], lv[kChunk], av[kChunk];
+  // exact merge: out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+  // Partitions are taken kChunk at a time with all their loads in flight together (each round
+  // trip is a full memory latency: the loads bypass the caches) and merged into a running
+  // (max, sum, value) exactly as the tiles were.
+  constexpr int kChunk = 8;
+  const int nslots = nparts + extra;
+  if constexpr (R >= 16) {
+    // many rows: a thread takes UE dims of one row (d0, d0 + TPR, ...), so the (max, sum)
+    // loads and the merge weights are shared by its UE elements, neighbouring lanes still read
+    // neighbouring dims, and each pass over R / RPP rows is one round trip
+    constexpr int UE = (R * D) / NTHREADS < 8 ? (R * D) / NTHREADS : 8;
+    constexpr int TPR = D / UE;            // threads per row
+    constexpr int RPP = NTHREADS / TPR;    // rows per pass
+    static_assert(D % UE == 0 && NTHREADS % TPR == 0 && R % RPP == 0, "merge tiling");
+    for (int h = tid / TPR; h < R; h += RPP) {
+      const int d0 = tid % TPR;
+      const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
+      const float* ml = p.ws_ml + row0 * 2;
+      const float* ac = p.ws_acc + row0 * D + d0;
+      float mx = kNegInf, ls = 0.f, a[UE];
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        const bool in = i0 + j < nslots;
-        const int i = in ? i0 + j : i0;
-        mv[j] = fetch(ml + 2 * i);
-        lv[j] = fetch(ml + 2 * i + 1);
-        av[j] = fetch(ac + (size_t)i * D);
-        if (!in) mv[j] = kNegInf;
+      for (int u = 0; u < UE; ++u) a[u] = 0.f;
+      for (int i0 = 0; i0 < nslots; i0 += kChunk) {
+        float mv[kChunk], lv[kChunk], av[kChunk][UE];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const bool in = i0 + j < nslots;
+          const int i = in ? i0 + j : i0;
+          mv[j] = fetch(ml + 2 * i);
+          lv[j] = fetch(ml + 2 * i + 1);
+#pragma unroll
+          for (int u = 0; u < UE; ++u) av[j][u] = fetch(ac + (size_t)i * D + u * TPR);
+          if (!in) mv[j] = kNegInf;
+        }
+        float mc = mx;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
+        const float r = fexp2(mx - mc);  // mx = -inf only before the first chunk: r = 0
+        ls *= r;
+#pragma unroll
+        for (int u = 0; u < UE; ++u) a[u] *= r;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const float w = fexp2(mv[j] - mc);
+          ls = fmaf(w, lv[j], ls);
+#pragma unroll
+          for (int u = 0; u < UE; ++u) a[u] = fmaf(w, av[j][u], a[u]);
+        }
+        mx = mc;
       }
-      float mc = mx;
+      _Float16* o = p.out + ((size_t)b * p.num_q_heads + h0 + h) * D + d0;
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
-      const float r = fexp2(mx - mc);  // mx = -inf only before the first chunk: r = 0
-      ls *= r;
-      a *= r;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        const float w = fexp2(mv[j] - mc);
-        ls = fmaf(w, lv[j], ls);
-        a = fmaf(w, av[j], a);
-      }
-      mx = mc;
+      for (int u = 0; u < UE; ++u) o[u * TPR] = (_Float16)(a[u] / ls);
     }
-    p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(a / ls);
+  } else {
+    for (int idx = tid; idx < R * D; idx += NTHREADS) {
+      const int h = idx / D, d = idx - h * D;
+      const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
+      const float* ml = p.ws_ml + row0 * 2;
+      const float* ac = p.ws_acc + row0 * D + d;
+      float mx = kNegInf, ls = 0.f, a = 0.f;
+      for (int i0 = 0; i0 < nslots; i0 += kChunk) {
+        float mv[kChunk], lv[kChunk], av[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const bool in = i0 + j < nslots;
+          const int i = in ? i0 + j : i0;
+          mv[j] = fetch(ml + 2 * i);
+          lv[j] = fetch(ml + 2 * i + 1);
+          av[j] = fetch(ac + (size_t)i * D);
+          if (!in) mv[j] = kNegInf;
+        }
+        float mc = mx;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
+        const float r = fexp2(mx - mc);
+        ls *= r;
+        a *= r;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+          const float w = fexp2(mv[j] - mc);
+          ls = fmaf(w, lv[j], ls);
+          a = fmaf(w, av[j], a);
+        }
+        mx = mc;
+      }
+      p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(a / ls);
+    }
   }
 }
 

@@ -54,6 +54,8 @@ def test_partition_choice_and_workspace_size():
     # at most half the longest context: 2048-token contexts split at least in two
     assert pa.decode_partition_tokens(64, 32, 32, 128, 16, 2048) == 1024
     assert pa.decode_partition_tokens(100, 32, 8, 128, 16, 1409) == 512
+    # matrix-core decode (G = 16k) aims at one workgroup per CU: MQA 64 x 2048 -> 4 partitions
+    assert pa.decode_partition_tokens(64, 32, 1, 128, 16, 2048) == 512
     # few sequences: smaller partitions for parallelism, down to 256
     assert pa.decode_partition_tokens(1, 32, 8, 128, 16, 4096) == 256
     assert pa.decode_partition_tokens(4, 32, 8, 128, 16, 32768) == 1024
