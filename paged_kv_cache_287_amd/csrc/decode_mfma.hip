@@ -12,10 +12,11 @@
 //     tokens 4(l/16)..4(l/16)+3, so the online softmax (running max / sum per row, as in the
 //     FlashAttention paragraph of the same talk summary) needs only two cross-row exchanges.
 //   * O^T += V^T P^T with v_mfma_f32_16x16x16_f16: B = P^T is exactly the probabilities each
-//     lane just computed (converted to fp16); A = V^T comes from the V tile staged through a
-//     padded per-wave LDS buffer (V is stored dim-contiguous, the operand wants 4 tokens of one
-//     dim per lane). The accumulator lane l holds row l%16, so rescaling by the running max is
-//     lane-local.
+//     lane just computed (converted to fp16); A = V^T comes from a per-wave LDS tile stored
+//     transposed ([dim][token]): each lane loads 4 (or 2) consecutive tokens of one 8-dim chunk
+//     of V and stores them as one 8-byte write per dim, and the operand (4 tokens of one dim)
+//     is one 8-byte read. The accumulator lane l holds row l%16, so rescaling by the running
+//     max is lane-local.
 // Everything else (partitioning, block-id walk, double-buffered non-temporal loads, fp8 scales,
 // merge through LDS, partial publish / last-arrival merge) follows the VALU kernel.
 #include "decode_common.hpp"
@@ -25,11 +26,15 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 template <int D, int BS, int NT, bool KV8>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p) {
   constexpr int R = 16 * NT;         // query rows of one KV head handled by a workgroup
+  constexpr int TPL = D / 32;        // consecutive V tokens a lane loads (one 8-dim chunk)
+  constexpr int VTS = 20;            // V^T row stride in halves (16 tokens + 4): the staging
+                                     // stores and the operand reads are both bank-conflict free
   constexpr int KK = D / 32;         // 32-dim steps of QK
   constexpr int MT = D / 16;         // 16-dim slices of the output
   constexpr int ESZ = KV8 ? 1 : 2;   // bytes per cached element
@@ -37,8 +42,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   constexpr int TILE_BYTES = BS * ROW_BYTES;
   constexpr int LANE_BYTES = 8 * ESZ;  // 8 elements per lane per step
   constexpr int NWORDS = LANE_BYTES / 4;
-  constexpr int VRS = D + 8;         // staged V row stride in halves: rows stay 16-byte aligned
-                                     // and the 4 token groups of a read fall on different banks
   static_assert(BS % kRows == 0, "block size");
 
   const int hg = blockIdx.x;
@@ -115,23 +118,32 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // LDS: a per-wave staging tile for V, reused after the loop for the workgroup merge
+  // LDS: a per-wave transposed V tile ([dim][token]), reused after the loop for the merge
   constexpr int kMergeFloats = kWaves * R * (D + 2);
-  static_assert(kWaves * kTileTokens * VRS * 2 <= kMergeFloats * 4, "staging fits the merge area");
+  static_assert(kWaves * D * VTS * 2 <= kMergeFloats * 4, "staging fits the merge area");
   __shared__ __align__(16) float smem[kMergeFloats];
-  _Float16* vst = reinterpret_cast<_Float16*>(smem) + wave * kTileTokens * VRS;
+  _Float16* vt = reinterpret_cast<_Float16*>(smem) + wave * D * VTS;
 
-  Chunk<NWORDS> ka[KK], va[KK], kb[KK], vb[KK];
+  // K is loaded in the MFMA operand layout; V as TPL consecutive tokens of one 8-dim chunk per
+  // lane, so that it is stored transposed with one TPL-half store per dim
+  const int vch = lane / (16 / TPL);   // 8-dim chunk
+  const int vtg = lane % (16 / TPL);   // token group: tokens TPL vtg .. +TPL-1
+  Chunk<NWORDS> ka[KK], va[TPL], kb[KK], vb[TPL];
 
-  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[KK], Chunk<NWORDS>(&vc)[KK]) {
+  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[KK], Chunk<NWORDS>(&vc)[TPL]) {
     const int id = block_of(i, lr);
     const size_t off = (size_t)id * blk_stride +
                        (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES + lq * LANE_BYTES);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      kc[kk] = load_chunk<NWORDS, true>(kbase + off + kk * 32 * ESZ);
-      vc[kk] = load_chunk<NWORDS, true>(vbase + off + kk * 32 * ESZ);
-    }
+    for (int kk = 0; kk < KK; ++kk) kc[kk] = load_chunk<NWORDS, true>(kbase + off + kk * 32 * ESZ);
+    // a lane's TPL tokens start at a multiple of TPL, so they share one block
+    const int vid = block_of(i, TPL * vtg);
+    const size_t voff = (size_t)vid * blk_stride +
+                        (size_t)(((woff + kTileTokens * i + TPL * vtg) % BS) * ROW_BYTES +
+                                 vch * LANE_BYTES);
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+      vc[u] = load_chunk<NWORDS, true>(vbase + voff + (size_t)u * ROW_BYTES);
   };
 
   // 8 elements of a chunk as fp16 (E4M3 codes decode exactly)
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     return __builtin_bit_cast(h8, w);
   };
 
-  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[KK], const Chunk<NWORDS>(&vc)[KK],
+  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[KK], const Chunk<NWORDS>(&vc)[TPL],
                           bool masked) {
     const int tok0 = wbase + kTileTokens * i;
     // per-token multipliers: softmax scale (and the K / V block scales of an E4M3 cache) for
@@ -194,22 +206,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       pB[nt] = h4{(_Float16)(pw[0] * vmul), (_Float16)(pw[1] * vmul), (_Float16)(pw[2] * vmul),
                   (_Float16)(pw[3] * vmul)};
     }
-    // stage V (token lr, dims 32 kk + 8 lq .. +8) as fp16; tokens past the context are zeros so
-    // that stale or poisoned slots cannot reach the sums
-    const bool vvalid = !masked || (tok0 + lr < L);
+    // stage V transposed as fp16: dim 8 vch + e gets this lane's TPL tokens in one store;
+    // tokens past the context are zeros so that stale or poisoned slots cannot reach the sums
+    h8 vv[TPL];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      h8 vv = to_h8(vc[kk]);
-      if (!vvalid) vv = h8{0, 0, 0, 0, 0, 0, 0, 0};
-      *reinterpret_cast<h8*>(vst + lr * VRS + 32 * kk + 8 * lq) = vv;
+    for (int u = 0; u < TPL; ++u) {
+      vv[u] = to_h8(vc[u]);
+      if (masked && tok0 + TPL * vtg + u >= L) vv[u] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16* dst = vt + (8 * vch + e) * VTS + TPL * vtg;
+      if constexpr (TPL == 4)
+        *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
+      else
+        *reinterpret_cast<h2v*>(dst) = h2v{vv[0][e], vv[1][e]};
     }
     __builtin_amdgcn_wave_barrier();
-    // O^T[dim][row] += V^T[dim][token] P^T[token][row], 16 dims at a time
+    // O^T[dim][row] += V^T[dim][token] P^T[token][row], 16 dims at a time; the A operand (dim
+    // 16 mt + lr, tokens 4 lq .. +3) is one 8-byte read
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      h4 vA;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vA[j] = vst[(4 * lq + j) * VRS + 16 * mt + lr];
+      const h4 vA = *reinterpret_cast<const h4*>(vt + (16 * mt + lr) * VTS + 4 * lq);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vA, pB[nt], o[nt][mt], 0, 0, 0);
@@ -234,10 +252,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     if (has_tail) issue_tile(i + 1, kb, vb);
     consume_tile(i, ka, va, false);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      ka[kk] = kb[kk];
-      va[kk] = vb[kk];
-    }
+    for (int kk = 0; kk < KK; ++kk) ka[kk] = kb[kk];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) va[u] = vb[u];
     ++i;
   }
   if (has_tail) consume_tile(i, ka, va, true);
