@@ -255,8 +255,10 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
  *     enc(x / s) and scale[blk, h] = s. enc clamps to [-448, 448] and rounds to nearest even.
  * The scale thus stays >= the block's max |value| / 448, the rule used to quantize whole blocks.
  *
- * Precondition (not checked): non-negative slots are distinct; for E4M3 caches at most one
- * token per block per call (one decode step appends one token per sequence).
+ * For E4M3 caches, consecutive tokens of the call that land in the same block (a run, e.g. a
+ * prefill chunk's tokens in order) are applied in that order, each under the policy above.
+ * Precondition (not checked): non-negative slots are distinct; for E4M3 caches the tokens that
+ * land in one block are consecutive in the call.
  * Validated: pointers (scales NULL for fp16, non-NULL for E4M3), 16-byte alignment of k, v,
  * caches; 8-byte alignment of slot_mapping; sizes; num_blocks * block_size < 2^31.
  */

@@ -75,7 +75,7 @@ def kv_write_fp8(k: np.ndarray, v: np.ndarray, k_codes: np.ndarray, v_codes: np.
 
     The pages give no scale policy for appending to an 8-bit cache; the one computed here keeps
     each scale an upper bound of its block's content over 448, the rule the input quantizer
-    uses. For each token (at most one per block per call) and KV head, all in float32:
+    uses. For each token, in the order of the call, and KV head, all in float32:
 
     * ``s_prev`` = the block's scale, or 0 when the token lands at offset 0 (a fresh block);
     * ``a`` = max |x| over the token's row; ``s = a / 448`` if ``a > s_prev * 448``, else

@@ -48,8 +48,9 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint4* __restrict__
 //   a = max |x| over the token's row; s = a / 448 if a > s_prev * 448 else s_prev; s = 1 if 0;
 //   if s changed and earlier tokens exist, their codes c become enc((dec(c) * s_prev) / s);
 //   the token is stored as enc(x / s); enc clamps to +-448 and rounds to nearest-even.
-// All arithmetic is fp32 with IEEE division. At most one token per block per call (a decode
-// step appends one token per sequence, and sequences never write into a shared block).
+// All arithmetic is fp32 with IEEE division. Tokens of one call that land in the same block are
+// applied in call order (they must be consecutive in the call: a decode step's single token, or
+// a prefill chunk's tokens in order); sequences never write into a shared block.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float e4m3_max() { return 448.f; }
@@ -67,53 +68,71 @@ template <int D>
 __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
     const _Float16* __restrict__ k, const _Float16* __restrict__ v, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
-    const int64_t* __restrict__ slot_mapping, int num_kv_heads, int block_size, int64_t num_slots) {
-  constexpr int PER = D / 64;  // elements per lane: 2 (D 128) or 1 (D 64)
-  const int t = blockIdx.x / num_kv_heads;
-  const int h = blockIdx.x - t * num_kv_heads;
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int off = (int)(slot - blk * block_size);
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int block_size,
+    int64_t num_slots) {
+  constexpr int PER = D / 64;  // bytes (elements) a lane owns in every row: 2 (D 128) or 1 (D 64)
+  const int t0 = blockIdx.x / num_kv_heads;
+  const int h = blockIdx.x - t0 * num_kv_heads;
+  const int64_t slot0 = slot_mapping[t0];
+  if (slot0 < 0 || slot0 >= num_slots) return;
+  const int64_t blk = slot0 / block_size;
+  // Consecutive tokens of the call that land in one block form a run; the wave of the run's
+  // first token applies them in order (the scale policy is sequential within a block).
+  if (t0 > 0) {
+    const int64_t sp = slot_mapping[t0 - 1];
+    if (sp >= 0 && sp < num_slots && sp / block_size == blk) return;
+  }
   const int lane = threadIdx.x;
   for (int which = 0; which < 2; ++which) {
-    const _Float16* row = (which == 0 ? k : v) + ((size_t)t * num_kv_heads + h) * D;
     uint8_t* tile = (which == 0 ? k_cache : v_cache) + ((size_t)blk * num_kv_heads + h) * block_size * D;
     float* sc = (which == 0 ? k_scale : v_scale) + (size_t)blk * num_kv_heads + h;
-    float x[PER];
-    float amax = 0.f;
+    // The block's scale is carried through the run in a (wave-uniform) register, and every lane
+    // only ever touches its own PER bytes of each row, so no lane reads what another wrote.
+    float s_cur = 0.f;
+    for (int t = t0; t < num_tokens; ++t) {
+      const int64_t slot = t == t0 ? slot0 : slot_mapping[t];
+      if (t > t0 && (slot < 0 || slot >= num_slots || slot / block_size != blk)) break;
+      const int off = (int)(slot - blk * block_size);
+      const _Float16* row = (which == 0 ? k : v) + ((size_t)t * num_kv_heads + h) * D;
+      float x[PER];
+      float amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      x[e] = (float)row[lane * PER + e];
-      amax = fmaxf(amax, fabsf(x[e]));
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    const float s_prev = off == 0 ? 0.f : *sc;
-    float s = amax > s_prev * e4m3_max() ? amax / e4m3_max() : s_prev;
-    if (s == 0.f) s = 1.f;
-    if (s != s_prev && off > 0) {
-      // re-encode the codes already in the block, four per lane per step
-      uint32_t* words = reinterpret_cast<uint32_t*>(tile);
-      const int nwords = off * D / 4;
-      for (int i = lane; i < nwords; i += 64) {
-        const uint32_t w = words[i];
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-        uint32_t o = enc_pair<false>((lo.x * s_prev) / s, (lo.y * s_prev) / s, 0u);
-        o = enc_pair<true>((hi.x * s_prev) / s, (hi.y * s_prev) / s, o);
-        words[i] = o;
+      for (int e = 0; e < PER; ++e) {
+        x[e] = (float)row[lane * PER + e];
+        amax = fmaxf(amax, fabsf(x[e]));
       }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+      const float s_prev = off == 0 ? 0.f : (t == t0 ? *sc : s_cur);
+      float s = amax > s_prev * e4m3_max() ? amax / e4m3_max() : s_prev;
+      if (s == 0.f) s = 1.f;
+      if (s != s_prev && off > 0) {
+        // re-encode the codes already in the block (this lane's bytes of rows 0 .. off-1)
+        for (int r = 0; r < off; ++r) {
+          uint8_t* p = tile + (size_t)r * D + lane * PER;
+          if constexpr (PER == 2) {
+            const uint32_t w = *reinterpret_cast<const uint16_t*>(p);
+            const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+            *reinterpret_cast<uint16_t*>(p) =
+                (uint16_t)(enc_pair<false>((c.x * s_prev) / s, (c.y * s_prev) / s, 0u) & 0xFFFFu);
+          } else {
+            const uint32_t w = *p;
+            const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+            *p = (uint8_t)(enc_pair<false>((c.x * s_prev) / s, 0.f, 0u) & 0xFFu);
+          }
+        }
+      }
+      uint8_t* dst = tile + (size_t)off * D + lane * PER;
+      if constexpr (PER == 2) {
+        const uint32_t o = enc_pair<false>(x[0] / s, x[1] / s, 0u);
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(o & 0xFFFFu);
+      } else {
+        const uint32_t o = enc_pair<false>(x[0] / s, 0.f, 0u);
+        *dst = (uint8_t)(o & 0xFFu);
+      }
+      s_cur = s;
     }
-    uint8_t* dst = tile + (size_t)off * D + lane * PER;
-    if constexpr (PER == 2) {
-      const uint32_t o = enc_pair<false>(x[0] / s, x[1] / s, 0u);
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(o & 0xFFFFu);
-    } else {
-      const uint32_t o = enc_pair<false>(x[0] / s, 0.f, 0u);
-      *dst = (uint8_t)(o & 0xFFu);
-    }
-    if (lane == 0) *sc = s;
+    if (lane == 0) *sc = s_cur;
   }
 }
 
@@ -210,10 +229,12 @@ hipError_t launch_kv_write_fp8(const void* k, const void* v, void* k_cache, void
   auto vc = static_cast<uint8_t*>(v_cache);
   if (head_dim == 128)
     kv_write_fp8_kernel<128><<<grid, 64, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
-                                                      slot_mapping, num_kv_heads, block_size, slots);
+                                                      slot_mapping, num_tokens, num_kv_heads,
+                                                      block_size, slots);
   else
     kv_write_fp8_kernel<64><<<grid, 64, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
-                                                     slot_mapping, num_kv_heads, block_size, slots);
+                                                     slot_mapping, num_tokens, num_kv_heads,
+                                                     block_size, slots);
   return hipGetLastError();
 }
 

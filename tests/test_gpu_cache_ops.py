@@ -207,6 +207,42 @@ def test_fp8_append_bit_exact_over_pool_then_decode(d):
     assert_attention_close(out, ref, f"decode after fp8 appends, D={d}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_append_of_prefill_chunks_then_prefill(d):
+    """Chunked prefill into an 8-bit cache: every chunk token appended in one call (consecutive
+    tokens in one block form a run applied in order), codes and scales bit-exact with the
+    oracle's sequential append, some rows scaled up so scales grow mid-run; then the chunks
+    attend over the appended pool."""
+    import paged_kv_cache_287_amd as pa
+
+    ctx, chunk = [40, 17, 100, 33, 64, 5], [25, 17, 70, 10, 64, 5]
+    pc = workloads.prefill_case(650 + d, ctx, chunk, 8, 4, d, 16, kv_dtype="fp8_e4m3")
+    c = pc.cache
+    parts = [pc.chunk_kv(b) for b in range(len(ctx))]
+    rng = np.random.default_rng(651)
+    new_k = np.concatenate([p_[0] for p_ in parts]).astype(np.float32)
+    new_v = np.concatenate([p_[1] for p_ in parts]).astype(np.float32)
+    grow = rng.choice([1.0, 1.0, 4.0], size=(new_k.shape[0], 1, 1))
+    new_k, new_v = (new_k * grow).astype(np.float16), (new_v * grow).astype(np.float16)
+    slots = np.concatenate([p_[2] for p_ in parts]).astype(np.int64)
+    ek, ev, eks, evs = oracle.kv_write_fp8(new_k, new_v, c.k_cache, c.v_cache, c.k_scale,
+                                           c.v_scale, slots)
+    gk, gv, gks, gvs = dev(c.k_cache), dev(c.v_cache), dev(c.k_scale), dev(c.v_scale)
+    log(f"[fp8 chunk append] D={d}: {len(slots)} tokens in one call")
+    pa.pa_kv_write(dev(new_k), dev(new_v), gk, gv, dev(slots), k_scale=gks, v_scale=gvs)
+    torch.cuda.synchronize()
+    assert (bits(gk) == ek).all() and (bits(gv) == ev).all(), "codes differ"
+    assert (bits(gks) == host_bits(eks)).all() and (bits(gvs) == host_bits(evs)).all(), "scales differ"
+    out = torch.full_like(dev(pc.q), float("nan"))
+    pa.pa_prefill(out, dev(pc.q), gk, gv, dev(c.block_tables), dev(c.context_lens),
+                  dev(pc.query_start), float(c.scale), max_query_len=max(chunk),
+                  max_context_len=max(ctx), k_scale=gks, v_scale=gvs)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(pc.q, ek, ev, c.block_tables, c.context_lens, pc.query_start, c.scale,
+                         kv_dtype="fp8_e4m3", k_scale=eks, v_scale=evs)
+    assert_attention_close(out, ref, f"prefill after fp8 chunk append, D={d}")
+
+
 def test_fp8_append_rounds_ties_to_even():
     import paged_kv_cache_287_amd as pa
 
