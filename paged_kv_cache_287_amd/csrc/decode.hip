@@ -12,28 +12,30 @@
 //
 // Mapping onto CDNA4:
 //   * workgroup = (KV head [x GT query heads], sequence, context partition), 4 waves; the
-//     partition's tokens are split evenly over the waves in 16-token tiles.
-//   * within a wave, each 16-lane row holds one token per step; lane `col` of the row holds
-//     elements [col*E, col*E+E) of that token (E = D/16). One step of the wave therefore loads
-//     4 consecutive token rows of a block: for D = 128 fp16 that is 1 KiB of contiguous memory
-//     with one 16-byte load per lane. K and V use the same addressing.
-//   * q . k: v_dot2 (fp16 x fp16 -> fp32) over the lane's elements, then a 16-lane all-reduce
-//     with four DPP adds (quad_perm xor 1, xor 2, row_half_mirror, row_mirror). Every lane of a
-//     row ends with the bit-identical score.
-//   * each row keeps its own online-softmax state (max, sum) per query head and a partial
-//     output of E floats per lane and head; rows and waves are merged once, through LDS, at the
-//     end of the partition. Scores are kept in log2 units (scale * log2 e folded in) so the
-//     exponentials are single v_exp_f32 instructions. The running maximum only moves when a
-//     score passes it by more than 8 (log2 units), which skips the rescaling of most tiles.
+//     partition's tokens are split evenly over the waves in whole tiles of a few steps.
+//   * within a wave, LPT consecutive lanes hold one token per step, each lane 16 contiguous
+//     bytes of it (8 for E4M3 rows of 64 elements in blocks of 8): LPT = 16 for fp16 rows of 128
+//     elements, 8 for E4M3 rows of 128 or fp16 rows of 64, 4 for E4M3 rows of 64. One step of
+//     the wave therefore loads 64 / LPT consecutive token rows of a block, 1 KiB of contiguous
+//     memory. K and V use the same addressing.
+//   * q . k: v_dot2 (fp16 x fp16 -> fp32) over the lane's elements, then an all-reduce over the
+//     token's lanes with DPP adds (quad_perm xor 1, xor 2, row_half_mirror, row_mirror). Every
+//     lane of the token ends with the bit-identical score.
+//   * each token row keeps its own online-softmax state (max, sum) per query head and a partial
+//     output of E floats per lane and head; the rows of a 16-lane DPP row merge in registers,
+//     then DPP rows and waves once, through LDS, at the end of the partition. Scores are kept in
+//     log2 units (scale * log2 e folded in) so the exponentials are single v_exp_f32
+//     instructions. The running maximum only moves when a score passes it by more than 8 (log2
+//     units), which skips the rescaling of most tiles.
 //   * P.V: a lane's tokens of two steps are paired element by element, so one v_dot2 per
 //     element and head adds two tokens' contributions (probabilities rounded to fp16).
 //   * the block ids a wave needs are fetched once, one per lane, and read back with
 //     v_readlane, so the table walk costs no memory latency inside the tile loop; the next
 //     tile's K and V loads are issued before the current tile is consumed.
-//   * grid x = KV head (x head group) is the fastest-varying dimension; with 8 KV heads the
-//     round-robin dispatch of workgroups over the 8 XCDs puts every workgroup of one KV head on
-//     one XCD, so blocks shared by several sequences (a common prefix) are re-read from that
-//     XCD's L2.
+//   * grid x = head group x KV heads + KV head is the fastest-varying dimension; with a multiple
+//     of 8 KV heads the round-robin dispatch of workgroups over the 8 XCDs puts every workgroup
+//     of one KV head on one XCD, so blocks shared by several head groups or sequences (a common
+//     prefix) are re-read from that XCD's L2.
 //   * results depend only on logical token positions (fixed tile, row and merge order), so
 //     they are deterministic and independent of physical block placement.
 #include "decode_common.hpp"
@@ -47,12 +49,15 @@ __device__ __forceinline__ float dpp_mov(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row receives the same bits.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x);  // row_half_mirror: pairs the two quads of each half-row
-  x += dpp_mov<0x140>(x);  // row_mirror: pairs the two half-rows
+// Sum over groups of LPT consecutive lanes (4, 8 or 16) of a DPP row; every lane of a group
+// receives the same bits.
+template <int LPT>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16, "lane group");
+  x += dpp_mov<0xB1>(x);                          // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);                          // quad_perm [2,3,0,1]
+  if constexpr (LPT >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: pairs the quads of a half-row
+  if constexpr (LPT >= 16) x += dpp_mov<0x140>(x); // row_mirror: pairs the two half-rows
   return x;
 }
 
@@ -82,26 +87,72 @@ __device__ __forceinline__ void to_half_pairs(const Chunk<(KV8 ? E : 2 * E) / 4>
 // rescaled (log2 units): probabilities stay below 256.
 constexpr float kRescaleSlack = 8.f;
 
+// Lane layout of one token's row of D cached elements: LPT consecutive lanes hold it, each
+// LANE_BYTES contiguous bytes (16 wherever the row allows it, so every lane issues one 16-byte
+// load), and one wave step covers RW = 64 / LPT consecutive tokens of one block. A tile is NSTEP
+// steps, two where a lane's partial outputs (E per query head) already take 64 registers.
+// Fewer lanes per token means fewer per-token instructions (score reduction, softmax) per byte,
+// which is what bounds the kernel when 8-bit codes halve the bytes per token.
+template <int D, int BS, int GT, bool KV8>
+struct RowLayout {
+  static constexpr int ESZ = KV8 ? 1 : 2;                       // bytes per cached element
+  static constexpr int ROW_BYTES = D * ESZ;                     // one token of one head
+  static constexpr int LPT = ROW_BYTES / 16 > kWave / BS ? ROW_BYTES / 16 : kWave / BS;
+  static constexpr int LANE_BYTES = ROW_BYTES / LPT;            // 16, or 8 for E4M3 D 64 BS 8
+  static constexpr int E = D / LPT;                             // elements per lane per token
+  static constexpr int RW = kWave / LPT;                        // tokens per wave step
+  static constexpr int NSTEP = E * GT >= 64 ? 2 : 4;            // steps per tile
+  static constexpr int TT = RW * NSTEP;                         // tokens per tile
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16, "lane groups are 4, 8 or 16 lanes");
+  static_assert(BS % RW == 0, "a step's tokens share a block");
+  static_assert(NSTEP % 2 == 0, "P.V pairs the tokens of two steps");
+};
+
+// Merge the online-softmax state of this lane with that of the lane CTRL (a DPP row rotation)
+// points to; both hold the same elements of different tokens.
+template <int CTRL, int GT, int E>
+__device__ __forceinline__ void merge_lane_states(float (&m)[GT], float (&l)[GT],
+                                                  float (&acc)[GT][E]) {
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const float mo = dpp_mov<CTRL>(m[h]);
+    const float lo = dpp_mov<CTRL>(l[h]);
+    const float mn = fmaxf(m[h], mo);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float a = fexp2(m[h] - ms);
+    const float c = fexp2(mo - ms);
+    l[h] = a * l[h] + c * lo;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = a * acc[h][e] + c * dpp_mov<CTRL>(acc[h][e]);
+    m[h] = mn;
+  }
+}
+
 template <int D, int BS, int GT, bool KV8>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
-  constexpr int E = D / 16;                 // elements per lane per token
-  constexpr int ESZ = KV8 ? 1 : 2;          // bytes per cached element
-  constexpr int LANE_BYTES = E * ESZ;       // 16, 8 or 4
+  using Lay = RowLayout<D, BS, GT, KV8>;
+  constexpr int LPT = Lay::LPT;
+  constexpr int E = Lay::E;
+  constexpr int RW = Lay::RW;
+  constexpr int NSTEP = Lay::NSTEP;
+  constexpr int TT = Lay::TT;
+  constexpr int LANE_BYTES = Lay::LANE_BYTES;
   constexpr int NWORDS = LANE_BYTES / 4;
   constexpr int NH2 = E / 2;                // fp16 pairs per lane per token
-  constexpr int ROW_BYTES = D * ESZ;        // one token of one head
+  constexpr int ROW_BYTES = Lay::ROW_BYTES;
   constexpr int TILE_BYTES = BS * ROW_BYTES;  // one (block, head) tile
-  static_assert(BS % kRows == 0, "a step's four tokens must share a block");
   // host-validated: part_tokens is a power of two in [256, 4096] with part_tokens / 4 <= 64 * BS,
   // so a wave's tokens are whole blocks and fit one block id per lane
 
+  // With 8 or more KV heads, head groups of one KV head are kvh, kvh + Hkv, ...: workgroup ids
+  // are dealt round-robin over the 8 XCDs, so all of them read that KV head through one L2.
   const int hg = blockIdx.x;
   const int b = blockIdx.y;
   // partitions are dispatched last first: only long contexts have high partition indices, so
   // their full workgroups start early instead of forming the tail of the grid
   const int part = p.max_parts - 1 - (int)blockIdx.z;
-  const int kvh = hg / p.head_groups;
-  const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * GT;
+  const int kvh = hg % p.num_kv_heads;
+  const int h0 = kvh * p.group + (hg / p.num_kv_heads) * GT;
   const SeqRange sr = seq_range<BS>(p, b);
   const int L = sr.L;
   // partitions beyond the grid's (context longer than the host bound) are dropped, never
@@ -114,8 +165,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int row = lane >> 4;
-  const int col = lane & 15;
+  const int row = lane / LPT;   // token of the step
+  const int col = lane % LPT;   // element chunk [col * E, col * E + E)
 
   // ---- query rows of this head group: E fp16 per lane per head -------------------------
   uint32_t qw[GT][NH2];
@@ -123,20 +174,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   for (int h = 0; h < GT; ++h) {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(
         p.q + ((size_t)b * p.num_q_heads + h0 + h) * D + col * E);
-    const Chunk<E / 2> c = load_chunk<E / 2>(qp);
 #pragma unroll
-    for (int i = 0; i < NH2; ++i) qw[h][i] = c.w[i];
+    for (int c = 0; c < NH2 / 4; ++c) {
+      const Chunk<4> ch = load_chunk<4>(qp + 16 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qw[h][4 * c + i] = ch.w[i];
+    }
   }
 
   // ---- block ids of this wave's tokens: lane j holds logical block lb0 + j ---------------
   // The partition's tokens [p0, p0 + pn) are split evenly over the waves in whole tiles, so a
   // short partition (the end of a context) keeps every wave busy. A full partition gives each
   // wave part_tokens / 4 tokens. p0 is a multiple of the block size and share of the tile, so a
-  // tile never straddles a block of 16 tokens or more (and covers two whole blocks of 8), and
-  // a wave's range spans at most 64 blocks.
+  // step never straddles a block, and a wave's range spans at most 64 blocks.
   const int p0 = sr.start + part * part_tokens;
   const int pn = max(0, min(L - p0, part_tokens));
-  const int share = (pn + kWaves * kTileTokens - 1) / (kWaves * kTileTokens) * kTileTokens;
+  const int share = (pn + kWaves * TT - 1) / (kWaves * TT) * TT;
   const int wbase = p0 + wave * share;
   const int woff = wbase % BS;  // lane j holds logical block wbase / BS + j
   const int nblk = min((L + BS - 1) / BS, p.max_blocks_per_seq);
@@ -161,12 +214,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
   }
 
-  Chunk<NWORDS> ka[kSteps], va[kSteps], kb[kSteps], vb[kSteps];
+  Chunk<NWORDS> ka[NSTEP], va[NSTEP], kb[NSTEP], vb[NSTEP];
 
-  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[kSteps], Chunk<NWORDS>(&vc)[kSteps]) {
+  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[NSTEP], Chunk<NWORDS>(&vc)[NSTEP]) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int t = kTileTokens * i + kRows * s;  // first token of the step, wave-relative
+    for (int s = 0; s < NSTEP; ++s) {
+      const int t = TT * i + RW * s;  // first token of the step, wave-relative
       const int id = __builtin_amdgcn_readlane(my_id, (woff + t) / BS);
       const size_t off = (size_t)id * blk_stride + (size_t)(((woff + t) % BS) * ROW_BYTES + lane_off);
       kc[s] = load_chunk<NWORDS, true>(kbase + off);
@@ -174,17 +227,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     }
   };
 
-  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[kSteps],
-                          const Chunk<NWORDS>(&vc)[kSteps], bool masked) {
-    const int tok0 = wbase + kTileTokens * i;
-    float sc[kSteps][GT];
-    float kmul[kSteps], vmul[kSteps];
+  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[NSTEP],
+                          const Chunk<NWORDS>(&vc)[NSTEP], bool masked) {
+    const int tok0 = wbase + TT * i;
+    float sc[NSTEP][GT];
+    float kmul[NSTEP], vmul[NSTEP];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       kmul[s] = p.scale_log2;
       vmul[s] = 1.f;
       if constexpr (KV8) {
-        const int t = kTileTokens * i + kRows * s;
+        const int t = TT * i + RW * s;
         const int id = __builtin_amdgcn_readlane(my_id, (woff + t) / BS);
         kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
         vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
@@ -200,11 +253,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
       }
     }
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const bool valid = !masked || (tok0 + kRows * s + row < L);
+    for (int s = 0; s < NSTEP; ++s) {
+      const bool valid = !masked || (tok0 + RW * s + row < L);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float x = row_sum16(sc[s][h]) * kmul[s];
+        const float x = lane_group_sum<LPT>(sc[s][h]) * kmul[s];
         sc[s][h] = valid ? x : kNegInf;
       }
     }
@@ -212,10 +265,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     // sums of 2^(s - m) terms), so it moves, and l and acc are rescaled, only when some row's
     // score exceeds it by more than kRescaleSlack; probabilities then stay below 2^kRescaleSlack.
     // The decision is wave-uniform and the result is the same softmax up to rounding.
-    float pw[kSteps][GT];
+    float pw[NSTEP][GT];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-      const float mt = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
+      float mt = sc[0][h];
+#pragma unroll
+      for (int s = 1; s < NSTEP; ++s) mt = fmaxf(mt, sc[s][h]);
       if (__builtin_amdgcn_ballot_w64(mt > m[h] + kRescaleSlack) != 0) {
         const float mn = fmaxf(m[h], mt);
         const float alpha = fexp2(m[h] - (mn == kNegInf ? 0.f : mn));
@@ -226,24 +281,27 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
       }
       const float ms = m[h] == kNegInf ? 0.f : m[h];
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) pw[s][h] = fexp2(sc[s][h] - ms);
-      l[h] += (pw[0][h] + pw[1][h]) + (pw[2][h] + pw[3][h]);
+      for (int s = 0; s < NSTEP; ++s) pw[s][h] = fexp2(sc[s][h] - ms);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < NSTEP / 2; ++j) ps += pw[2 * j][h] + pw[2 * j + 1][h];
+      l[h] += ps;
     }
     // Weighted value sum as fp16 dot products over token pairs: the lane's tokens of steps 2j
     // and 2j + 1 are paired element by element (byte permutes), the two probabilities rounded
     // to fp16, and one v_dot2 per element and head adds both tokens.
-    uint32_t vh[kSteps][NH2];
+    uint32_t vh[NSTEP][NH2];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       to_half_pairs<E, KV8>(vc[s], vh[s]);
       if (masked) {
-        const bool valid = tok0 + kRows * s + row < L;
+        const bool valid = tok0 + RW * s + row < L;
 #pragma unroll
         for (int w = 0; w < NH2; ++w) vh[s][w] = valid ? vh[s][w] : 0u;
       }
     }
 #pragma unroll
-    for (int j = 0; j < kSteps / 2; ++j) {
+    for (int j = 0; j < NSTEP / 2; ++j) {
       uint32_t lo[NH2], hi[NH2];
 #pragma unroll
       for (int w = 0; w < NH2; ++w) {
@@ -268,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   // inside this wave's range. Two register buffers alternate so the next tile's loads are in
   // flight while the current one is consumed.
   const int avail = max(0, min(p0 + pn - wbase, share));
-  const int n_full = avail / kTileTokens;
-  const bool has_tail = (avail % kTileTokens) != 0;
+  const int n_full = avail / TT;
+  const bool has_tail = (avail % TT) != 0;
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
   int i = 0;
@@ -283,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     if (has_tail) issue_tile(i + 1, kb, vb);
     consume_tile(i, ka, va, false);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       ka[s] = kb[s];
       va[s] = vb[s];
     }
@@ -291,17 +349,25 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   }
   if (has_tail) consume_tile(i, ka, va, true);
 
-  // ---- merge the 4 rows x kWaves waves of this workgroup through LDS --------------------
-  __shared__ float s_acc[kWaves * kRows][GT][D];
-  __shared__ float s_ml[kWaves * kRows][GT][2];
-  const int sub = wave * kRows + row;
+  // ---- the 16 / LPT tokens rows of a DPP row merge in registers (rotations by 8, then 4) ----
+  if constexpr (LPT <= 8) merge_lane_states<0x128>(m, l, acc);  // row_ror:8
+  if constexpr (LPT <= 4) merge_lane_states<0x124>(m, l, acc);  // row_ror:4
+
+  // ---- merge the 4 DPP rows x kWaves waves of this workgroup through LDS ---------------
+  // Lanes 0 .. LPT-1 of each DPP row now hold the whole row's state.
+  constexpr int kDppRows = kWave / 16;
+  __shared__ float s_acc[kWaves * kDppRows][GT][D];
+  __shared__ float s_ml[kWaves * kDppRows][GT][2];
+  const int sub = wave * kDppRows + (lane >> 4);
+  if ((lane & 15) < LPT) {
 #pragma unroll
-  for (int h = 0; h < GT; ++h) {
+    for (int h = 0; h < GT; ++h) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) s_acc[sub][h][col * E + e] = acc[h][e];
-    if (col == 0) {
-      s_ml[sub][h][0] = m[h];
-      s_ml[sub][h][1] = l[h];
+      for (int e = 0; e < E; ++e) s_acc[sub][h][col * E + e] = acc[h][e];
+      if (col == 0) {
+        s_ml[sub][h][0] = m[h];
+        s_ml[sub][h][1] = l[h];
+      }
     }
   }
   __syncthreads();
@@ -310,12 +376,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   auto local_merge = [&](int h, int d, float& mx, float& ls, float& a) {
     mx = kNegInf;
 #pragma unroll
-    for (int k = 0; k < kWaves * kRows; ++k) mx = fmaxf(mx, s_ml[k][h][0]);
+    for (int k = 0; k < kWaves * kDppRows; ++k) mx = fmaxf(mx, s_ml[k][h][0]);
     const float ms = mx == kNegInf ? 0.f : mx;
     ls = 0.f;
     a = 0.f;
 #pragma unroll
-    for (int k = 0; k < kWaves * kRows; ++k) {
+    for (int k = 0; k < kWaves * kDppRows; ++k) {
       const float w = fexp2(s_ml[k][h][0] - ms);
       ls = fmaf(w, s_ml[k][h][1], ls);
       a = fmaf(w, s_acc[k][h][d], a);
@@ -338,7 +404,9 @@ hipError_t dispatch_gt(const DecodeParams& p, int num_seqs, int gt, hipStream_t 
     case 1: return launch_one<D, BS, 1, KV8>(p, num_seqs, stream);
     case 2: return launch_one<D, BS, 2, KV8>(p, num_seqs, stream);
     case 4: return launch_one<D, BS, 4, KV8>(p, num_seqs, stream);
-    case 8: return launch_one<D, BS, 8, KV8>(p, num_seqs, stream);
+    case 8:
+      if constexpr (!KV8) return launch_one<D, BS, 8, KV8>(p, num_seqs, stream);  // E4M3: at most 4
+      break;
   }
   return hipErrorInvalidValue;
 }

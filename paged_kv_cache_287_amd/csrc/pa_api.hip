@@ -25,10 +25,11 @@ int hip_status(hipError_t e) {
 
 // Resolves the partition size (0 = automatic) and the grid's partition count; false if invalid.
 bool resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int block_size,
-                       long long max_ctx, int partition_tokens, int* part_tokens, int* max_parts) {
+                       bool kv8, long long max_ctx, int partition_tokens, int* part_tokens,
+                       int* max_parts) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_ctx > (1LL << 30)) return false;
   const int group = num_q_heads / num_kv_heads;
-  const int units_per_seq = num_kv_heads * (group / pa::decode_rows(group));
+  const int units_per_seq = num_kv_heads * (group / pa::decode_rows(group, kv8));
   const int ctx = (int)(max_ctx > 0 ? max_ctx : 1);
   int pt = partition_tokens;
   if (pt == 0)
@@ -68,7 +69,8 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
       !supported_block_size(block_size) || !known_dtype(kv_dtype) || max_context_len <= 0)
     return 0;
   int pt = 0, parts = 0;
-  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, max_context_len,
+  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size,
+                         kv_dtype == PA_KV_FP8_E4M3, max_context_len,
                          partition_tokens, &pt, &parts))
     return 0;
   return pt;
@@ -82,7 +84,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                             partition_tokens);
   if (pt == 0) return 0;
   const int group = num_q_heads / num_kv_heads;
-  const int hg_total = num_kv_heads * (group / pa::decode_rows(group));
+  const int hg_total =
+      num_kv_heads * (group / pa::decode_rows(group, kv_dtype == PA_KV_FP8_E4M3));
   return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
                               (int)pa::ceil_div(max_context_len, pt)).total;
 }
@@ -128,11 +131,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (max_ctx > (long long)max_blocks_per_seq * block_size || max_ctx > (1LL << 30))
     return PA_ERR_INVALID_ARG;
   int part_tokens = 0, max_parts = 0;
-  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, max_ctx,
+  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, fp8, max_ctx,
                          partition_tokens, &part_tokens, &max_parts))
     return partition_tokens != 0 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
-  const int gt = pa::decode_rows(group);
+  const int gt = pa::decode_rows(group, fp8);
   // prefix blocks beyond the clamp (table width, on-chip id list, host bound on contexts) are
   // simply decoded per sequence, so the clamp never changes the result
   int prefix_blocks = 0, prefix_split = 0, prefix_slices = 0;
@@ -248,7 +251,8 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
                                             partition_tokens);
   if (pt == 0) return 0;
   const int group = num_q_heads / num_kv_heads;
-  const int hg_total = num_kv_heads * (group / pa::decode_rows(group));
+  const int hg_total =
+      num_kv_heads * (group / pa::decode_rows(group, kv_dtype == PA_KV_FP8_E4M3));
   return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
                               (int)pa::ceil_div(max_context_len, pt) + pa::kMaxPrefixSlices).total;
 }

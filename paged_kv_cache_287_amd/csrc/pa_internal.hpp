@@ -35,14 +35,17 @@ inline bool valid_part_tokens(int pt, int block_size) {
 
 // Query heads per workgroup. Groups of 16 or more query heads per KV head (MQA-like) stack 32 or
 // 16 of them into matrix-core tiles; smaller groups use the VALU kernel with the largest
-// compiled tile (8, 4, 2 or 1) dividing G. (Padding 4 or 8 rows into a 16-row matrix-core tile
-// was measured slower than the VALU kernel for fp16 and for E4M3 caches: the transposed V
-// operand costs more LDS reads than the dot products it replaces.)
+// compiled tile dividing G: 8, 4, 2 or 1 query heads for fp16 caches, at most 4 for E4M3 ones
+// (their lanes hold 16 elements of a token, and 8 heads of partial outputs no longer fit the
+// register file: measured 64 us with two 4-head workgroups per KV head against 85 us with one
+// 8-head workgroup, GQA-8 at 64 x 2,048 tokens). Padding 4 or 8 rows into a 16-row matrix-core
+// tile was measured slower than the VALU kernel for fp16 and for E4M3 caches: the transposed V
+// operand costs more LDS reads than the dot products it replaces.
 inline bool decode_uses_mfma(int group) { return group >= 16 && group % 16 == 0; }
-inline int decode_rows(int group) {
+inline int decode_rows(int group, bool kv8) {
   if (decode_uses_mfma(group)) return group % 32 == 0 ? 32 : 16;
   for (int gt : {8, 4, 2, 1})
-    if (group % gt == 0) return gt;
+    if (group % gt == 0 && !(kv8 && gt > 4)) return gt;
   return 1;
 }
 

@@ -71,6 +71,19 @@ def test_head_groupings(hq, hkv):
     run_case(case)
 
 
+@pytest.mark.parametrize("hq,hkv,d,bs", [(16, 2, 128, 16), (64, 8, 128, 16), (24, 3, 64, 16),
+                                         (8, 1, 64, 8), (12, 4, 128, 32), (6, 2, 64, 64),
+                                         (16, 2, 64, 16), (64, 8, 64, 8)])
+@pytest.mark.parametrize("kv_dtype", ["f16", "fp8_e4m3"])
+def test_head_groupings_dims_and_dtypes(hq, hkv, d, bs, kv_dtype):
+    """Groups of 8 (one 8-head workgroup for fp16, two 4-head workgroups per KV head for E4M3,
+    with KV-head counts that are and are not multiples of 8) and of 3 and 2, over both head dims
+    and lane layouts (16, 8 or 4 lanes per token)."""
+    case = workloads.random_case(210 + hq + hkv + d + bs, [5, 300, 777, 64], hq, hkv, d, bs,
+                                 kv_dtype=kv_dtype, name=f"groups_{hq}q_{hkv}kv_d{d}_{kv_dtype}")
+    run_case(case)
+
+
 def test_long_context_many_partitions():
     case = workloads.random_case(300, [40000, 9000, 1], 8, 2, 128, 16, name="long_context")
     run_case(case)
@@ -138,6 +151,8 @@ def test_deterministic_across_runs():
 def test_block_size_does_not_change_the_arithmetic():
     # the same logical K/V placed with block sizes 8..64 gives bit-identical outputs for a fixed
     # partition size, because tiles, partitions and merge order follow logical positions only
+    # (fp16 D 128: the lane layout is the same for every block size; E4M3 pools are not compared,
+    # their per-block scales depend on the block size)
     ref = None
     for bs in (8, 16, 32, 64):
         case = workloads.random_case(402, LENS, 32, 8, 128, bs)

@@ -343,7 +343,7 @@ def sweep(block_size: int, num_seqs: int = 128) -> DecodeCase:
 def variant(num_kv_heads: int, kv_dtype: str = "f16", num_seqs: int = 64, ctx: int = 2048) -> DecodeCase:
     """64 x 2048 tokens, BS 16, 32 q heads over 32 (MHA), 8 (GQA) or 1 (MQA) KV heads, KV in
     fp16 or E4M3 with per-(block, head) scales. The fp8 pool quantizes the same fp16 draw."""
-    assert num_kv_heads in (32, 8, 1)
+    assert 32 % num_kv_heads == 0
     seed = SEEDS["variants"]
     case = random_case([seed, num_kv_heads], [ctx] * num_seqs, 32, num_kv_heads, 128, 16,
                        name=f"variant_hkv{num_kv_heads}_{kv_dtype}")
