@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     }
   };
 
-  finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, local_merge);
+  finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, GT, local_merge);
 }
 
 template <int D, int BS, int GT, bool KV8>
@@ -403,6 +403,7 @@ hipError_t dispatch_gt(const DecodeParams& p, int num_seqs, int gt, hipStream_t 
   switch (gt) {
     case 1: return launch_one<D, BS, 1, KV8>(p, num_seqs, stream);
     case 2: return launch_one<D, BS, 2, KV8>(p, num_seqs, stream);
+    case 3: return launch_one<D, BS, 3, KV8>(p, num_seqs, stream);
     case 4: return launch_one<D, BS, 4, KV8>(p, num_seqs, stream);
     case 8:
       if constexpr (!KV8) return launch_one<D, BS, 8, KV8>(p, num_seqs, stream);  // E4M3: at most 4

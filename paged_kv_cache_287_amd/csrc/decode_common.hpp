@@ -92,17 +92,18 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
 
 // End of one (sequence, head group, partition) workgroup. merge(h, d, mx, ls, a) returns the
 // workgroup's combined running max, running sum and weighted value sum for element d of its
-// query row h (R rows, head dim D). With one partition and no earlier partial the normalised
-// output is written directly; otherwise the partial is published (after the `extra` slots an
-// earlier pass filled) and the workgroup that arrives last merges all slots exactly and resets
-// the arrival counter to zero.
+// query row h (the first `rows` of R rows, head dim D). With one partition and no earlier
+// partial the normalised output is written directly; otherwise the partial is published (after
+// the `extra` slots an earlier pass filled) and the workgroup that arrives last merges all slots
+// exactly and resets the arrival counter to zero.
 template <int R, int D, int NTHREADS, typename Merge>
 __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, int hg, int part,
-                                                 int nparts, int extra, int h0, Merge&& merge) {
+                                                 int nparts, int extra, int h0, int rows,
+                                                 Merge&& merge) {
   const int tid = threadIdx.x;
   if (nparts == 1 && extra == 0) {
     // the whole sequence fits one partition: normalise and write the output directly
-    for (int idx = tid; idx < R * D; idx += NTHREADS) {
+    for (int idx = tid; idx < rows * D; idx += NTHREADS) {
       const int h = idx / D, d = idx - h * D;
       float mx, ls, a;
       merge(h, d, mx, ls, a);
@@ -112,7 +113,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
   }
 
   // ---- several partitions: publish this one's (max, sum, value sum) ----------------------
-  for (int idx = tid; idx < R * D; idx += NTHREADS) {
+  for (int idx = tid; idx < rows * D; idx += NTHREADS) {
     const int h = idx / D, d = idx - h * D;
     float mx, ls, a;
     merge(h, d, mx, ls, a);
@@ -156,7 +157,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
     constexpr int TPR = D / UE;            // threads per row
     constexpr int RPP = NTHREADS / TPR;    // rows per pass
     static_assert(D % UE == 0 && NTHREADS % TPR == 0 && R % RPP == 0, "merge tiling");
-    for (int h = tid / TPR; h < R; h += RPP) {
+    for (int h = tid / TPR; h < rows; h += RPP) {
       const int d0 = tid % TPR;
       const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
       const float* ml = p.ws_ml + row0 * 2;
@@ -197,7 +198,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
       for (int u = 0; u < UE; ++u) o[u * TPR] = (_Float16)(a[u] / ls);
     }
   } else {
-    for (int idx = tid; idx < R * D; idx += NTHREADS) {
+    for (int idx = tid; idx < rows * D; idx += NTHREADS) {
       const int h = idx / D, d = idx - h * D;
       const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
       const float* ml = p.ws_ml + row0 * 2;

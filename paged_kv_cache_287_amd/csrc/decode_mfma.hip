@@ -1,4 +1,4 @@
-// Paged decode attention for large query groups (G >= 16 query heads per KV head, e.g. MQA)
+// Paged decode attention for large query groups (G >= 5 query heads per KV head, e.g. MQA)
 // on gfx950 matrix cores.
 //
 // With G query heads sharing one KV head ("LLM 추론 확장, 품질·비용 절충 필수", attention-heads
@@ -17,6 +17,10 @@
 //     of V and stores them as one 8-byte write per dim, and the operand (4 tokens of one dim)
 //     is one 8-byte read. The accumulator lane l holds row l%16, so rescaling by the running
 //     max is lane-local.
+// Groups that are not a multiple of 16 fill 16- or 32-row tiles with padding rows of zero
+// queries: the matrix cores still do the dot products for less VALU time than the VALU kernel's
+// dot2 chains (GQA-8 at 64 x 2,048 tokens: 51 us against 76 us for fp16 KV, 45 against 64 for
+// E4M3), while at 4 heads the VALU kernel is as fast (fp16) or faster (E4M3).
 // Everything else (partitioning, block-id walk, double-buffered non-temporal loads, fp8 scales,
 // merge through LDS, partial publish / last-arrival merge) follows the VALU kernel.
 #include "decode_common.hpp"
@@ -49,8 +53,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   // partitions are dispatched last first: only long contexts have high partition indices, so
   // their full workgroups start early instead of forming the tail of the grid
   const int part = p.max_parts - 1 - (int)blockIdx.z;
+  // query rows this workgroup owns: R, or fewer in a padded tile (the padding rows hold zero
+  // queries and are never stored)
+  const int rows = p.group / p.head_groups;
   const int kvh = hg / p.head_groups;
-  const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * R;
+  const int h0 = kvh * p.group + (hg - kvh * p.head_groups) * rows;
   const SeqRange sr = seq_range<BS>(p, b);
   const int L = sr.L;
   const int part_tokens = p.part_tokens;
@@ -70,8 +77,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qb[nt][kk] = *reinterpret_cast<const h8*>(
-          p.q + ((size_t)b * p.num_q_heads + h0 + 16 * nt + lr) * D + 32 * kk + 8 * lq);
+      qb[nt][kk] = 16 * nt + lr < rows
+                       ? *reinterpret_cast<const h8*>(p.q + ((size_t)b * p.num_q_heads + h0 +
+                                                             16 * nt + lr) * D + 32 * kk + 8 * lq)
+                       : h8{0, 0, 0, 0, 0, 0, 0, 0};
 
   // ---- block ids of this wave's tokens: lane j holds logical block wbase / BS + j ------------
   // The partition's tokens [p0, p0 + pn) are split evenly over the waves in whole tiles, so a
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       a = fmaf(wt, s_acc[(w * R + h) * D + d], a);
     }
   };
-  finish_partition<R, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, local_merge);
+  finish_partition<R, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, rows, local_merge);
 }
 
 template <int D, int BS, int NT, bool KV8>
@@ -322,7 +331,7 @@ hipError_t dispatch_bs(const DecodeParams& p, int num_seqs, int bs, hipStream_t 
 
 template <int D, bool KV8>
 hipError_t dispatch_rows(const DecodeParams& p, int num_seqs, int bs, int rows, hipStream_t stream) {
-  return rows == 32 ? dispatch_bs<D, KV8, 2>(p, num_seqs, bs, stream)
+  return rows > 16 ? dispatch_bs<D, KV8, 2>(p, num_seqs, bs, stream)
                     : dispatch_bs<D, KV8, 1>(p, num_seqs, bs, stream);
 }
 

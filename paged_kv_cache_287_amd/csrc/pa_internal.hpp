@@ -33,18 +33,27 @@ inline bool valid_part_tokens(int pt, int block_size) {
   return pt / kWaves <= kWave * block_size;
 }
 
-// Query heads per workgroup. Groups of 16 or more query heads per KV head (MQA-like) stack 32 or
-// 16 of them into matrix-core tiles; smaller groups use the VALU kernel with the largest
-// compiled tile dividing G: 8, 4, 2 or 1 query heads for fp16 caches, at most 4 for E4M3 ones
-// (their lanes hold 16 elements of a token, and 8 heads of partial outputs no longer fit the
-// register file: measured 64 us with two 4-head workgroups per KV head against 85 us with one
-// 8-head workgroup, GQA-8 at 64 x 2,048 tokens). Padding 4 or 8 rows into a 16-row matrix-core
-// tile was measured slower than the VALU kernel for fp16 and for E4M3 caches: the transposed V
-// operand costs more LDS reads than the dot products it replaces.
-inline bool decode_uses_mfma(int group) { return group >= 16 && group % 16 == 0; }
+// Query heads per workgroup. Groups of 5 or more query heads per KV head use the matrix-core
+// kernel: 32 or 16 heads per tile when G is a multiple of 16; otherwise the group is cut into
+// the fewest tiles of at most 32 rows that divide it evenly (one tile up to G = 32), padded to 16
+// or 32 rows. A padded tile beats the VALU kernel there (GQA-8 at 64 x 2,048 tokens: 51 against
+// 76 us for fp16 KV, 45 against 64 us for E4M3), and the VALU alternative for 5, 6 or 7 heads
+// would read each K/V tile once per small head tile. Groups of 1 to 4 heads (and odd groups
+// above 32) use the VALU kernel with the largest compiled tile dividing G: 8, 4, 3, 2 or 1 query
+// heads for fp16 caches, at most 4 for E4M3 ones (their lanes hold 16 elements of a token, and
+// 8 heads of partial outputs no longer fit the register file). At G = 4 the padded tile was
+// measured as fast as the VALU kernel for fp16 and slower for E4M3.
+inline int mfma_rows(int group) {
+  if (group < 5) return 0;
+  if (group % 32 == 0) return 32;
+  if (group % 16 == 0) return 16;
+  const int tiles = (group + 31) / 32;
+  return group % tiles == 0 ? group / tiles : 0;
+}
+inline bool decode_uses_mfma(int group) { return mfma_rows(group) > 0; }
 inline int decode_rows(int group, bool kv8) {
-  if (decode_uses_mfma(group)) return group % 32 == 0 ? 32 : 16;
-  for (int gt : {8, 4, 2, 1})
+  if (decode_uses_mfma(group)) return mfma_rows(group);
+  for (int gt : {8, 4, 3, 2, 1})
     if (group % gt == 0 && !(kv8 && gt > 4)) return gt;
   return 1;
 }
