@@ -34,7 +34,7 @@ bool resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int bloc
   int pt = partition_tokens;
   if (pt == 0)
     pt = pa::auto_part_tokens(num_seqs, units_per_seq, ctx, block_size,
-                              pa::decode_target_units(group));
+                              pa::decode_target_units(group), pa::decode_single_units(group));
   if (!pa::valid_part_tokens(pt, block_size)) return false;
   const long long parts = pa::ceil_div(ctx, pt);
   if (parts > 65535) return false;

@@ -60,19 +60,34 @@ inline int decode_rows(int group, bool kv8) {
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Automatic split-context partition size: the largest power of two in [256, 4096], and at most
-// half the longest context, whose grid still has at least `target_units` workgroups; if none
-// has, the smallest. Longer partitions amortise each workgroup's start-up (q, table and
-// first-tile latency) and its merge; shorter ones give more parallelism and a shorter tail when
-// lengths are uneven, and splitting the longest sequences at least in two keeps one workgroup
-// from holding a whole long sequence while the rest of the GPU idles. The target is four
-// workgroups per CU for the VALU kernel and one for the matrix-core kernel, whose 16- or 32-row
-// workgroups are heavier and whose merges cost more per partition (measured best on MI355X).
+// Automatic split-context partition size.
+// (1) One partition per sequence when the smallest power of two in [256, 4096] covering the
+//     longest context is valid for the block size and the grid still has `single_units`
+//     workgroups (two per CU for the VALU kernel, one per CU for the matrix-core kernel): no
+//     partials, no merge, and one start-up per (sequence, head group). Measured faster on every
+//     uniform-length shape (8B shape 186 -> 179 us, GQA-4 64 x 2048 96 -> 89 us, MHA 335 -> 322
+//     us) and on the shared-prefix workloads (equal, or 125 -> 115 us with forks).
+// (2) Otherwise the largest power of two in [256, 4096], and at most half the longest context,
+//     whose grid still has at least `target_units` workgroups; if none has, the smallest.
+//     Longer partitions amortise each workgroup's start-up (q, table and first-tile latency) and
+//     its merge; shorter ones give more parallelism and a shorter tail when lengths are uneven,
+//     and splitting the longest sequences at least in two keeps one workgroup from holding a
+//     whole long sequence while the rest of the GPU idles. The target is four workgroups per CU
+//     for the VALU kernel and one for the matrix-core kernel, whose 16- or 32-row workgroups
+//     are heavier and whose merges cost more per partition (measured best on MI355X).
 inline long long decode_target_units(int group) {
   return decode_uses_mfma(group) ? (long long)kNumCUs : 4LL * kNumCUs;
 }
+inline long long decode_single_units(int group) {
+  return decode_uses_mfma(group) ? (long long)kNumCUs : 2LL * kNumCUs;
+}
 inline int auto_part_tokens(int num_seqs, int units_per_seq, int max_context_len, int block_size,
-                            long long target_units) {
+                            long long target_units, long long single_units) {
+  int whole = kMinPartTokens;
+  while (whole < max_context_len && whole < kMaxPartTokens) whole *= 2;
+  if (whole >= max_context_len && valid_part_tokens(whole, block_size) &&
+      (long long)num_seqs * units_per_seq >= single_units)
+    return whole;
   for (int pt = kMaxPartTokens; pt > kMinPartTokens; pt /= 2) {
     if (!valid_part_tokens(pt, block_size) || 2LL * pt > max_context_len) continue;
     const long long units = (long long)num_seqs * units_per_seq * ceil_div(max_context_len, pt);

@@ -49,13 +49,22 @@ def test_abi_version_and_status_strings():
 
 
 def test_partition_choice_and_workspace_size():
-    # 8B-shaped: 64 seqs x 8 KV heads x ceil(4096 / 2048) = 1024 workgroups >= 4 per CU
-    assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096) == 2048
-    # at most half the longest context: 2048-token contexts split at least in two
-    assert pa.decode_partition_tokens(64, 32, 32, 128, 16, 2048) == 1024
-    assert pa.decode_partition_tokens(100, 32, 8, 128, 16, 1409) == 512
+    # one partition per sequence when it covers the longest context and the grid keeps two
+    # workgroups per CU: 8B-shaped 64 seqs x 8 KV heads = 512 workgroups
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096) == 4096
+    assert pa.decode_partition_tokens(64, 32, 32, 128, 16, 2048) == 2048
+    assert pa.decode_partition_tokens(100, 32, 8, 128, 16, 1409) == 2048
+    # too few workgroups for one partition each: 32 seqs x 8 KV heads = 256 < 512, so
+    # partitions of at most half the longest context with >= 4 workgroups per CU
+    assert pa.decode_partition_tokens(32, 32, 8, 128, 16, 4096) == 1024
+    # longest context beyond one partition: 128 seqs of up to 7503 tokens -> 2048
+    assert pa.decode_partition_tokens(128, 32, 8, 128, 16, 7503) == 2048
+    # block size 8 caps a partition at 2048 tokens, so 4096-token contexts split
+    assert pa.decode_partition_tokens(64, 32, 8, 128, 8, 4096) == 2048
     # matrix-core decode (G = 16k) aims at one workgroup per CU: MQA 64 x 2048 -> 4 partitions
     assert pa.decode_partition_tokens(64, 32, 1, 128, 16, 2048) == 512
+    # padded matrix-core tile, 64 seqs x 4 KV heads = 256 workgroups: one partition each
+    assert pa.decode_partition_tokens(64, 32, 4, 128, 16, 2048) == 2048
     # few sequences: smaller partitions for parallelism, down to 256
     assert pa.decode_partition_tokens(1, 32, 8, 128, 16, 4096) == 256
     assert pa.decode_partition_tokens(4, 32, 8, 128, 16, 32768) == 1024

@@ -39,6 +39,16 @@ def test_8b_workload_full_size():
     run_case(gen(workloads.eight_b))
 
 
+def test_8b_workload_split_in_two_partitions():
+    """The same full-size workload split into 2,048-token partitions (publish + last-arrival
+    merge), checked on 8 sequences."""
+    case = gen(workloads.eight_b)
+    out = gpu_decode(case_to_device(case), case.scale, partition_tokens=2048)
+    torch.cuda.synchronize()
+    seqs = [0, 9, 18, 27, 36, 45, 54, 63]
+    assert_attention_close(out[seqs], oracle_decode(case, seqs=seqs), "8b, 2048-token partitions")
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32, 64])
 def test_sweep_workload(bs):
     run_case(gen(workloads.sweep, bs))
