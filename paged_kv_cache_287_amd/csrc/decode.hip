@@ -324,30 +324,28 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 
   // Tiles [0, n_full) are complete; tile n_full is the masked tail when the context ends
   // inside this wave's range. Two register buffers alternate so the next tile's loads are in
-  // flight while the current one is consumed.
+  // flight while the current one is consumed. The steady-state loop issues its loads
+  // unconditionally: a conditional load would make the compiler's wait counts assume the
+  // shorter queue and drain the prefetched tile before the current one is finished.
   const int avail = max(0, min(p0 + pn - wbase, share));
   const int n_full = avail / TT;
   const bool has_tail = (avail % TT) != 0;
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
   int i = 0;
-  for (; i + 1 < n_full; i += 2) {
+  for (; i + 2 < n_tiles; i += 2) {
     issue_tile(i + 1, kb, vb);
     consume_tile(i, ka, va, false);
-    if (i + 2 < n_tiles) issue_tile(i + 2, ka, va);
+    issue_tile(i + 2, ka, va);
     consume_tile(i + 1, kb, vb, false);
   }
-  if (i < n_full) {
-    if (has_tail) issue_tile(i + 1, kb, vb);
+  if (i + 1 < n_tiles) {
+    issue_tile(i + 1, kb, vb);
     consume_tile(i, ka, va, false);
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      ka[s] = kb[s];
-      va[s] = vb[s];
-    }
-    ++i;
+    consume_tile(i + 1, kb, vb, has_tail);
+  } else if (i < n_tiles) {
+    consume_tile(i, ka, va, has_tail);
   }
-  if (has_tail) consume_tile(i, ka, va, true);
 
   // ---- the 16 / LPT tokens rows of a DPP row merge in registers (rotations by 8, then 4) ----
   if constexpr (LPT <= 8) merge_lane_states<0x128>(m, l, acc);  // row_ror:8

@@ -244,29 +244,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     __builtin_amdgcn_wave_barrier();
   };
 
-  // same double-buffered walk as the VALU kernel
+  // same double-buffered walk as the VALU kernel (unconditional loads in the steady state)
   const int avail = max(0, min(p0 + pn - wbase, share));
   const int n_full = avail / kTileTokens;
   const bool has_tail = (avail % kTileTokens) != 0;
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
   int i = 0;
-  for (; i + 1 < n_full; i += 2) {
+  for (; i + 2 < n_tiles; i += 2) {
     issue_tile(i + 1, kb, vb);
     consume_tile(i, ka, va, false);
-    if (i + 2 < n_tiles) issue_tile(i + 2, ka, va);
+    issue_tile(i + 2, ka, va);
     consume_tile(i + 1, kb, vb, false);
   }
-  if (i < n_full) {
-    if (has_tail) issue_tile(i + 1, kb, vb);
+  if (i + 1 < n_tiles) {
+    issue_tile(i + 1, kb, vb);
     consume_tile(i, ka, va, false);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) ka[kk] = kb[kk];
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) va[u] = vb[u];
-    ++i;
+    consume_tile(i + 1, kb, vb, has_tail);
+  } else if (i < n_tiles) {
+    consume_tile(i, ka, va, has_tail);
   }
-  if (has_tail) consume_tile(i, ka, va, true);
 
   // row sums: the four lanes of a row held partial sums over their own tokens
 #pragma unroll
