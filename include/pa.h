@@ -73,11 +73,14 @@ int pa_last_hip_error(void);
 
 /*
  * Split-context partition size pa_decode uses for this shape: context tokens handled by one
- * workgroup. partition_tokens = 0 asks for the automatic choice: the largest power of two in
- * [256, 4096], at most max_context_len / 2, that still gives at least 1024 workgroups for
- * max_context_len (four per compute unit of a 256-CU gfx950), else 256. An explicit value must
- * be a power of two in [256, 4096] with value <= 256 * block_size. Returns 0 if the arguments
- * are invalid.
+ * workgroup. partition_tokens = 0 asks for the automatic choice: one partition per sequence
+ * (the smallest power of two >= max_context_len, at most 4096 and valid for the block size)
+ * when that grid still has at least 512 workgroups (two per compute unit of a 256-CU gfx950;
+ * 256 when G = Hq / Hkv >= 5, which runs on matrix-core tiles); otherwise the largest power of
+ * two in [256, 4096], at most max_context_len / 2, that still gives at least 1024 workgroups
+ * (256 when G >= 5), else 256. Workgroups = num_seqs x Hkv x head tiles per KV head x partitions.
+ * An explicit value must be a power of two in [256, 4096] with value <= 256 * block_size.
+ * Returns 0 if the arguments are invalid.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, int32_t max_context_len,

@@ -61,7 +61,7 @@ def test_partition_choice_and_workspace_size():
     assert pa.decode_partition_tokens(128, 32, 8, 128, 16, 7503) == 2048
     # block size 8 caps a partition at 2048 tokens, so 4096-token contexts split
     assert pa.decode_partition_tokens(64, 32, 8, 128, 8, 4096) == 2048
-    # matrix-core decode (G = 16k) aims at one workgroup per CU: MQA 64 x 2048 -> 4 partitions
+    # matrix-core decode (G >= 5) aims at one workgroup per CU: MQA 64 x 2048 -> 4 partitions
     assert pa.decode_partition_tokens(64, 32, 1, 128, 16, 2048) == 512
     # padded matrix-core tile, 64 seqs x 4 KV heads = 256 workgroups: one partition each
     assert pa.decode_partition_tokens(64, 32, 4, 128, 16, 2048) == 2048

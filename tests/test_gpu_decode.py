@@ -214,7 +214,7 @@ def test_workspace_reuse_leaves_counters_zero():
     assert int(counters.abs().sum()) == 0
 
 
-# ---- matrix-core path: 16 or more query heads per KV head -------------------------------------
+# ---- matrix-core path: 16 or 32 query heads per KV head (MQA-like) --------------------------
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [8, 16, 64])
 @pytest.mark.parametrize("kv_dtype", ["f16", "fp8_e4m3"])
