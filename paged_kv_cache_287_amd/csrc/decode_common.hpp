@@ -111,6 +111,41 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
     }
     return;
   }
+  if (nparts == 1) {
+    // this launch's only partition of the sequence plus the `extra` partials an earlier launch
+    // (the shared-prefix pass) stored: merge them here and write the output, with no publish of
+    // this partition and no arrival count
+    for (int idx = tid; idx < rows * D; idx += NTHREADS) {
+      const int h = idx / D, d = idx - h * D;
+      float mx, ls, a;
+      merge(h, d, mx, ls, a);
+      const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
+      float mv[kMaxPrefixSlices], lv[kMaxPrefixSlices], av[kMaxPrefixSlices];
+#pragma unroll
+      for (int j = 0; j < kMaxPrefixSlices; ++j) {
+        const bool in = j < extra;
+        const size_t slot = row0 + (in ? j : 0);
+        mv[j] = in ? fetch(p.ws_ml + slot * 2) : kNegInf;
+        lv[j] = in ? fetch(p.ws_ml + slot * 2 + 1) : 0.f;
+        av[j] = in ? fetch(p.ws_acc + slot * D + d) : 0.f;
+      }
+      float mc = mx;
+#pragma unroll
+      for (int j = 0; j < kMaxPrefixSlices; ++j) mc = fmaxf(mc, mv[j]);
+      const float ms = mc == kNegInf ? 0.f : mc;
+      const float w0 = fexp2(mx - ms);
+      ls *= w0;
+      a *= w0;
+#pragma unroll
+      for (int j = 0; j < kMaxPrefixSlices; ++j) {
+        const float w = fexp2(mv[j] - ms);
+        ls = fmaf(w, lv[j], ls);
+        a = fmaf(w, av[j], a);
+      }
+      p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(ls > 0.f ? a / ls : 0.f);
+    }
+    return;
+  }
 
   // ---- several partitions: publish this one's (max, sum, value sum) ----------------------
   for (int idx = tid; idx < rows * D; idx += NTHREADS) {
