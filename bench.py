@@ -49,7 +49,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones (the first ~10 ms of back-to-back "
+                         "calls after the GPU idled run ~6 %% slower on MI355X)")
     ap.add_argument("--workload", default="8b",
                     help="8b | tiny | prefix | sweep_bs{8,16,32,64} | variant_hkv{32,8,1}_{f16,fp8_e4m3}"
                          " | prefill_8b (chunked prefill: its own JSON line in TFLOP/s)")
@@ -69,6 +71,10 @@ def parse():
                          "known traffic that hardware byte counters are scaled against")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="split-context partition size passed to pa_decode (0 = library's choice)")
+    ap.add_argument("--append", choices=["fused", "separate"], default="fused",
+                    help="fused: the step's append runs inside the decode call (pa_decode_append) "
+                         "wherever the step is one token per sequence at its newest position; "
+                         "separate: pa_kv_write, then the decode call")
     ap.add_argument("--decode", choices=["auto", "plain", "shared_prefix"], default="auto",
                     help="decode entry point: shared_prefix reads each group's shared blocks once "
                          "(auto: whenever the workload has prefix groups)")
@@ -353,9 +359,20 @@ def main():
         max_prefix = max(1, int(case.group_prefix_blocks.max()))
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # pa_decode_append takes one new row per sequence, at its newest position L - 1
+    newest = [int(case.block_tables[b, (int(L) - 1) // case.block_size]) * case.block_size
+              + (int(L) - 1) % case.block_size if int(L) > 0 else -1
+              for b, L in enumerate(case.context_lens)]
+    fused = (args.append == "fused" and not shared and nk.shape[0] == case.num_seqs
+             and np.array_equal(np.asarray(slots, np.int64), np.asarray(newest, np.int64)))
 
     def decode():
-        if shared:
+        if fused:
+            pa.pa_decode_append(out, q, g_nk, g_nv, kc, vc, g_slots, tables, lens,
+                                float(case.scale), k_scale=ks, v_scale=vs,
+                                max_context_len=max_ctx, partition_tokens=part_tokens,
+                                workspace=ws)
+        elif shared:
             pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, g_gs, g_gpb, float(case.scale),
                                        max_group_seqs=max_group,
                                        max_prefix_blocks=max_prefix, k_scale=ks, v_scale=vs,
@@ -368,7 +385,8 @@ def main():
     def step():
         if g_pairs.shape[0]:
             pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
-        pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
+        if not fused:
+            pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
         decode()
 
     def timed(fn, n):
@@ -392,6 +410,26 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    # The attainable-bandwidth probe runs first: it also brings the idle GPU up to speed before
+    # the warm-up steps.
+    attainable = None
+    if args.probe_gib > 0:
+        progress(f"streaming-read probe over {args.probe_gib:g} GiB")
+        buf = torch.empty(int(args.probe_gib * 2 ** 30), dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        times = []
+        for i in range(12):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pa.stream_read_probe(buf, sink)
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 2:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        attainable = buf.numel() / statistics.median(times) / 1e9
+        del buf
 
     progress(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -450,24 +488,6 @@ def main():
                    "p90_us": times[(9 * len(times)) // 10]}
         del fa
 
-    attainable = None
-    if args.probe_gib > 0:
-        progress(f"streaming-read probe over {args.probe_gib:g} GiB")
-        buf = torch.empty(int(args.probe_gib * 2 ** 30), dtype=torch.uint8, device="cuda")
-        buf.fill_(1)
-        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        times = []
-        for i in range(12):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pa.stream_read_probe(buf, sink)
-            e1.record(stream)
-            e1.synchronize()
-            if i >= 2:
-                times.append(e0.elapsed_time(e1) * 1e-3)
-        attainable = buf.numel() / statistics.median(times) / 1e9
-        del buf
-
     swap = None
     if args.swap_blocks > 0:
         n = min(args.swap_blocks, case.num_blocks)
@@ -505,6 +525,8 @@ def main():
     seq_tokens = int(case.context_lens.sum())
     value = kvb / (ms_per_step * 1e-3) / 1e9
     call_bytes = decode_call_bytes(case)
+    if fused:  # the new rows: read from k_new / v_new and written to the cache
+        call_bytes += 2 * 2 * int(np.asarray(nk).nbytes)
     achieved = call_bytes / (avg_call_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -515,9 +537,12 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": ("pa_decode_shared_prefix (prefix pass prefill_kernel<PREFIX> + decode "
                            "partition kernel, merge fused)") if shared else
+                          ("pa_decode_append (decode partition kernel with the step's append and "
+                           "the cross-partition merge fused)") if fused else
                           "pa_decode (decode partition kernel, cross-partition merge fused)",
                 "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3,
-                "timing": "HIP events around the timed back-to-back pa_decode calls"}
+                "timing": "HIP events around the timed back-to-back calls of the entry point "
+                          "named in kernel"}
     cpu = None
     if not args.no_cpu_baseline:
         progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
@@ -542,9 +567,12 @@ def main():
                    "max_context_len": max_ctx, "q_heads": case.num_q_heads,
                    "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
                    "block_size": case.block_size, "kv_dtype": case.kv_dtype,
-                   "step": "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
+                   "step": ("copy_blocks(pairs) + decode_append (kv_write of 1 token/seq fused "
+                            "into the decode launch)") if fused else
+                           "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
                    "partition_tokens": part_tokens,
-                   "decode": "shared_prefix" if shared else "plain"},
+                   "decode": "shared_prefix" if shared else "plain",
+                   "append": "fused" if fused else "separate"},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attainable_read_gbs": attainable,
         "frac_of_attainable": None if attainable is None else value / attainable,

@@ -140,6 +140,46 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* stream);
 
 /*
+ * pa_decode_append — one decode step's append and attention in one call: the new token of
+ * every sequence is stored into the paged cache at its slot and attended together with the
+ * tokens already cached.
+ *
+ * A decode step writes the new token's key and value to the slot the block table gives it
+ * ("vLLM의 핵심 이해: PagedAttention", section 6: a token maps to a page and a position in it)
+ * and then attends over all tokens so far, the new one included ("serving-paged-attention",
+ * section "캐시가 얼마나 큰지부터"). This call computes exactly
+ *     pa_kv_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens = num_seqs, ...);
+ *     pa_decode(out, q, k_cache, v_cache, ...);
+ * with bit-identical out and caches. For fp16 caches whose head groups run on the vector-ALU
+ * decode kernel (G = Hq / Hkv <= 4, and groups above 32 that no 16- or 32-row matrix-core tile
+ * divides) it is one kernel launch: every workgroup covering position context_lens[b] - 1 takes
+ * that token's K/V from k_new/v_new[b] instead of the cache, and one workgroup per (sequence,
+ * KV head) stores them at slot_mapping[b]. Other shapes (E4M3 caches, 5 <= G <= 32, multiples
+ * of 16) launch the append kernel and then the decode kernel, both on `stream`.
+ *
+ *   k_new, v_new   [num_seqs, Hkv, D] fp16, device, 16-byte aligned: row b is sequence b's new
+ *                  token (one token per sequence, in sequence order).
+ *   slot_mapping   [num_seqs] int64, device, 8-byte aligned: block * block_size + offset of that
+ *                  token; < 0 (or >= num_blocks * block_size) = sequence b appends nothing this
+ *                  step and its cache is attended as it is.
+ *   k_scale, v_scale  as for pa_decode; for E4M3 caches they are updated by the append.
+ * Other arguments as for pa_decode (same workspace size: pa_decode_workspace_bytes).
+ * Precondition (not checked), beyond pa_decode's: a non-negative slot_mapping[b] is the slot of
+ * position context_lens[b] - 1 in b's table (the single-call fusion relies on it) and slots are
+ * unique. Violations give wrong values, never an access outside the buffers.
+ * Validated: as pa_decode, plus non-NULL k_new, v_new, slot_mapping with the alignments above,
+ * num_blocks * block_size < 2^31 and num_seqs * Hkv * D / 8 < 2^31.
+ */
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                     const int64_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                     int32_t partition_tokens, float scale, int32_t kv_dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_shared_prefix — pa_decode for batches in which groups of sequences share leading
  * blocks (one system prompt behind many requests, or the siblings of parallel sampling), with
  * the shared blocks read once per KV head for the whole group.

@@ -30,14 +30,17 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint4* __restrict__
   const int c = gid - row * chunks_per_row;
   const int t = row / num_kv_heads;
   const int h = row - t * num_kv_heads;
+  // the row's data and its slot are loaded together (one memory round trip, not two)
+  const size_t src = (size_t)row * chunks_per_row + c;
+  const uint4 kx = k[src];
+  const uint4 vx = v[src];
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;  // skipped token, or out of range: no write
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
   const size_t dst = (((size_t)blk * num_kv_heads + h) * block_size + off) * chunks_per_row + c;
-  const size_t src = (size_t)row * chunks_per_row + c;
-  k_cache[dst] = k[src];
-  v_cache[dst] = v[src];
+  k_cache[dst] = kx;
+  v_cache[dst] = vx;
 }
 
 // ---- append into an 8-bit (OCP E4M3) cache --------------------------------------------------

@@ -38,6 +38,12 @@
 //     prefix) are re-read from that XCD's L2.
 //   * results depend only on logical token positions (fixed tile, row and merge order), so
 //     they are deterministic and independent of physical block placement.
+//   * fused append (APPEND): the step's new token of each sequence (position L - 1, K/V rows
+//     given beside the cache) is both stored at its slot and attended in the same launch. Every
+//     workgroup that covers position L - 1 takes that token's K/V from the new rows instead of
+//     the cache, so no workgroup depends on another's store; the first head group of each KV
+//     head stores the rows from its last partition. The result is bit-identical to appending
+//     first and decoding afterwards.
 #include "decode_common.hpp"
 
 namespace pa {
@@ -128,8 +134,9 @@ __device__ __forceinline__ void merge_lane_states(float (&m)[GT], float (&l)[GT]
   }
 }
 
-template <int D, int BS, int GT, bool KV8>
+template <int D, int BS, int GT, bool KV8, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
+  static_assert(!(APPEND && KV8), "the fused append covers fp16 caches");
   using Lay = RowLayout<D, BS, GT, KV8>;
   constexpr int LPT = Lay::LPT;
   constexpr int E = Lay::E;
@@ -167,6 +174,21 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   const int lane = tid & 63;
   const int row = lane / LPT;   // token of the step
   const int col = lane % LPT;   // element chunk [col * E, col * E + E)
+
+  // ---- fused append: this lane's chunk of the new token's K and V rows ------------------
+  // Loaded whether or not the sequence appends (the row exists for every sequence), so the
+  // loads do not wait for the slot; newtok = L - 1 marks the position taken from them.
+  Chunk<NWORDS> knew{}, vnew{};
+  int64_t new_slot = -1;
+  int newtok = -1;
+  if constexpr (APPEND) {
+    const size_t nrow = ((size_t)b * p.num_kv_heads + kvh) * ROW_BYTES + col * LANE_BYTES;
+    knew = load_chunk<NWORDS>(p.k_new + nrow);
+    vnew = load_chunk<NWORDS>(p.v_new + nrow);
+    new_slot = p.slot_mapping[b];
+    if (new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS) newtok = L - 1;
+    else new_slot = -1;  // skipped token, or a slot outside the pool: no append
+  }
 
   // ---- query rows of this head group: E fp16 per lane per head -------------------------
   uint32_t qw[GT][NH2];
@@ -243,7 +265,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
         vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
       }
       uint32_t kh[NH2];
-      to_half_pairs<E, KV8>(kc[s], kh);
+      Chunk<NWORDS> kcs = kc[s];
+      if constexpr (APPEND) {
+        if (masked && tok0 + RW * s + row == newtok) kcs = knew;
+      }
+      to_half_pairs<E, KV8>(kcs, kh);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
         float d = 0.f;
@@ -293,7 +319,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     uint32_t vh[NSTEP][NH2];
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      to_half_pairs<E, KV8>(vc[s], vh[s]);
+      Chunk<NWORDS> vcs = vc[s];
+      if constexpr (APPEND) {
+        if (masked && tok0 + RW * s + row == newtok) vcs = vnew;
+      }
+      to_half_pairs<E, KV8>(vcs, vh[s]);
       if (masked) {
         const bool valid = tok0 + RW * s + row < L;
 #pragma unroll
@@ -328,8 +358,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   // unconditionally: a conditional load would make the compiler's wait counts assume the
   // shorter queue and drain the prefetched tile before the current one is finished.
   const int avail = max(0, min(p0 + pn - wbase, share));
-  const int n_full = avail / TT;
-  const bool has_tail = (avail % TT) != 0;
+  int n_full = avail / TT;
+  bool has_tail = (avail % TT) != 0;
+  if constexpr (APPEND) {
+    // the new token is the wave's last attended position: its tile takes the masked path,
+    // which substitutes the new rows (a tile past the end masks nothing else)
+    if (!has_tail && n_full > 0 && newtok >= wbase && newtok < wbase + avail) {
+      --n_full;
+      has_tail = true;
+    }
+  }
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
   int i = 0;
@@ -345,6 +383,20 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     consume_tile(i + 1, kb, vb, has_tail);
   } else if (i < n_tiles) {
     consume_tile(i, ka, va, has_tail);
+  }
+
+  // ---- fused append: store the new rows at their slot ----------------------------------
+  // Once per (sequence, KV head): the first head group's last partition, lanes 0 .. LPT-1 of
+  // wave 0 (one row). Nothing in this launch reads the slot's cached bytes for position L - 1.
+  if constexpr (APPEND) {
+    if (new_slot >= 0 && hg < p.num_kv_heads && part == nparts - 1 && wave == 0 && lane < LPT) {
+      const int64_t blk = new_slot / BS;
+      const int off = (int)(new_slot - blk * BS);
+      const size_t dst = ((size_t)blk * p.num_kv_heads + kvh) * TILE_BYTES +
+                         (size_t)off * ROW_BYTES + (size_t)col * LANE_BYTES;
+      store_chunk(p.k_cache_w + dst, knew);
+      store_chunk(p.v_cache_w + dst, vnew);
+    }
   }
 
   // ---- the 16 / LPT tokens rows of a DPP row merge in registers (rotations by 8, then 4) ----
@@ -389,34 +441,34 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, GT, local_merge);
 }
 
-template <int D, int BS, int GT, bool KV8>
+template <int D, int BS, int GT, bool KV8, bool APPEND>
 hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.head_groups, num_seqs, p.max_parts);
-  decode_partition_kernel<D, BS, GT, KV8><<<grid, kThreads, 0, stream>>>(p);
+  decode_partition_kernel<D, BS, GT, KV8, APPEND><<<grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int D, int BS, bool KV8>
+template <int D, int BS, bool KV8, bool APPEND>
 hipError_t dispatch_gt(const DecodeParams& p, int num_seqs, int gt, hipStream_t stream) {
   switch (gt) {
-    case 1: return launch_one<D, BS, 1, KV8>(p, num_seqs, stream);
-    case 2: return launch_one<D, BS, 2, KV8>(p, num_seqs, stream);
-    case 3: return launch_one<D, BS, 3, KV8>(p, num_seqs, stream);
-    case 4: return launch_one<D, BS, 4, KV8>(p, num_seqs, stream);
+    case 1: return launch_one<D, BS, 1, KV8, APPEND>(p, num_seqs, stream);
+    case 2: return launch_one<D, BS, 2, KV8, APPEND>(p, num_seqs, stream);
+    case 3: return launch_one<D, BS, 3, KV8, APPEND>(p, num_seqs, stream);
+    case 4: return launch_one<D, BS, 4, KV8, APPEND>(p, num_seqs, stream);
     case 8:
-      if constexpr (!KV8) return launch_one<D, BS, 8, KV8>(p, num_seqs, stream);  // E4M3: at most 4
+      if constexpr (!KV8) return launch_one<D, BS, 8, KV8, APPEND>(p, num_seqs, stream);  // E4M3: at most 4
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool APPEND>
 hipError_t dispatch_bs(const DecodeParams& p, int num_seqs, int bs, int gt, hipStream_t stream) {
   switch (bs) {
-    case 8: return dispatch_gt<D, 8, KV8>(p, num_seqs, gt, stream);
-    case 16: return dispatch_gt<D, 16, KV8>(p, num_seqs, gt, stream);
-    case 32: return dispatch_gt<D, 32, KV8>(p, num_seqs, gt, stream);
-    case 64: return dispatch_gt<D, 64, KV8>(p, num_seqs, gt, stream);
+    case 8: return dispatch_gt<D, 8, KV8, APPEND>(p, num_seqs, gt, stream);
+    case 16: return dispatch_gt<D, 16, KV8, APPEND>(p, num_seqs, gt, stream);
+    case 32: return dispatch_gt<D, 32, KV8, APPEND>(p, num_seqs, gt, stream);
+    case 64: return dispatch_gt<D, 64, KV8, APPEND>(p, num_seqs, gt, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -426,11 +478,18 @@ hipError_t dispatch_bs(const DecodeParams& p, int num_seqs, int bs, int gt, hipS
 hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                          int head_tile, bool kv_fp8, hipStream_t stream) {
   if (head_dim == 128)
-    return kv_fp8 ? dispatch_bs<128, true>(p, num_seqs, block_size, head_tile, stream)
-                  : dispatch_bs<128, false>(p, num_seqs, block_size, head_tile, stream);
+    return kv_fp8 ? dispatch_bs<128, true, false>(p, num_seqs, block_size, head_tile, stream)
+                  : dispatch_bs<128, false, false>(p, num_seqs, block_size, head_tile, stream);
   if (head_dim == 64)
-    return kv_fp8 ? dispatch_bs<64, true>(p, num_seqs, block_size, head_tile, stream)
-                  : dispatch_bs<64, false>(p, num_seqs, block_size, head_tile, stream);
+    return kv_fp8 ? dispatch_bs<64, true, false>(p, num_seqs, block_size, head_tile, stream)
+                  : dispatch_bs<64, false, false>(p, num_seqs, block_size, head_tile, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_append(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
+                                int head_tile, hipStream_t stream) {
+  if (head_dim == 128) return dispatch_bs<128, false, true>(p, num_seqs, block_size, head_tile, stream);
+  if (head_dim == 64) return dispatch_bs<64, false, true>(p, num_seqs, block_size, head_tile, stream);
   return hipErrorInvalidValue;
 }
 

@@ -59,6 +59,17 @@ __device__ __forceinline__ Chunk<NWORDS> load_chunk(const uint8_t* ptr) {
   return c;
 }
 
+template <int NWORDS>
+__device__ __forceinline__ void store_chunk(uint8_t* ptr, const Chunk<NWORDS>& c) {
+  if constexpr (NWORDS == 4) {
+    *reinterpret_cast<u32x4*>(ptr) = u32x4{c.w[0], c.w[1], c.w[2], c.w[3]};
+  } else if constexpr (NWORDS == 2) {
+    *reinterpret_cast<u32x2*>(ptr) = u32x2{c.w[0], c.w[1]};
+  } else {
+    *reinterpret_cast<uint32_t*>(ptr) = c.w[0];
+  }
+}
+
 // Context range [start, L) of sequence b covered by this call's partitions, and the number of
 // partial slots that an earlier pass already filled for it. Plain decode covers the whole
 // context. With shared-prefix groups, a member of a group with a non-empty prefix starts after

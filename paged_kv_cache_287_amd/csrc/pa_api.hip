@@ -94,10 +94,20 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 namespace {
 
-// Shared body of pa_decode and pa_decode_shared_prefix (groups == nullptr for plain decode).
+// The new-token arguments of pa_decode_append (all null for the other decode entry points).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+  float* k_scale_w;  // writable scales of an 8-bit cache
+  float* v_scale_w;
+};
+
+// Shared body of pa_decode, pa_decode_shared_prefix (groups != nullptr) and pa_decode_append
+// (app != nullptr).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                 const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                const int32_t* context_lens, const int32_t* group_start,
+                const int32_t* context_lens, const AppendArgs* app, const int32_t* group_start,
                 const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_seqs,
                 int32_t max_prefix_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -119,6 +129,14 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       !aligned(v_scale, 4))))
     return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535) return PA_ERR_INVALID_ARG;
+  if (app) {
+    if (!app->k_new || !app->v_new || !app->slot_mapping || !aligned(app->k_new, 16) ||
+        !aligned(app->v_new, 16) || !aligned(app->slot_mapping, 8))
+      return PA_ERR_INVALID_ARG;
+    if ((long long)num_blocks * block_size >= (1LL << 31)) return PA_ERR_INVALID_ARG;
+    if ((long long)num_seqs * num_kv_heads * (head_dim * 2 / 16) >= (1LL << 31))
+      return PA_ERR_INVALID_ARG;
+  }
   const bool groups = group_start != nullptr;
   if (groups) {
     if (!group_prefix_blocks || !aligned(group_start, 4) || !aligned(group_prefix_blocks, 4) ||
@@ -220,6 +238,28 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     const int rc = hip_status(pa::launch_prefix_pass(f, num_groups, head_dim, block_size, fp8, st));
     if (rc != PA_OK) return rc;
   }
+  if (app) {
+    if (!fp8 && !pa::decode_uses_mfma(group)) {
+      // one launch: the VALU decode kernel stores and attends the new rows itself
+      p.k_new = static_cast<const uint8_t*>(app->k_new);
+      p.v_new = static_cast<const uint8_t*>(app->v_new);
+      p.slot_mapping = app->slot_mapping;
+      p.k_cache_w = static_cast<uint8_t*>(const_cast<void*>(k_cache));
+      p.v_cache_w = static_cast<uint8_t*>(const_cast<void*>(v_cache));
+      return hip_status(pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, st));
+    }
+    // the append kernel first (E4M3 caches: with the block-scale policy), then the decode
+    const hipError_t e =
+        fp8 ? pa::launch_kv_write_fp8(app->k_new, app->v_new, const_cast<void*>(k_cache),
+                                      const_cast<void*>(v_cache), app->k_scale_w, app->v_scale_w,
+                                      app->slot_mapping, num_seqs, num_kv_heads, head_dim,
+                                      block_size, num_blocks, st)
+            : pa::launch_kv_write(app->k_new, app->v_new, const_cast<void*>(k_cache),
+                                  const_cast<void*>(v_cache), app->slot_mapping, num_seqs,
+                                  num_kv_heads, head_dim, block_size, num_blocks, st);
+    const int rc = hip_status(e);
+    if (rc != PA_OK) return rc;
+  }
   if (pa::decode_uses_mfma(group))
     return hip_status(pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8, st));
   return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8, st));
@@ -237,8 +277,23 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes_given,
               void* stream) {
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                     block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                     nullptr, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                     partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
+}
+
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                     const int64_t* slot_mapping, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                     int32_t partition_tokens, float scale, int32_t kv_dtype, void* workspace,
+                     size_t workspace_bytes_given, void* stream) {
+  const AppendArgs app{k_new, v_new, slot_mapping, k_scale, v_scale};
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
                      partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
 }
 
@@ -270,7 +325,7 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                             void* stream) {
   if (!group_start) return PA_ERR_INVALID_ARG;
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     group_start, group_prefix_blocks, num_groups, max_group_seqs,
+                     nullptr, group_start, group_prefix_blocks, num_groups, max_group_seqs,
                      max_prefix_blocks, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, partition_tokens, scale, kv_dtype,

@@ -143,6 +143,14 @@ struct DecodeParams {
   int32_t group;        // G = Hq / Hkv
   int32_t head_groups;  // G / GT workgroups per KV head
   float scale_log2;     // softmax scale * log2(e)
+  // Fused append (pa_decode_append, fp16 caches): the new token of sequence b sits at position
+  // context_lens[b] - 1; its rows k_new/v_new[b] ([S, Hkv, D]) are attended in place of the
+  // cache's and stored at slot_mapping[b] (< 0: no append). Null for plain decode.
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const int64_t* slot_mapping;
+  uint8_t* k_cache_w;   // writable views of k_cache / v_cache for that store
+  uint8_t* v_cache_w;
 };
 
 // ---- prefill geometry ------------------------------------------------------------------
@@ -198,6 +206,8 @@ struct PrefillParams {
 // Launchers: return hipSuccess or the launch error. Arguments are already validated.
 hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                          int head_tile, bool kv_fp8, hipStream_t stream);
+hipError_t launch_decode_append(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
+                                int head_tile, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                               int rows, bool kv_fp8, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,

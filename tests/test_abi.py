@@ -124,6 +124,37 @@ def test_decode_rejects_bad_arguments(over, expect):
     assert pa.lib.pa_decode(*decode_args(**over)) == expect
 
 
+def append_args(**over):
+    a = dict(out=FAKE, q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None,
+             v_scale=None, slot_mapping=FAKE, block_tables=FAKE, context_lens=FAKE, num_seqs=2,
+             num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10,
+             max_blocks_per_seq=4, max_context_len=0, partition_tokens=0, scale=0.125, kv_dtype=0,
+             workspace=None, workspace_bytes=0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(k_new=None), pa.PA_ERR_INVALID_ARG),
+    (dict(v_new=None), pa.PA_ERR_INVALID_ARG),
+    (dict(slot_mapping=None), pa.PA_ERR_INVALID_ARG),
+    (dict(k_new=FAKE + 8), pa.PA_ERR_INVALID_ARG),  # misaligned new rows
+    (dict(v_new=FAKE + 2), pa.PA_ERR_INVALID_ARG),
+    (dict(slot_mapping=FAKE + 4), pa.PA_ERR_INVALID_ARG),
+    (dict(num_blocks=1 << 28), pa.PA_ERR_INVALID_ARG),  # num_blocks * BS >= 2^31
+    # and everything pa_decode checks
+    (dict(out=None), pa.PA_ERR_INVALID_ARG),
+    (dict(num_q_heads=7), pa.PA_ERR_INVALID_ARG),
+    (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1), pa.PA_ERR_INVALID_ARG),  # E4M3 without scales
+    (dict(k_scale=FAKE, v_scale=FAKE), pa.PA_ERR_INVALID_ARG),  # fp16 with scales
+    (dict(max_blocks_per_seq=64), pa.PA_ERR_WORKSPACE),
+    (dict(partition_tokens=300), pa.PA_ERR_UNSUPPORTED),
+])
+def test_decode_append_rejects_bad_arguments(over, expect):
+    assert pa.lib.pa_decode_append(*append_args(**over)) == expect
+
+
 def kvw_args(**over):
     a = dict(k=FAKE, v=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
              slot_mapping=FAKE, num_tokens=3,
