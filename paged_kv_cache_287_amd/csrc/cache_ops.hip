@@ -67,8 +67,10 @@ __device__ __forceinline__ uint32_t enc_pair(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
+// Launched with two waves per (token, KV head): wave 0 appends K, wave 1 appends V (each cache
+// has its own scales, so the two are independent and run side by side).
 template <int D>
-__global__ __launch_bounds__(64) void kv_write_fp8_kernel(
+__global__ __launch_bounds__(128) void kv_write_fp8_kernel(
     const _Float16* __restrict__ k, const _Float16* __restrict__ v, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
     const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int block_size,
@@ -85,18 +87,24 @@ __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
     const int64_t sp = slot_mapping[t0 - 1];
     if (sp >= 0 && sp < num_slots && sp / block_size == blk) return;
   }
-  const int lane = threadIdx.x;
-  for (int which = 0; which < 2; ++which) {
+  const int lane = threadIdx.x & 63;
+  const int which = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  {
     uint8_t* tile = (which == 0 ? k_cache : v_cache) + ((size_t)blk * num_kv_heads + h) * block_size * D;
     float* sc = (which == 0 ? k_scale : v_scale) + (size_t)blk * num_kv_heads + h;
+    const _Float16* src = which == 0 ? k : v;
     // The block's scale is carried through the run in a (wave-uniform) register, and every lane
     // only ever touches its own PER bytes of each row, so no lane reads what another wrote.
+    // The block's stored scale and the next token's slot are loaded before they are needed, so
+    // each token costs one memory round trip.
+    const float s_stored = *sc;
     float s_cur = 0.f;
+    int64_t slot = slot0;
     for (int t = t0; t < num_tokens; ++t) {
-      const int64_t slot = t == t0 ? slot0 : slot_mapping[t];
       if (t > t0 && (slot < 0 || slot >= num_slots || slot / block_size != blk)) break;
+      const int64_t next = t + 1 < num_tokens ? slot_mapping[t + 1] : -1;
       const int off = (int)(slot - blk * block_size);
-      const _Float16* row = (which == 0 ? k : v) + ((size_t)t * num_kv_heads + h) * D;
+      const _Float16* row = src + ((size_t)t * num_kv_heads + h) * D;
       float x[PER];
       float amax = 0.f;
 #pragma unroll
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
       }
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-      const float s_prev = off == 0 ? 0.f : (t == t0 ? *sc : s_cur);
+      const float s_prev = off == 0 ? 0.f : (t == t0 ? s_stored : s_cur);
       float s = amax > s_prev * e4m3_max() ? amax / e4m3_max() : s_prev;
       if (s == 0.f) s = 1.f;
       if (s != s_prev && off > 0) {
@@ -134,6 +142,7 @@ __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
         *dst = (uint8_t)(o & 0xFFu);
       }
       s_cur = s;
+      slot = next;
     }
     if (lane == 0) *sc = s_cur;
   }
@@ -231,11 +240,11 @@ hipError_t launch_kv_write_fp8(const void* k, const void* v, void* k_cache, void
   auto kc = static_cast<uint8_t*>(k_cache);
   auto vc = static_cast<uint8_t*>(v_cache);
   if (head_dim == 128)
-    kv_write_fp8_kernel<128><<<grid, 64, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
+    kv_write_fp8_kernel<128><<<grid, 128, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
                                                       slot_mapping, num_tokens, num_kv_heads,
                                                       block_size, slots);
   else
-    kv_write_fp8_kernel<64><<<grid, 64, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
+    kv_write_fp8_kernel<64><<<grid, 128, 0, stream>>>(kk, vv, kc, vc, k_scale, v_scale,
                                                      slot_mapping, num_tokens, num_kv_heads,
                                                      block_size, slots);
   return hipGetLastError();

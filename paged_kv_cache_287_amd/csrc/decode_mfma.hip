@@ -22,7 +22,10 @@
 // dot2 chains (GQA-8 at 64 x 2,048 tokens: 51 us against 76 us for fp16 KV, 45 against 64 for
 // E4M3), while at 4 heads the VALU kernel is as fast (fp16) or faster (E4M3).
 // Everything else (partitioning, block-id walk, double-buffered non-temporal loads, fp8 scales,
-// merge through LDS, partial publish / last-arrival merge) follows the VALU kernel.
+// merge through LDS, partial publish / last-arrival merge, the fused append) follows the VALU
+// kernel. For the fused append the new K/V rows of the workgroup's (sequence, KV head) are
+// staged once in LDS (512 bytes at D 128), where the lanes of position L - 1 read them in the
+// last tile: holding them in registers would cost the 16-row tile a wave per SIMD.
 #include "decode_common.hpp"
 
 namespace pa {
@@ -33,8 +36,9 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int D, int BS, int NT, bool KV8>
+template <int D, int BS, int NT, bool KV8, bool APPEND>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p) {
+  static_assert(!(APPEND && KV8), "the fused append covers fp16 caches");
   constexpr int R = 16 * NT;         // query rows of one KV head handled by a workgroup
   constexpr int TPL = D / 32;        // consecutive V tokens a lane loads (one 8-dim chunk)
   constexpr int VTS = 20;            // V^T row stride in halves (16 tokens + 4): the staging
@@ -81,6 +85,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                        ? *reinterpret_cast<const h8*>(p.q + ((size_t)b * p.num_q_heads + h0 +
                                                              16 * nt + lr) * D + 32 * kk + 8 * lq)
                        : h8{0, 0, 0, 0, 0, 0, 0, 0};
+
+  // ---- fused append: threads 0 .. 2 NEWC - 1 load the new K row's, then the new V row's
+  // 16-byte chunks (the rows exist for every sequence; the slot decides whether they are used)
+  constexpr int NEWC = ROW_BYTES / 16;
+  __shared__ __align__(16) uint8_t s_new[APPEND ? 2 * ROW_BYTES : 16];
+  Chunk<4> nrow{};
+  int64_t new_slot = -1;
+  int newtok = -1;  // position whose K/V come from s_new instead of the cache
+  if constexpr (APPEND) {
+    const size_t roff = ((size_t)b * p.num_kv_heads + kvh) * ROW_BYTES + (tid % NEWC) * 16;
+    if (tid < 2 * NEWC) nrow = load_chunk<4>((tid < NEWC ? p.k_new : p.v_new) + roff);
+    new_slot = p.slot_mapping[b];
+    if (new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS) newtok = L - 1;
+    else new_slot = -1;  // skipped token, or a slot outside the pool: no append
+  }
 
   // ---- block ids of this wave's tokens: lane j holds logical block wbase / BS + j ------------
   // The partition's tokens [p0, p0 + pn) are split evenly over the waves in whole tiles, so a
@@ -185,6 +204,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     h8 kA[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) kA[kk] = to_h8(kc[kk]);
+    if constexpr (APPEND) {
+      if (masked && tok0 + lr == newtok) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          kA[kk] = *reinterpret_cast<const h8*>(s_new + (32 * kk + 8 * lq) * 2);
+      }
+    }
     h4 pB[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -221,6 +247,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
       vv[u] = to_h8(vc[u]);
+      if constexpr (APPEND) {
+        if (masked && tok0 + TPL * vtg + u == newtok)
+          vv[u] = *reinterpret_cast<const h8*>(s_new + ROW_BYTES + vch * 16);
+      }
       if (masked && tok0 + TPL * vtg + u >= L) vv[u] = h8{0, 0, 0, 0, 0, 0, 0, 0};
     }
 #pragma unroll
@@ -246,10 +276,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 
   // same double-buffered walk as the VALU kernel (unconditional loads in the steady state)
   const int avail = max(0, min(p0 + pn - wbase, share));
-  const int n_full = avail / kTileTokens;
-  const bool has_tail = (avail % kTileTokens) != 0;
+  int n_full = avail / kTileTokens;
+  bool has_tail = (avail % kTileTokens) != 0;
+  if constexpr (APPEND) {
+    // the new token is the wave's last attended position: its tile takes the masked path
+    if (!has_tail && n_full > 0 && newtok >= wbase && newtok < wbase + avail) {
+      --n_full;
+      has_tail = true;
+    }
+  }
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
+  if constexpr (APPEND) {
+    // after the first tile's loads: the block-id wait before them has already retired the
+    // new-row loads, so staging them costs no extra round trip
+    if (tid < 2 * NEWC)
+      *reinterpret_cast<u32x4*>(s_new + tid * 16) = u32x4{nrow.w[0], nrow.w[1], nrow.w[2], nrow.w[3]};
+    __syncthreads();
+  }
   int i = 0;
   for (; i + 2 < n_tiles; i += 2) {
     issue_tile(i + 1, kb, vb);
@@ -263,6 +307,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     consume_tile(i + 1, kb, vb, has_tail);
   } else if (i < n_tiles) {
     consume_tile(i, ka, va, has_tail);
+  }
+
+  // fused append: the first head group's last partition stores the new rows at their slot
+  if constexpr (APPEND) {
+    if (new_slot >= 0 && hg == kvh * p.head_groups && part == nparts - 1 && tid < 2 * NEWC) {
+      const int64_t blk = new_slot / BS;
+      const int off = (int)(new_slot - blk * BS);
+      const size_t dst = ((size_t)blk * p.num_kv_heads + kvh) * TILE_BYTES +
+                         (size_t)off * ROW_BYTES + (size_t)(tid % NEWC) * 16;
+      *reinterpret_cast<u32x4*>((tid < NEWC ? p.k_cache_w : p.v_cache_w) + dst) =
+          *reinterpret_cast<const u32x4*>(s_new + tid * 16);
+    }
   }
 
   // row sums: the four lanes of a row held partial sums over their own tokens
@@ -308,28 +364,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   finish_partition<R, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, rows, local_merge);
 }
 
-template <int D, int BS, int NT, bool KV8>
+template <int D, int BS, int NT, bool KV8, bool APPEND>
 hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.head_groups, num_seqs, p.max_parts);
-  decode_mfma_kernel<D, BS, NT, KV8><<<grid, kThreads, 0, stream>>>(p);
+  decode_mfma_kernel<D, BS, NT, KV8, APPEND><<<grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int D, bool KV8, int NT>
+template <int D, bool KV8, int NT, bool APPEND>
 hipError_t dispatch_bs(const DecodeParams& p, int num_seqs, int bs, hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_one<D, 8, NT, KV8>(p, num_seqs, stream);
-    case 16: return launch_one<D, 16, NT, KV8>(p, num_seqs, stream);
-    case 32: return launch_one<D, 32, NT, KV8>(p, num_seqs, stream);
-    case 64: return launch_one<D, 64, NT, KV8>(p, num_seqs, stream);
+    case 8: return launch_one<D, 8, NT, KV8, APPEND>(p, num_seqs, stream);
+    case 16: return launch_one<D, 16, NT, KV8, APPEND>(p, num_seqs, stream);
+    case 32: return launch_one<D, 32, NT, KV8, APPEND>(p, num_seqs, stream);
+    case 64: return launch_one<D, 64, NT, KV8, APPEND>(p, num_seqs, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool APPEND = false>
 hipError_t dispatch_rows(const DecodeParams& p, int num_seqs, int bs, int rows, hipStream_t stream) {
-  return rows > 16 ? dispatch_bs<D, KV8, 2>(p, num_seqs, bs, stream)
-                    : dispatch_bs<D, KV8, 1>(p, num_seqs, bs, stream);
+  return rows > 16 ? dispatch_bs<D, KV8, 2, APPEND>(p, num_seqs, bs, stream)
+                    : dispatch_bs<D, KV8, 1, APPEND>(p, num_seqs, bs, stream);
 }
 
 }  // namespace
@@ -342,6 +398,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim,
   if (head_dim == 64)
     return kv_fp8 ? dispatch_rows<64, true>(p, num_seqs, block_size, rows, stream)
                   : dispatch_rows<64, false>(p, num_seqs, block_size, rows, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_mfma_append(const DecodeParams& p, int num_seqs, int head_dim,
+                                     int block_size, int rows, hipStream_t stream) {
+  if (head_dim == 128) return dispatch_rows<128, false, true>(p, num_seqs, block_size, rows, stream);
+  if (head_dim == 64) return dispatch_rows<64, false, true>(p, num_seqs, block_size, rows, stream);
   return hipErrorInvalidValue;
 }
 

@@ -239,13 +239,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     if (rc != PA_OK) return rc;
   }
   if (app) {
-    if (!fp8 && !pa::decode_uses_mfma(group)) {
-      // one launch: the VALU decode kernel stores and attends the new rows itself
+    if (!fp8) {
+      // one launch: the decode kernel stores and attends the new rows itself
       p.k_new = static_cast<const uint8_t*>(app->k_new);
       p.v_new = static_cast<const uint8_t*>(app->v_new);
       p.slot_mapping = app->slot_mapping;
       p.k_cache_w = static_cast<uint8_t*>(const_cast<void*>(k_cache));
       p.v_cache_w = static_cast<uint8_t*>(const_cast<void*>(v_cache));
+      if (pa::decode_uses_mfma(group))
+        return hip_status(pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, st));
       return hip_status(pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, st));
     }
     // the append kernel first (E4M3 caches: with the block-scale policy), then the decode

@@ -2,8 +2,8 @@
 attend) against the float64 oracle's append followed by its decode, and bit-equality with the
 two-call path (pa_kv_write, then pa_decode) on the same inputs.
 
-The fused single launch covers fp16 caches with head groups on the vector-ALU kernel; E4M3
-caches and matrix-core head groups run the append kernel and then the decode kernel, and are
+For fp16 caches the call is one launch of the decode kernel (vector-ALU or matrix-core, by
+head-group size); E4M3 caches run the append kernel and then the decode kernel, and are
 checked here the same way. Lengths include multiples of every tile size (the new token then ends
 a full tile), a single token (the output must be the new value row exactly), sequences that skip
 the append (negative slot) and explicit 256-token partitions (the new token in the last of
@@ -116,9 +116,11 @@ def test_append_gqa4_ragged(d, bs, partition_tokens):
         assert np.array_equal(got[h], nv[0, h // 4].view(np.int16)), h
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (33, 1), (16, 2), (32, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (33, 1), (16, 2), (32, 1), (24, 2),
+                                    (64, 2)])
 def test_append_head_groupings(hq, hkv):
-    """G = 1, 2, 3 and 33 run the fused launch; G = 8 and 32 (matrix-core decode) append first."""
+    """G = 1, 2, 3 and 33 on the vector-ALU kernel; G = 8 (padded 16-row tile) and 32 (two
+    16-row tiles) on the matrix-core kernel."""
     case = workloads.random_case(720 + hq + hkv, LENS, hq, hkv, 128, 16,
                                  name=f"append_{hq}q_{hkv}kv")
     check_case(case, 721 + hq, skip=(5,), what=f"append {hq}q/{hkv}kv")
@@ -126,11 +128,13 @@ def test_append_head_groupings(hq, hkv):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_append_fp8_cache(d):
-    """E4M3 caches: the block-scale append, then the decode (two launches)."""
-    case = workloads.random_case(740 + d, LENS, 8, 2, d, 16, kv_dtype="fp8_e4m3",
-                                 name=f"append_fp8_d{d}")
-    check_case(case, 741 + d, skip=(3,), what=f"append E4M3 D{d}")
+@pytest.mark.parametrize("hq", [8, 64])
+def test_append_fp8_cache(d, hq):
+    """E4M3 caches: the block-scale append, then the decode (two launches), on the vector-ALU
+    (G 4) and matrix-core (G 32) kernels."""
+    case = workloads.random_case(740 + d + hq, LENS, hq, 2, d, 16, kv_dtype="fp8_e4m3",
+                                 name=f"append_fp8_d{d}_{hq}q")
+    check_case(case, 741 + d, skip=(3,), what=f"append E4M3 D{d} {hq}q")
 
 
 def test_append_reuses_workspace_and_repeats_bit_exactly():
@@ -181,3 +185,16 @@ def test_append_8b_workload_full_size():
     ek, ev = oracle.kv_write(nk, nv, case.k_cache, case.v_cache, slots)
     ref = oracle_decode(case, seqs=seqs, k_cache=ek, v_cache=ev)
     assert_attention_close(out1[seqs], ref, "append, 8b workload")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
+def test_append_matrix_core_ragged(d, bs):
+    """MQA-like groups (32 query heads per KV head) over every block size and head size, with
+    256-token partitions: the new rows reach the matrix-core tiles through LDS."""
+    case = workloads.random_case(800 + d + bs, LENS, 32, 1, d, bs, name=f"append_mqa_d{d}_bs{bs}")
+    nk, nv, slots, out = check_case(case, 801 + bs, skip=(4,), partition_tokens=256,
+                                    what=f"append MQA D{d} BS{bs}")
+    got = bits(out)[0]
+    for h in range(case.num_q_heads):
+        assert np.array_equal(got[h], nv[0, 0].view(np.int16)), h
