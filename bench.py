@@ -466,6 +466,20 @@ def main():
     progress(f"timing {args.steps} decode calls")
     _, event_call = timed(decode, args.steps)
     avg_call_ms = event_call * 1e3
+    separate_ms = None
+    if fused:
+        # the same step with the append as its own launch (pa_kv_write, then pa_decode), for
+        # comparison: bit-identical results
+        def step_separate():
+            if g_pairs.shape[0]:
+                pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
+            pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
+            pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
+                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws)
+
+        progress(f"timing {args.steps} steps with the append launched separately")
+        _, event_sep = timed(step_separate, args.steps)
+        separate_ms = event_sep * 1e3
 
     # per-call timing after evicting L2 and the 256 MiB Infinity Cache with a 1 GiB read (a
     # read leaves no dirty lines behind whose write-back would slow the timed call)
@@ -558,6 +572,7 @@ def main():
         "event_ms_per_step": event_step * 1e3,
         "launch": "eager" if graph is None else "hip graph replay of the step",
         "eager_ms_per_step": eager_wall * 1e3,
+        "separate_append_event_ms_per_step": separate_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -78,12 +78,21 @@ def trace(args) -> None:
         if dom is None and is_dominant(name, args.kernel):
             dom = (name, int(r["Calls"]), avg)
     out.append("")
+    # kernels that run once per call beside the dominant one (the shared-prefix pass)
+    extra = []
+    for pre in args.also:
+        for r in rows:
+            if is_dominant(r["Name"], pre):
+                extra.append((r["Name"], float(r["AverageNs"]) / 1e3))
+                break
     if dom is not None:
         nbytes = roof["algorithmic_bytes_per_call"]
-        gbs = nbytes / (dom[2] * 1e-6) / 1e9
-        out.append(f"`{short(dom[0], 200)}`: {nbytes} algorithmic bytes per call (KV + q + out + "
-                   f"table entries, plus the appended rows when the append is fused) / "
-                   f"{dom[2]:.1f} us average over {dom[1]} calls = {gbs:.0f} GB/s "
+        call_us = dom[2] + sum(t for _, t in extra)
+        gbs = nbytes / (call_us * 1e-6) / 1e9
+        parts = " + ".join([f"{dom[2]:.1f} us (`{short(dom[0], 200)}`, {dom[1]} calls)"] +
+                           [f"{t:.1f} us (`{short(n, 200)}`)" for n, t in extra])
+        out.append(f"{nbytes} algorithmic bytes per call (KV + q + out + table entries, plus the "
+                   f"appended rows when the append is fused) / {parts} average = {gbs:.0f} GB/s "
                    f"({100 * gbs / 8000:.1f} % of 8 TB/s).")
         out.append(f"The same run's bench line: {roof['avg_call_us']:.1f} us per call "
                    f"(HIP events over the timed back-to-back calls), {b['ms_per_step'] * 1e3:.1f} "
@@ -165,6 +174,8 @@ def main() -> None:
     ap.add_argument("--command", action="append", default=[], help="command that made the data")
     ap.add_argument("--kernel", default="decode_partition_kernel",
                     help="name prefix of the dominant kernel")
+    ap.add_argument("--also", action="append", default=[],
+                    help="name prefix of another kernel launched once per call (trace mode)")
     ap.add_argument("--workload", default="8b", help="bench.py --workload of the run")
     ap.add_argument("--out", required=True)
     ap.add_argument("--json", default=None)

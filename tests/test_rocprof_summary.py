@@ -76,3 +76,7 @@ def test_trace_reports_the_dominant_kernel(tmp_path):
     assert "| `decode_partition_kernel<128, 16, 4, false, true>` | 10 | 165.0 | 160.0 | 170.0 |" in text
     # 1 GiB per call / 165 us
     assert "6508 GB/s (81.3 % of 8 TB/s)" in text
+    # a second kernel of the same call adds its average to the call time: 1 GiB / 175 us
+    run("trace", str(d), "--bench-log", str(tmp_path / "b.log"), "--command", "cmd", "--also",
+        "other", "--out", out)
+    assert "6136 GB/s (76.7 % of 8 TB/s)" in open(out).read()
