@@ -86,14 +86,22 @@ def trace(args) -> None:
                 extra.append((r["Name"], float(r["AverageNs"]) / 1e3))
                 break
     if dom is not None:
-        nbytes = roof["algorithmic_bytes_per_call"]
         call_us = dom[2] + sum(t for _, t in extra)
-        gbs = nbytes / (call_us * 1e-6) / 1e9
         parts = " + ".join([f"{dom[2]:.1f} us (`{short(dom[0], 200)}`, {dom[1]} calls)"] +
                            [f"{t:.1f} us (`{short(n, 200)}`)" for n, t in extra])
-        out.append(f"{nbytes} algorithmic bytes per call (KV + q + out + table entries, plus the "
-                   f"appended rows when the append is fused) / {parts} average = {gbs:.0f} GB/s "
-                   f"({100 * gbs / 8000:.1f} % of 8 TB/s).")
+        if roof.get("unit") == "TFLOP/s":
+            flops = b["flops_per_call"]
+            tf = flops / (call_us * 1e-6) / 1e12
+            out.append(f"{flops} algorithmic flops per call (4 D per attended query-key pair and "
+                       f"query head) / {parts} average = {tf:.0f} TFLOP/s "
+                       f"({100 * tf / roof['peak']:.1f} % of the {roof['peak']:.0f} TFLOP/s "
+                       f"dense fp16 matrix-core peak).")
+        else:
+            nbytes = roof["algorithmic_bytes_per_call"]
+            gbs = nbytes / (call_us * 1e-6) / 1e9
+            out.append(f"{nbytes} algorithmic bytes per call (KV + q + out + table entries, plus "
+                       f"the appended rows when the append is fused) / {parts} average = "
+                       f"{gbs:.0f} GB/s ({100 * gbs / 8000:.1f} % of 8 TB/s).")
         out.append(f"The same run's bench line: {roof['avg_call_us']:.1f} us per call "
                    f"(HIP events over the timed back-to-back calls), {b['ms_per_step'] * 1e3:.1f} "
                    f"us per step, value {b['value']:.0f} {b['unit']}.")
