@@ -85,11 +85,13 @@ def test_head_groupings(hq, hkv):
                                          (8, 1, 64, 8), (12, 4, 128, 32), (6, 2, 64, 64),
                                          (16, 2, 64, 16), (64, 8, 64, 8), (24, 2, 128, 16),
                                          (20, 2, 64, 32), (15, 1, 128, 8), (48, 2, 128, 16),
-                                         (40, 5, 64, 16)])
+                                         (40, 5, 64, 16), (88, 1, 128, 16), (88, 1, 64, 32),
+                                         (70, 2, 64, 16)])
 @pytest.mark.parametrize("kv_dtype", ["f16", "fp8_e4m3"])
 def test_head_groupings_dims_and_dtypes(hq, hkv, d, bs, kv_dtype):
-    """Groups of 8 to 15 (one padded 16-row matrix-core tile), of 24 (VALU tiles of 8 heads for
-    fp16, 4 for E4M3) and of 3 and 2, with KV-head counts that are and are not multiples of 8,
+    """Groups of 8 to 15 (one padded 16-row matrix-core tile), 20 and 24 (padded 32-row tiles),
+    3 and 2 (VALU), 88 (the one size up to 128 on VALU tiles of 8 heads for fp16, 4 for E4M3)
+    and 35 (VALU, one head per tile), with KV-head counts that are and are not multiples of 8,
     over both head dims and the VALU kernel's lane layouts (16, 8 or 4 lanes per token)."""
     case = workloads.random_case(210 + hq + hkv + d + bs, [5, 300, 777, 64], hq, hkv, d, bs,
                                  kv_dtype=kv_dtype, name=f"groups_{hq}q_{hkv}kv_d{d}_{kv_dtype}")

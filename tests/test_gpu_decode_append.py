@@ -116,11 +116,12 @@ def test_append_gqa4_ragged(d, bs, partition_tokens):
         assert np.array_equal(got[h], nv[0, h // 4].view(np.int16)), h
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (33, 1), (16, 2), (32, 1), (24, 2),
-                                    (64, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (33, 1), (88, 1), (35, 1), (16, 2),
+                                    (32, 1), (24, 2), (64, 2)])
 def test_append_head_groupings(hq, hkv):
-    """G = 1, 2, 3 and 33 on the vector-ALU kernel; G = 8 (padded 16-row tile) and 32 (two
-    16-row tiles) on the matrix-core kernel."""
+    """G = 1, 2, 3, 33 (3-head tiles), 88 (8-head tiles) and 35 (1-head tiles) on the
+    vector-ALU kernel; G = 8 and 12 (padded 16-row tiles) and 32 (two 16-row tiles) on the
+    matrix-core kernel."""
     case = workloads.random_case(720 + hq + hkv, LENS, hq, hkv, 128, 16,
                                  name=f"append_{hq}q_{hkv}kv")
     check_case(case, 721 + hq, skip=(5,), what=f"append {hq}q/{hkv}kv")
