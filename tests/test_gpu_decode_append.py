@@ -199,3 +199,36 @@ def test_append_matrix_core_ragged(d, bs):
     got = bits(out)[0]
     for h in range(case.num_q_heads):
         assert np.array_equal(got[h], nv[0, 0].view(np.int16)), h
+
+
+@pytest.mark.parametrize("name", ["variant_hkv1_f16", "variant_hkv4_f16", "variant_hkv32_fp8_e4m3",
+                                  "sweep_bs16"])
+def test_append_full_size_workloads(name):
+    """The benchmark's other workloads at full size in the launch configuration it times
+    (automatic partition size): MQA and GQA-8 through the matrix-core fused launch, MHA with an
+    E4M3 cache through the append-then-decode route, and uneven lengths split over several
+    partitions. Fused against two calls bit for bit (outputs and caches), the oracle on sampled
+    sequences."""
+    case = gen(workloads.by_name, name)
+    nk, nv, slots = new_rows(case, 790)
+    g_nk, g_nv, g_slots = dev(nk), dev(nv), dev(slots)
+    d1 = case_to_device(case)
+    out1 = run_fused(d1, g_nk, g_nv, g_slots, case.scale)
+    d2 = case_to_device(case)
+    out2 = run_two_calls(d2, g_nk, g_nv, g_slots, case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), name
+    for key in ("k_cache", "v_cache", "k_scale", "v_scale"):
+        if d1[key] is not None:
+            assert torch.equal(d1[key].view(torch.uint8), d2[key].view(torch.uint8)), key
+    del d2
+    seqs = [0, 21, 42, case.num_seqs - 1]
+    if case.kv_dtype == "f16":
+        ek, ev = oracle.kv_write(nk, nv, case.k_cache, case.v_cache, slots)
+        eks = evs = None
+    else:
+        ek, ev, eks, evs = oracle.kv_write_fp8(nk, nv, case.k_cache, case.v_cache, case.k_scale,
+                                               case.v_scale, slots)
+    ref = oracle.decode(case.q, ek, ev, case.block_tables, case.context_lens, case.scale,
+                        kv_dtype=case.kv_dtype, k_scale=eks, v_scale=evs, seqs=seqs)
+    assert_attention_close(out1[seqs], ref, f"append, {name}")
