@@ -232,3 +232,53 @@ def test_append_full_size_workloads(name):
     ref = oracle.decode(case.q, ek, ev, case.block_tables, case.context_lens, case.scale,
                         kv_dtype=case.kv_dtype, k_scale=eks, v_scale=evs, seqs=seqs)
     assert_attention_close(out1[seqs], ref, f"append, {name}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 1)])
+def test_append_captured_in_a_graph_replays_exactly(hq, hkv):
+    """pa_decode_append captured once into a HIP graph (256-token partitions, so every replay
+    also runs the cross-partition merge and returns the arrival counters to zero) and replayed
+    several times with eager work between the replays: every replay matches the eager call bit
+    for bit. The workspace is passed in, so nothing inside the capture allocates or clears."""
+    import paged_kv_cache_287_amd as pa
+
+    case = workloads.random_case(820 + hq, LENS, hq, hkv, 128, 16, name=f"append_graph_{hq}q")
+    nk, nv, slots = new_rows(case, 821)
+    ek, ev, _, _, ref = expected(case, nk, nv, slots)
+    d = case_to_device(case)
+    g_nk, g_nv, g_slots = dev(nk), dev(nv), dev(slots)
+    need = pa.decode_workspace_bytes(case.num_seqs, hq, hkv, 128, 16,
+                                     case.block_tables.shape[1] * 16, 0, 256)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+
+    def step():
+        pa.pa_decode_append(out, d["q"], g_nk, g_nv, d["k_cache"], d["v_cache"], g_slots,
+                            d["block_tables"], d["context_lens"], float(case.scale),
+                            partition_tokens=256, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_attention_close(eager, ref, f"eager fused step {hq}q/{hkv}kv")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+    assert np.array_equal(bits(d["k_cache"]), host_bits(ek))
+    assert np.array_equal(bits(d["v_cache"]), host_bits(ev))
+    assert int(ws[:256].count_nonzero()) == 0, "arrival counters not returned to zero"
