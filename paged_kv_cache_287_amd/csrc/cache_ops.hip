@@ -81,8 +81,9 @@ __global__ __launch_bounds__(128) void kv_write_fp8_kernel(
   const int64_t slot0 = slot_mapping[t0];
   if (slot0 < 0 || slot0 >= num_slots) return;
   const int64_t blk = slot0 / block_size;
-  // Consecutive tokens of the call that land in one block form a run; the wave of the run's
-  // first token applies them in order (the scale policy is sequential within a block).
+  // Consecutive tokens of the call that land in one block form a run; the workgroup of the
+  // run's first token applies them in order, K in one wave and V in the other (the scale policy
+  // is sequential within a block).
   if (t0 > 0) {
     const int64_t sp = slot_mapping[t0 - 1];
     if (sp >= 0 && sp < num_slots && sp / block_size == blk) return;
