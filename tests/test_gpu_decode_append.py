@@ -282,3 +282,15 @@ def test_append_captured_in_a_graph_replays_exactly(hq, hkv):
     assert np.array_equal(bits(d["k_cache"]), host_bits(ek))
     assert np.array_equal(bits(d["v_cache"]), host_bits(ev))
     assert int(ws[:256].count_nonzero()) == 0, "arrival counters not returned to zero"
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 1)])
+def test_append_with_empty_sequences(hq, hkv):
+    """Sequences with an empty context (nothing appended, slot -1) between ordinary ones: their
+    output is +0 and the pool equals the oracle's append of the others, on both kernels."""
+    case = workloads.random_case(840 + hq, [0, 1, 37, 0, 16, 300], hq, hkv, 128, 16,
+                                 name=f"append_empty_{hq}q")
+    nk, nv, slots, out = check_case(case, 841, what=f"append with empty contexts {hq}q/{hkv}kv")
+    assert slots[0] == -1 and slots[3] == -1
+    got = bits(out)
+    assert (got[0] == 0).all() and (got[3] == 0).all()
