@@ -347,19 +347,34 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   }
   __syncthreads();
 
-  auto local_merge = [&](int h, int d, float& mx, float& ls, float& a) {
-    mx = kNegInf;
+  // Each row's running max, wave weights and running sum are formed once (one thread per row)
+  // and then shared by its D elements, in the order a per-element merge would use.
+  __shared__ float s_wt[kWaves][R];
+  __shared__ float s_row[R][2];
+  if (tid < rows) {
+    const int h = tid;
+    float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_ml[(w * R + h) * 2]);
     const float ms = mx == kNegInf ? 0.f : mx;
-    ls = 0.f;
-    a = 0.f;
+    float ls = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float wt = fexp2(s_ml[(w * R + h) * 2] - ms);
       ls = fmaf(wt, s_ml[(w * R + h) * 2 + 1], ls);
-      a = fmaf(wt, s_acc[(w * R + h) * D + d], a);
+      s_wt[w][h] = wt;
     }
+    s_row[h][0] = mx;
+    s_row[h][1] = ls;
+  }
+  __syncthreads();
+
+  auto local_merge = [&](int h, int d, float& mx, float& ls, float& a) {
+    mx = s_row[h][0];
+    ls = s_row[h][1];
+    a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) a = fmaf(s_wt[w][h], s_acc[(w * R + h) * D + d], a);
   };
   finish_partition<R, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, rows, local_merge);
 }
