@@ -88,10 +88,39 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
 
 /* Bytes of device workspace pa_decode needs for these arguments (same meaning as in pa_decode;
  * max_context_len must be the value pa_decode will see, > 0); 0 if none is needed (every
- * sequence fits one partition) or if the arguments are invalid. */
+ * sequence fits one partition) or if the arguments are invalid. The value is a multiple of
+ * 16384. A larger workspace serves every call whose own size fits in it (see below).
+ *
+ * Workspace layout. The split partitions of a sequence are merged by the workgroup that
+ * arrives last, which needs one arrival counter per (sequence, head group) besides the partial
+ * results themselves (talk summary, FlashAttention paragraph: partial softmax states combine
+ * exactly). A workspace of W bytes (the workspace_bytes argument) is split by W alone: the first
+ * Z = 256 * floor(W / 16384) bytes are the counter zone, the rest the partial zone. Every call
+ * keeps its counters at the start of the counter zone and its partials at the start of the
+ * partial zone, so calls of different shapes (more sequences, more head groups, other partition
+ * sizes) can share one buffer: no call reads as a counter a byte that another call wrote as a
+ * partial. Rules:
+ *   - pass the same workspace_bytes in every call on one buffer (the zones depend on it);
+ *   - the counter zone must be zero before the first call: zero-fill the buffer, or call
+ *     pa_decode_workspace_reset. Every call that runs to completion leaves it zero again;
+ *   - calls sharing a workspace must not overlap in time (same stream, or synchronised);
+ *   - if a call did not run to completion (an aborted or failed stream) or calls did overlap,
+ *     counters may be left non-zero, and a later call would then leave some outputs unwritten:
+ *     call pa_decode_workspace_reset before the next use. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t kv_dtype, int32_t partition_tokens);
+
+/*
+ * pa_decode_workspace_reset — enqueue a clear of a decode workspace's counter zone (its first
+ * 256 * floor(workspace_bytes / 16384) bytes) on `stream`, as a kernel (graph-capturable, no
+ * memset node). Use it on fresh memory instead of a full zero-fill, and to recover after a call
+ * that did not complete or calls that overlapped (see the workspace layout above). The partial
+ * zone needs no clearing. A workspace smaller than 16384 bytes has no counter zone: PA_OK, nothing
+ * enqueued.
+ * Validated: workspace non-NULL and 256-byte aligned when there is something to clear.
+ */
+int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_decode — one query token per sequence attends over its paged KV cache.
@@ -114,11 +143,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                    pa_decode_partition_tokens). Results are bit-identical for a given
  *                    partition size; different sizes round differently (within tolerance).
  *   scale            softmax scale (finite), usually 1/sqrt(head_dim).
- *   workspace        >= pa_decode_workspace_bytes(...) bytes of device memory, 256-byte
- *                    aligned (may be NULL when that size is 0). It must be ZERO-FILLED before
- *                    its first use; every call leaves the bytes it uses as counters at zero
- *                    again, so one zero-fill serves any later calls that fit in it. Calls that
- *                    share a workspace must not overlap in time (same stream, or synchronised).
+ *   workspace        device memory, 256-byte aligned, of workspace_bytes >=
+ *                    pa_decode_workspace_bytes(...) bytes (may be NULL when that size is 0),
+ *                    under the rules of the workspace layout above: its counter zone is zero
+ *                    before the first call (zero-fill, or pa_decode_workspace_reset), every
+ *                    completed call leaves it zero, and one buffer, always passed with the
+ *                    same workspace_bytes, serves later calls of any shape that fit in it.
+ *                    Calls that share a workspace must not overlap in time.
  *   num_blocks       NB, the number of blocks in each cache.
  * Preconditions (not checked): 0 <= context_lens[b] <= max_context_len (as passed or implied);
  * 0 <= block_tables[b, i] < num_blocks for i < ceil(L / BS) (later entries are never read);
@@ -211,8 +242,8 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
  *                        that are attended per sequence, which gives the same result. The
  *                        prefix is cut into at most 4 slices of at least 128 tokens, one
  *                        workgroup each, so that short prefixes still spread over the GPU.
- *   workspace            >= pa_decode_shared_prefix_workspace_bytes(...) bytes, zero-filled
- *                        before its first use, as for pa_decode (always needed here).
+ *   workspace            >= pa_decode_shared_prefix_workspace_bytes(...) bytes, under the
+ *                        rules of pa_decode's workspace (always needed here).
  * Other arguments as for pa_decode.
  * Preconditions (not checked), beyond pa_decode's: every member's first group_prefix_blocks[g]
  * table entries equal the first member's, and group_prefix_blocks[g] * block_size <= the

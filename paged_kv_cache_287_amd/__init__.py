@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
-    "decode_workspace_bytes", "decode_partition_tokens", "pa_decode",
+    "decode_workspace_bytes", "decode_workspace_reset", "decode_partition_tokens", "pa_decode",
     "shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_prefill", "pa_kv_write",
     "pa_copy_blocks", "pa_swap_blocks", "stream_read_probe",
 ]
@@ -57,6 +57,7 @@ EXPORTED_SYMBOLS = {
     "pa_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _p]),
     "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
+    "pa_decode_workspace_reset": (ctypes.c_int, [_p, _sz, _p]),
 }
 
 
@@ -122,6 +123,17 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
     """Workspace bytes for pa_decode (allocate zero-filled: it holds counters)."""
     return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                              block_size, max_context_len, kv_dtype, partition_tokens))
+
+
+def decode_workspace_reset(workspace: torch.Tensor, *, stream=None) -> None:
+    """Enqueue a clear of the workspace's counter zone (fresh memory, or recovery after a call
+    that did not complete)."""
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    st = lib.pa_decode_workspace_reset(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_workspace_reset")
 
 
 def decode_partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

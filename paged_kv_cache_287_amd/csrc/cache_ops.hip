@@ -201,6 +201,15 @@ __global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
   }
 }
 
+// Zero fill of a 16-byte aligned range with vector stores (a kernel rather than a memset
+// node, so that a caller may capture it in a graph): clears the arrival counters of a decode
+// workspace.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
 
 hipError_t launch_swap_blocks(const void* src_k, const void* src_v, const float* src_ks,
@@ -259,6 +268,15 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
   copy_blocks_kernel<<<dim3(num_pairs, num_kv_heads), kCopyThreads, 0, stream>>>(
       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), k_scale, v_scale,
       block_mapping, num_kv_heads, chunks_per_tile, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const size_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 1024 ? want : 1024);
+  zero_fill_kernel<<<blocks, 256, 0, stream>>>(static_cast<uint4*>(p), n);
   return hipGetLastError();
 }
 

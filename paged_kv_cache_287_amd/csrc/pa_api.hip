@@ -172,8 +172,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const pa::WorkspaceLayout ws = pa::workspace_layout(num_seqs, num_q_heads,
                                                       num_kv_heads * (group / gt), head_dim,
                                                       part_slots);
-  if (ws.total > 0 &&
-      (workspace == nullptr || workspace_bytes_given < ws.total || !aligned(workspace, 256)))
+  if (ws.total > 0 && (workspace == nullptr || !pa::workspace_fits(ws, workspace_bytes_given) ||
+                       !aligned(workspace, 256)))
     return PA_ERR_WORKSPACE;
 
   pa::DecodeParams p{};
@@ -186,9 +186,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   char* wsb = static_cast<char*>(workspace);
-  p.counters = ws.total ? reinterpret_cast<int32_t*>(wsb + ws.counters_off) : nullptr;
-  p.ws_ml = ws.total ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
-  p.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc_off) : nullptr;
+  const size_t zone = pa::ws_counter_zone(workspace_bytes_given);
+  p.counters = ws.total ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+  p.ws_ml = ws.total ? reinterpret_cast<float*>(wsb + zone + ws.ml_rel) : nullptr;
+  p.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + zone + ws.acc_rel) : nullptr;
   p.group_start = group_start;
   p.group_prefix_blocks = group_prefix_blocks;
   p.num_groups = groups ? num_groups : 0;
@@ -467,6 +468,13 @@ int pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scal
                                            num_kv_heads, head_dim, block_size, src_num_blocks,
                                            dst_num_blocks, fp8 ? 1 : 2,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  const size_t zone = pa::ws_counter_zone(workspace_bytes);
+  if (zone == 0) return PA_OK;  // too small to hold counters: nothing to clear
+  if (!workspace || !aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_zero_fill(workspace, zone, static_cast<hipStream_t>(stream)));
 }
 
 int pa_stream_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {

@@ -96,21 +96,43 @@ inline int auto_part_tokens(int num_seqs, int units_per_seq, int max_context_len
   return kMinPartTokens;
 }
 
-// Workspace layout: [counters: S * HG_total int32][ml: S*Hq*P*2 f32][acc: S*Hq*P*D f32], each
-// section 256-byte aligned. Needed only when a sequence may span more than one partition.
+// Workspace layout. A workspace of W bytes is split by its size alone into a counter zone
+// [0, Z(W)) and a partial zone [Z(W), W), with Z(W) = 256 * floor(W / 16384): 1/64 of the
+// buffer. A call keeps its arrival counters ([S * HG_total] int32) at the start of the counter
+// zone and its partials ([ml: S*Hq*P*2 f32][acc: S*Hq*P*D f32], 256-byte aligned) at the start
+// of the partial zone. Calls of any shape that pass the same W therefore never read a byte as a
+// counter that another call wrote as a partial: the zones do not depend on the call's shape.
+// Needed only when a sequence may span more than one partition (or take prefix partials).
+constexpr size_t kWsGranule = 16384;
+constexpr size_t kWsCounterPerGranule = 256;
+inline size_t ws_counter_zone(size_t w) { return w / kWsGranule * kWsCounterPerGranule; }
+
 struct WorkspaceLayout {
-  size_t counters_off, ml_off, acc_off, total;
+  size_t counter_bytes;  // bytes of counters this call uses (0: no workspace needed)
+  size_t partial_bytes;  // bytes of partials this call uses
+  size_t ml_rel, acc_rel;  // offsets of the two partial arrays inside the partial zone
+  size_t total;          // smallest W whose zones hold both (a multiple of kWsGranule)
 };
 inline WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_groups_total,
                                         int head_dim, int max_parts) {
-  WorkspaceLayout w{0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0};
   if (max_parts <= 1) return w;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-  w.ml_off = up((size_t)num_seqs * head_groups_total * sizeof(int32_t));
-  w.acc_off = w.ml_off + up(rows * 2 * sizeof(float));
-  w.total = w.acc_off + rows * head_dim * sizeof(float);
+  w.counter_bytes = (size_t)num_seqs * head_groups_total * sizeof(int32_t);
+  w.ml_rel = 0;
+  w.acc_rel = up(rows * 2 * sizeof(float));
+  w.partial_bytes = w.acc_rel + rows * head_dim * sizeof(float);
+  const size_t n_ctr = (w.counter_bytes + kWsCounterPerGranule - 1) / kWsCounterPerGranule;
+  const size_t per_granule = kWsGranule - kWsCounterPerGranule;
+  const size_t n_par = (w.partial_bytes + per_granule - 1) / per_granule;
+  w.total = (n_ctr > n_par ? n_ctr : n_par) * kWsGranule;
   return w;
+}
+// True when a workspace of `given` bytes holds this call's counters and partials.
+inline bool workspace_fits(const WorkspaceLayout& w, size_t given) {
+  const size_t z = ws_counter_zone(given);
+  return w.counter_bytes <= z && w.partial_bytes <= given - z;
 }
 
 struct DecodeParams {
@@ -232,6 +254,7 @@ hipError_t launch_swap_blocks(const void* src_k, const void* src_v, const float*
                               float* dst_vs, const int32_t* block_mapping, int num_pairs,
                               int num_kv_heads, int head_dim, int block_size, int src_blocks,
                               int dst_blocks, int elem_bytes, hipStream_t stream);
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace pa

@@ -77,10 +77,20 @@ def test_partition_choice_and_workspace_size():
     assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096, 7, 0) == 0
     # one partition: no workspace
     assert pa.decode_workspace_bytes(64, 32, 8, 128, 16, 512, 0, 512) == 0
-    # counters (64 seqs x 8 head groups) + (m, l) + values, 256-byte aligned sections
+    # A workspace of W bytes has a counter zone of 256 bytes per 16 KiB and a partial zone for
+    # the rest; the size is the fewest 16 KiB granules whose zones hold the call's counters
+    # (64 seqs x 8 head groups, int32) and its partials ((m, l) then values, 256-byte aligned)
     rows = 64 * 32 * 8
-    expect = (64 * 8 * 4 + 255) // 256 * 256 + (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
-    assert pa.decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0, 512) == expect
+    counters = 64 * 8 * 4
+    partials = (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    granules = max(-(-counters // 256), -(-partials // (16384 - 256)))
+    assert pa.decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0, 512) == granules * 16384
+    # MHA with many sequences: 4096 seqs x 32 head groups of counters (2048 granules' worth) still
+    # fit the counter zone of the granules the partials need
+    w = pa.decode_workspace_bytes(4096, 32, 32, 64, 16, 512, 0, 256)
+    rows = 4096 * 32 * 2
+    assert w == -(-(rows * 8 + rows * 64 * 4) // (16384 - 256)) * 16384
+    assert 4096 * 32 * 4 <= w // 16384 * 256
     assert pa.decode_workspace_bytes(64, 32, 8, 96, 16, 4096) == 0  # unsupported head_dim
     assert pa.decode_workspace_bytes(64, 32, 8, 128, 12, 4096) == 0  # unsupported block size
 
@@ -115,6 +125,8 @@ def decode_args(**over):
     (dict(num_seqs=70000), pa.PA_ERR_INVALID_ARG),
     (dict(max_blocks_per_seq=64), pa.PA_ERR_WORKSPACE),  # 1024 tokens -> 4 partitions of 256
     (dict(max_blocks_per_seq=64, workspace=FAKE, workspace_bytes=10), pa.PA_ERR_WORKSPACE),
+    # 4 seqs x 2 head groups of counters and 4 x 8 x 4 partial rows need 5 granules of 16 KiB
+    (dict(max_blocks_per_seq=64, workspace=FAKE, workspace_bytes=4 * 16384), pa.PA_ERR_WORKSPACE),
     (dict(max_blocks_per_seq=64, workspace=FAKE + 16, workspace_bytes=1 << 30), pa.PA_ERR_WORKSPACE),
     (dict(partition_tokens=300), pa.PA_ERR_UNSUPPORTED),
     (dict(partition_tokens=8192), pa.PA_ERR_UNSUPPORTED),
@@ -313,3 +325,12 @@ def test_shared_prefix_workspace_has_one_more_slot_per_row():
     assert shared - plain >= 64 * 32 * (2 + 128) * 4
     assert pa.shared_prefix_workspace_bytes(4, 8, 2, 128, 16, 64) > 0
     assert pa.decode_workspace_bytes(4, 8, 2, 128, 16, 64) == 0
+
+
+def test_workspace_reset_validation():
+    # smaller than one 16 KiB granule: no counter zone, nothing to clear, nothing enqueued
+    assert pa.lib.pa_decode_workspace_reset(None, 16383, None) == pa.PA_OK
+    assert pa.lib.pa_decode_workspace_reset(None, 0, None) == pa.PA_OK
+    # a counter zone to clear needs a 256-byte aligned buffer
+    assert pa.lib.pa_decode_workspace_reset(None, 1 << 20, None) == pa.PA_ERR_INVALID_ARG
+    assert pa.lib.pa_decode_workspace_reset(FAKE + 16, 1 << 20, None) == pa.PA_ERR_INVALID_ARG

@@ -266,40 +266,90 @@ def test_fp8_append_rounds_ties_to_even():
 
 @pytest.mark.parametrize("kv_dtype", ["f16", "fp8_e4m3"])
 def test_swap_out_to_pinned_host_and_back(kv_dtype):
+    """Preemption by swap ("serving-paged-attention", section "그래도 넘칠 때 — 선점"): every
+    block of two sequences goes out to a pinned host pool and comes back into fresh device
+    blocks. After each leg the whole destination pool (K, V and, for E4M3, both scale arrays)
+    equals oracle.swap_blocks bit for bit, and the source pool is untouched; decode through the
+    re-pointed tables then matches the oracle and the decode from before the swap."""
     import paged_kv_cache_287_amd as pa
 
+    rng = np.random.default_rng(701)
     case = workloads.random_case(700, [300, 1000, 77, 513], 32, 8, 128, 16, kv_dtype=kv_dtype,
                                  pool_factor=3.0)
+    fp8 = kv_dtype != "f16"
     d = case_to_device(case)
+    ref = oracle_decode(case)
     before = gpu_decode(d, case.scale, partition_tokens=256)
-    # swap out every block of sequences 1 and 3 into a pinned host pool
+    assert_attention_close(before, ref, f"swap {kv_dtype}: decode before the swap")
     seqs = [1, 3]
     ids = np.concatenate([case.block_tables[b, : -(-int(case.context_lens[b]) // 16)] for b in seqs])
     n = len(ids)
-    shape = (n,) + case.k_cache.shape[1:]
-    tdt = torch.float16 if kv_dtype == "f16" else torch.uint8
-    hk = torch.zeros(shape, dtype=tdt).pin_memory()
-    hv = torch.zeros(shape, dtype=tdt).pin_memory()
-    hks = hvs = None
-    if kv_dtype != "f16":
-        hks = torch.zeros((n, case.num_kv_heads), dtype=torch.float32).pin_memory()
-        hvs = torch.zeros_like(hks).pin_memory()
-    out_map = np.stack([ids, np.arange(n)], 1).astype(np.int32)
+    # the host pool has spare blocks and holds garbage, so that untouched slots are checked too,
+    # and the blocks land in a scattered order
+    nh = n + 9
+    shape = (nh,) + case.k_cache.shape[1:]
+    if fp8:
+        hk0 = rng.integers(0, 256, shape, dtype=np.uint8)
+        hv0 = rng.integers(0, 256, shape, dtype=np.uint8)
+        hks0 = rng.random((nh, case.num_kv_heads), dtype=np.float32)
+        hvs0 = rng.random((nh, case.num_kv_heads), dtype=np.float32)
+    else:
+        hk0 = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+        hv0 = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+        hks0 = hvs0 = None
+
+    def pinned(x):
+        if x is None:
+            return None
+        t = torch.from_numpy(x.view(np.int16) if x.dtype == np.float16 else x).pin_memory()
+        return t.view(torch.float16) if x.dtype == np.float16 else t
+
+    hk, hv, hks, hvs = pinned(hk0), pinned(hv0), pinned(hks0), pinned(hvs0)
+    host_slots = rng.permutation(nh)[:n]
+    out_map = np.stack([ids, host_slots], 1).astype(np.int32)
     log(f"[swap] {kv_dtype}: {n} blocks out to pinned host memory")
     pa.pa_swap_blocks(d["k_cache"], d["v_cache"], hk, hv, dev(out_map), src_k_scale=d["k_scale"],
                       src_v_scale=d["v_scale"], dst_k_scale=hks, dst_v_scale=hvs)
     torch.cuda.synchronize()
-    assert (bits(hk) == host_bits(case.k_cache[ids])).all()
-    assert (bits(hv) == host_bits(case.v_cache[ids])).all()
-    if hks is not None:
-        assert (bits(hks) == host_bits(case.k_scale[ids])).all()
-    # clobber the old device blocks, swap back in at fresh ids, re-point the tables
-    d["k_cache"][torch.from_numpy(ids).long().cuda()] = 0
+    src_scales = (case.k_scale, case.v_scale) if fp8 else None
+    ek, ev, es = oracle.swap_blocks(case.k_cache, case.v_cache, hk0, hv0, out_map,
+                                    src_scales=src_scales,
+                                    dst_scales=(hks0, hvs0) if fp8 else None)
+    assert (bits(hk) == host_bits(ek)).all() and (bits(hv) == host_bits(ev)).all()
+    if fp8:
+        assert (bits(hks) == host_bits(es[0])).all() and (bits(hvs) == host_bits(es[1])).all()
+    # the device pool the blocks left is unchanged
+    assert (bits(d["k_cache"]) == host_bits(case.k_cache)).all()
+    assert (bits(d["v_cache"]) == host_bits(case.v_cache)).all()
+
+    # clobber the old device blocks (data and scales), then swap back in at free ids
+    dk, dv = case.k_cache.copy(), case.v_cache.copy()
+    dk[ids] = dk.dtype.type(0)
+    dv[ids] = dv.dtype.type(0)
+    dks = dvs = None
+    if fp8:
+        dks, dvs = case.k_scale.copy(), case.v_scale.copy()
+        dks[ids] = np.float32(-1.0)
+        dvs[ids] = np.float32(-1.0)
+    d["k_cache"], d["v_cache"] = dev_cache(dk), dev_cache(dv)
+    if fp8:
+        d["k_scale"], d["v_scale"] = dev(dks), dev(dvs)
     used = set(int(x) for r, L in zip(case.block_tables, case.context_lens) for x in r[: -(-int(L) // 16)])
-    free = np.array([i for i in range(case.num_blocks) if i not in used and i != case.pad_block][:n])
-    in_map = np.stack([np.arange(n), free], 1).astype(np.int32)
-    pa.pa_swap_blocks(hk, hv, d["k_cache"], d["v_cache"], dev(in_map), src_k_scale=hks, src_v_scale=hvs,
-                      dst_k_scale=d["k_scale"], dst_v_scale=d["v_scale"])
+    free = np.array([i for i in rng.permutation(case.num_blocks)
+                     if int(i) not in used and int(i) != case.pad_block][:n])
+    in_map = np.stack([host_slots, free], 1).astype(np.int32)
+    log(f"[swap] {kv_dtype}: {n} blocks back into the device pool")
+    pa.pa_swap_blocks(hk, hv, d["k_cache"], d["v_cache"], dev(in_map), src_k_scale=hks,
+                      src_v_scale=hvs, dst_k_scale=d["k_scale"], dst_v_scale=d["v_scale"])
+    torch.cuda.synchronize()
+    fk, fv, fs = oracle.swap_blocks(ek, ev, dk, dv, in_map, src_scales=es,
+                                    dst_scales=(dks, dvs) if fp8 else None)
+    assert (bits(d["k_cache"]) == host_bits(fk)).all() and (bits(d["v_cache"]) == host_bits(fv)).all()
+    if fp8:
+        assert (bits(d["k_scale"]) == host_bits(fs[0])).all()
+        assert (bits(d["v_scale"]) == host_bits(fs[1])).all()
+    # the host pool the blocks left is unchanged
+    assert (bits(hk) == host_bits(ek)).all() and (bits(hv) == host_bits(ev)).all()
     tables = case.block_tables.copy()
     pos = 0
     for b in seqs:
@@ -308,4 +358,15 @@ def test_swap_out_to_pinned_host_and_back(kv_dtype):
         pos += nb_
     after = gpu_decode(d, case.scale, block_tables=dev(tables), partition_tokens=256)
     torch.cuda.synchronize()
+    ref_after = oracle.decode(case.q, fk, fv, tables, case.context_lens, case.scale,
+                              kv_dtype=kv_dtype, k_scale=fs[0] if fp8 else None,
+                              v_scale=fs[1] if fp8 else None)
+    assert_attention_close(after, ref_after, f"swap {kv_dtype}: decode after the round trip")
     assert (bits(after) == bits(before)).all()
+
+
+def dev_cache(x: np.ndarray) -> torch.Tensor:
+    """A cache array on the device with its dtype (fp16 pools travel as their bit patterns)."""
+    if x.dtype == np.float16:
+        return dev(x.view(np.uint16)).view(torch.float16)
+    return dev(x)
