@@ -14,7 +14,9 @@
  *   - Pointers are DEVICE pointers unless marked otherwise; every call only enqueues work on
  *     `stream` (a hipStream_t; NULL = the legacy default stream) and returns without waiting.
  *   - The caller owns every buffer (including the decode workspace). The library allocates,
- *     frees and synchronises nothing and keeps no per-call state; calls are re-entrant.
+ *     frees and synchronises nothing and keeps no per-call state; calls are re-entrant. The one
+ *     exception is pa_decode_append_noalloc, whose workspace is a fixed device array inside
+ *     the library (one per GPU, shared by every such call on that GPU).
  *   - Only host-side scalars and pointers are validated, before anything is enqueued. On a
  *     validation failure nothing is enqueued and the status code says why. Launch failures
  *     return PA_ERR_HIP; pa_last_hip_error() then gives the hipError_t (per calling thread).
@@ -208,6 +210,40 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                      int32_t partition_tokens, float scale, int32_t kv_dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Size of the library's own decode workspace (per GPU) used by pa_decode_append_noalloc. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * pa_decode_append_noalloc — pa_decode_append without a caller-provided workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It allocates nothing and calls no allocating routine.
+ *
+ * Arguments, semantics and results are those of pa_decode_append (bit-identical outputs and
+ * caches for the same arguments), minus workspace and workspace_bytes: the split-context
+ * partials and arrival counters live in a file-scope device array of PA_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that each GPU the library runs on holds until the process ends.
+ *   - A call whose pa_decode_workspace_bytes(...) exceeds PA_NOALLOC_SCRATCH_BYTES returns
+ *     PA_ERR_WORKSPACE before anything is enqueued (choose a larger partition_tokens, or use
+ *     pa_decode_append with a workspace).
+ *   - The first call on a GPU that needs the array looks up its device address (the current
+ *     device's copy, hipGetSymbolAddress) and enqueues a clear of its counters on `stream`; that
+ *     first call should not be under graph capture. Later calls reuse the address.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents; each
+ *     completed call leaves its counters at zero. Calls that overlap in time on one GPU (other
+ *     streams, other threads) race on the array and give wrong results: serialise them.
+ * The current device (hipGetDevice) must be the device of the buffers and of `stream`.
+ * Validated: as pa_decode_append; PA_ERR_WORKSPACE as above; PA_ERR_UNSUPPORTED for a device
+ * ordinal >= 64.
+ */
+int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             const int64_t* slot_mapping, const int32_t* block_tables,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, int32_t partition_tokens, float scale,
+                             int32_t kv_dtype, void* stream);
 
 /*
  * pa_decode_shared_prefix — pa_decode for batches in which groups of sequences share leading

@@ -21,6 +21,7 @@ __all__ = [
     "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE", "PA_ERR_HIP",
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
     "decode_workspace_bytes", "decode_workspace_reset", "decode_partition_tokens", "pa_decode",
+    "pa_decode_append", "pa_decode_append_noalloc", "NOALLOC_SCRATCH_BYTES",
     "shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_prefill", "pa_kv_write",
     "pa_copy_blocks", "pa_swap_blocks", "stream_read_probe",
 ]
@@ -58,7 +59,13 @@ EXPORTED_SYMBOLS = {
                                       _i32, _i32, _i32, _p]),
     "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
     "pa_decode_workspace_reset": (ctypes.c_int, [_p, _sz, _p]),
+    "pa_decode_append_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
+                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                _f32, _i32, _p]),
 }
+
+#: bytes of the library's own per-GPU decode workspace (pa_decode_append_noalloc)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PaError(RuntimeError):
@@ -239,6 +246,50 @@ def pa_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_
                               _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_append")
+    return out
+
+
+def pa_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                             v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                             context_lens: torch.Tensor, scale: float, *,
+                             k_scale: Optional[torch.Tensor] = None,
+                             v_scale: Optional[torch.Tensor] = None, max_context_len: int = 0,
+                             partition_tokens: int = 0, stream=None) -> torch.Tensor:
+    """``pa_decode_append`` whose workspace is the library's own per-GPU device array: neither
+    this binding nor the library allocates. Calls that overlap on one GPU race on that array."""
+    _check(q, "q", (torch.float16,), 3)
+    _check(out, "out", (torch.float16,), 3)
+    _check(k_new, "k_new", (torch.float16,), 3)
+    _check(v_new, "v_new", (torch.float16,), 3)
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    _check(block_tables, "block_tables", (torch.int32,), 2)
+    _check(context_lens, "context_lens", (torch.int32,), 1)
+    kvt = _kv_dtype(k_cache)
+    if kvt == PA_KV_FP8_E4M3:
+        for n, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{n} is required for an 8-bit cache")
+            _check(s, n, (torch.float32,), 2)
+    num_seqs, num_q_heads, head_dim = q.shape
+    nb, num_kv_heads, block_size, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != head_dim or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if k_new.shape != (num_seqs, num_kv_heads, head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [num_seqs, Hkv, head_dim]")
+    if (block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs
+            or slot_mapping.shape[0] != num_seqs):
+        raise ValueError("block_tables / context_lens / slot_mapping must have one row per sequence")
+    st = lib.pa_decode_append_noalloc(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                      _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens),
+                                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, nb,
+                                      block_tables.shape[1], max_context_len, partition_tokens,
+                                      float(scale), kvt, _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_append_noalloc")
     return out
 
 

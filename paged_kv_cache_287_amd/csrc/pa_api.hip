@@ -3,9 +3,16 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/pa.h"
 #include "pa_internal.hpp"
+
+// Decode workspace of pa_decode_append_noalloc: each GPU the library runs on holds its own copy
+// for the life of the process (16 MiB, PA_NOALLOC_SCRATCH_BYTES in pa.h).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static_assert(kScratchBytes % pa::kWsGranule == 0, "whole workspace granules");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -41,6 +48,35 @@ bool resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int bloc
   *part_tokens = pt;
   *max_parts = (int)parts;
   return true;
+}
+
+// ---- library-owned decode workspace for callers that cannot allocate ---------------------
+// `scratch` (file scope, above) serves as the decode workspace of pa_decode_append_noalloc.
+// In host code its name is only a stand-in: the device address, different on every GPU, comes
+// from hipGetSymbolAddress with that GPU current, once per device, and only that address is used.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch; on the first call on that GPU, also enqueues a
+// clear of its counter zone on `stream` (before the caller's kernels, on the same stream).
+int scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (es != hipSuccess) return hip_status(es);
+    if (ptr == nullptr || !aligned(ptr, 256)) return PA_ERR_HIP;
+    const int rc = hip_status(pa::launch_zero_fill(ptr, pa::ws_counter_zone(kScratchBytes), stream));
+    if (rc != PA_OK) return rc;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
 }
 
 }  // namespace
@@ -298,6 +334,38 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
                      &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
                      partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
+}
+
+int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             const int64_t* slot_mapping, const int32_t* block_tables,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, int32_t partition_tokens, float scale,
+                             int32_t kv_dtype, void* stream) {
+  // the size check comes first, so an oversized call is rejected before anything touches the
+  // device; pa_decode_workspace_bytes returns 0 for invalid arguments, which decode_impl then
+  // reports itself
+  const long long max_ctx = max_context_len > 0 ? (long long)max_context_len
+                                                : (long long)max_blocks_per_seq * block_size;
+  size_t need = 0;
+  if (max_ctx > 0 && max_ctx <= (1LL << 30))
+    need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     (int32_t)max_ctx, kv_dtype, partition_tokens);
+  if (need > kScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (need > 0) {
+    const int rc = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+    if (rc != PA_OK) return rc;
+    ws_bytes = kScratchBytes;
+  }
+  const AppendArgs app{k_new, v_new, slot_mapping, k_scale, v_scale};
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                     partition_tokens, scale, kv_dtype, ws, ws_bytes, stream);
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -334,3 +334,14 @@ def test_workspace_reset_validation():
     # a counter zone to clear needs a 256-byte aligned buffer
     assert pa.lib.pa_decode_workspace_reset(None, 1 << 20, None) == pa.PA_ERR_INVALID_ARG
     assert pa.lib.pa_decode_workspace_reset(FAKE + 16, 1 << 20, None) == pa.PA_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_calls_beyond_its_array_before_touching_the_device():
+    # 512 sequences x 32 query heads x 16 partitions of 256 tokens need ~140 MiB of partials,
+    # more than the library's own 16 MiB array: rejected before any device call
+    need = pa.decode_workspace_bytes(512, 32, 8, 128, 16, 4096, pa.PA_KV_F16, 256)
+    assert need > pa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    st = pa.lib.pa_decode_append_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                                         FAKE, FAKE, 512, 32, 8, 128, 16, 40000, 256, 4096, 256,
+                                         0.088, pa.PA_KV_F16, None)
+    assert st == pa.PA_ERR_WORKSPACE
