@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--flushed-calls", type=int, default=50,
                     help="pa_decode calls timed one by one after evicting the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quality", action=argparse.BooleanOptionalAction, default=True,
+                    help="report the E4M3-vs-fp16 error of the head-layout variants (a sample)")
     ap.add_argument("--probe-gib", type=float, default=4.0,
                     help="size of the streaming-read probe that measures attainable bandwidth (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -136,35 +138,123 @@ def make_step_inputs(case):
     return (np.zeros((0, 2), np.int32), np.stack(ks), np.stack(vs), np.asarray(slots, np.int64))
 
 
-def cpu_baseline(case, budget_s: float):
-    """Time the float64 oracle, sequence by sequence, until the budget is spent."""
+def _oracle_worker(args):
+    """One process of the CPU baseline: decode its share of the sequences with the oracle, again
+    and again, until its time budget is spent (BLAS limited to one thread in the process)."""
+    case, seqs, budget_s = args
     import oracle
 
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limiter = None
-    done, bytes_done, tok_done = 0, 0, 0
-    bs = case.block_size
+        pass
     per_tok = 2 * case.num_kv_heads * case.head_dim * case.kv_bytes_per_value
+    done, tok_done, bytes_done = 0, 0, 0
     t0 = time.perf_counter()
-    for b in range(case.num_seqs):
-        oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
-                      case.scale, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
-                      v_scale=case.v_scale, seqs=[b])
-        done += 1
-        tok_done += int(case.context_lens[b])
-        bytes_done += int(case.context_lens[b]) * per_tok
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": bytes_done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {case.num_seqs} sequences of the same workload ({tok_done} "
-                      f"seq-tokens, {dt:.1f} s, float64 numpy, BLAS limited to 1 thread)",
-            "seq_tokens_per_s": tok_done / dt}
+    while True:
+        for b in seqs:
+            oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                          case.scale, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                          v_scale=case.v_scale, seqs=[b])
+            done += 1
+            tok_done += int(case.context_lens[b])
+            bytes_done += int(case.context_lens[b]) * per_tok
+            if time.perf_counter() - t0 > budget_s:
+                return done, tok_done, bytes_done, time.perf_counter() - t0
+
+
+_POOL_CASE = None  # the workload, inherited by the forked oracle processes
+
+
+def _pool_worker(args):
+    seqs, budget_s = args
+    return _oracle_worker((_POOL_CASE, seqs, budget_s))
+
+
+def cpu_baseline(case, budget_s: float, max_workers: int = 16):
+    """The float64 oracle on the host's cores: one process per core (at most ``max_workers``,
+    the CPU share of one GPU on the measurement boxes), each with BLAS at one thread, deals the
+    sequences round-robin and decodes its share until the budget is spent; then the same on one
+    core for comparison. Must run before the GPU is initialised (the processes are forked)."""
+    global _POOL_CASE
+    import multiprocessing as mp
+
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, max_workers, case.num_seqs))
+    share = [list(range(w, case.num_seqs, workers)) for w in range(workers)]
+    _POOL_CASE = case
+    multi_s = budget_s * 2 / 3
+    with mp.get_context("fork").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_pool_worker, [(sh, multi_s) for sh in share])
+        wall = time.perf_counter() - t0
+    _POOL_CASE = None
+    done = sum(r[0] for r in res)
+    tok = sum(r[1] for r in res)
+    byt = sum(r[2] for r in res)
+    one = _oracle_worker((case, list(range(case.num_seqs)), budget_s / 3))
+    return {"value": byt / wall / 1e9, "unit": "GB/s", "cores": workers, "threads": workers,
+            "affinity_cores": affinity, "kind": "oracle",
+            "sample": f"{done} sequence decodes of the same workload ({tok} seq-tokens) in "
+                      f"{wall:.1f} s by {workers} processes with BLAS at 1 thread each "
+                      f"(sequences dealt round-robin, repeated until each process's "
+                      f"{multi_s:.0f} s budget ran out), float64 numpy",
+            "seq_tokens_per_s": tok / wall,
+            "one_core": {"value": one[2] / one[3] / 1e9, "unit": "GB/s", "cores": 1,
+                         "seq_tokens_per_s": one[1] / one[3],
+                         "sample": f"{one[0]} sequence decodes in {one[3]:.1f} s on one process"}}
+
+
+def e4m3_quality(num_seqs: int = 4):
+    """Quality of the 8-bit KV cache, reported and not gated ("serving-paged-attention", section
+    "실무에서 만지는 지점": the effect of 8-bit KV on quality has to be measured on its own).
+    For each head layout of the head-layout variants (64 x 2048 tokens, Hq 32, Hkv 32 / 8 / 1;
+    here num_seqs sequences drawn by the same recipe), the E4M3 pool quantizes the same fp16
+    draw; the oracle decodes both, and pa_decode decodes the E4M3 pool on the GPU. Errors are
+    against the oracle's fp16-KV output: max |err|, and max |err| / max(|ref|, 2e-3)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import paged_kv_cache_287_amd as pa
+    import workloads
+
+    def dev(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.float16:
+            return torch.from_numpy(x.view(np.uint16)).cuda().view(torch.float16)
+        return torch.from_numpy(x).cuda()
+
+    def errs(got, ref):
+        e = np.abs(got - ref)
+        return {"max_abs_err": float(e.max()),
+                "max_rel_err": float((e / np.maximum(np.abs(ref), 2e-3)).max()),
+                "max_err_over_max_ref": float(e.max() / np.abs(ref).max()),
+                "rms_err": float(np.sqrt(np.mean(e ** 2)))}
+
+    report = {}
+    for hkv in (32, 8, 1):
+        f16 = workloads.variant(hkv, "f16", num_seqs=num_seqs)
+        e4 = workloads.variant(hkv, "fp8_e4m3", num_seqs=num_seqs)
+        ref = oracle.decode(f16.q, f16.k_cache, f16.v_cache, f16.block_tables, f16.context_lens,
+                            f16.scale)
+        o8 = oracle.decode(e4.q, e4.k_cache, e4.v_cache, e4.block_tables, e4.context_lens,
+                           e4.scale, kv_dtype="fp8_e4m3", k_scale=e4.k_scale, v_scale=e4.v_scale)
+        out = torch.empty(e4.q.shape, dtype=torch.float16, device="cuda")
+        pa.pa_decode(out, dev(e4.q), dev(e4.k_cache), dev(e4.v_cache), dev(e4.block_tables),
+                     dev(e4.context_lens), float(e4.scale), k_scale=dev(e4.k_scale),
+                     v_scale=dev(e4.v_scale))
+        gpu = out.float().cpu().numpy().astype(np.float64)
+        name = {32: "mha", 8: "gqa4", 1: "mqa"}[hkv]
+        report[name] = {"oracle_e4m3_vs_oracle_f16": errs(o8, ref),
+                        "gpu_e4m3_vs_oracle_f16": errs(gpu, ref)}
+    report["sample"] = (f"{num_seqs} sequences x 2048 tokens per head layout (Hq 32, D 128, BS 16),"
+                        f" seeded as the head-layout variants; E4M3 with one fp32 scale per"
+                        f" (block, KV head)")
+    return report
 
 
 def prefill_flops(pc) -> int:
@@ -322,11 +412,16 @@ def main():
     import paged_kv_cache_287_amd as pa
     import workloads
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
     progress(f"generating workload {args.workload}")
     case = workloads.by_name(args.workload)
     pairs, nk, nv, slots = make_step_inputs(case)
+    # the CPU baseline forks its oracle processes, so it runs before anything touches the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
 
     def dev(x):
         if x is None:
@@ -561,10 +656,10 @@ def main():
                 "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3,
                 "timing": "HIP events around the timed back-to-back calls of the entry point "
                           "named in kernel"}
-    cpu = None
-    if not args.no_cpu_baseline:
-        progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(case, args.cpu_seconds)
+    quality = None
+    if args.quality:
+        progress("E4M3 quality report (oracle on the host, pa_decode on the GPU)")
+        quality = e4m3_quality()
     line = {
         "metric": "paged decode attention: KV GB/s (% of HBM peak) + seq-tokens/s, 8B-shaped, 1 GPU",
         "value": value,
@@ -601,6 +696,7 @@ def main():
         "swap": swap,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "e4m3_quality": quality,
     }
     print(json.dumps(line), flush=True)
 

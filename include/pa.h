@@ -134,8 +134,10 @@ int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* str
  *     out[b, h, :] = softmax(scale * K_b q[b, h]) V_b           (fp32 accumulate, fp16 out)
  * evaluated with an online softmax (running max, running sum, running output) over tiles and
  * split across context partitions of partition_tokens tokens that are merged exactly (talk
- * summary, FlashAttention paragraph); the workgroup that finishes a sequence's last partition
- * does the merge, so one kernel launch covers the whole call. L = 0 gives out = 0. For E4M3 caches each value is
+ * summary, FlashAttention paragraph). A sequence that fits one partition is finished by its
+ * workgroup; split sequences are merged by a second small kernel on `stream` (groups of at most
+ * four query heads per KV head, the vector-ALU kernel) or by the workgroup that finishes a
+ * sequence's last partition (larger groups, the matrix-core kernel). L = 0 gives out = 0. For E4M3 caches each value is
  * decode(code) * scale[block, g] before use. context_lens counts every token to attend,
  * including one appended by this step's pa_kv_write.
  *

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "prefill_mfma.hip", "cache_ops.hip", "probe.hip"]
+SOURCES = ["pa_api.hip", "decode.hip", "decode_mfma.hip", "merge.hip", "prefill_mfma.hip", "cache_ops.hip",
+           "probe.hip"]
 
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

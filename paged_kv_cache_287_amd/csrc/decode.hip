@@ -223,6 +223,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     my_id = p.block_tables[(size_t)b * p.max_blocks_per_seq + lb];
     my_id = min(max(my_id, 0), p.num_blocks - 1);  // a bad id reads a wrong block, never outside the pool
   }
+  // E4M3: lane j also holds block j's K and V scales, loaded once with the ids (a scale load
+  // inside the tile loop would put one more memory round trip into every tile)
+  float my_ks = 1.f, my_vs = 1.f;
+  if constexpr (KV8) {
+    if (wbase < L) {
+      my_ks = p.k_scale[(size_t)my_id * p.num_kv_heads + kvh];
+      my_vs = p.v_scale[(size_t)my_id * p.num_kv_heads + kvh];
+    }
+  }
 
   const uint8_t* kbase = p.k_cache + (size_t)kvh * TILE_BYTES;
   const uint8_t* vbase = p.v_cache + (size_t)kvh * TILE_BYTES;
@@ -262,9 +271,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
       vmul[s] = 1.f;
       if constexpr (KV8) {
         const int t = TT * i + RW * s;
-        const int id = __builtin_amdgcn_readlane(my_id, (woff + t) / BS);
-        kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
-        vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+        const int j = (woff + t) / BS;
+        kmul[s] *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), j));
+        vmul[s] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), j));
       }
       uint32_t kh[NH2];
       Chunk<NWORDS> kcs = kc[s];
@@ -425,7 +434,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   __syncthreads();
 
   // combine the 16 row states of this workgroup for element d of query head h
-  auto local_merge = [&](int h, int d, float& mx, float& ls, float& a) {
+  auto local_merge = [&](int h, int d, float& mx, float& ls, float (&av)[1]) {
+    float& a = av[0];
     mx = kNegInf;
 #pragma unroll
     for (int k = 0; k < kWaves * kDppRows; ++k) mx = fmaxf(mx, s_ml[k][h][0]);
@@ -440,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     }
   };
 
-  finish_partition<GT, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, GT, local_merge);
+  finish_partition<GT, D, kThreads, 1>(p, b, hg, part, nparts, sr.extra, h0, GT, local_merge);
 }
 
 template <int D, int BS, int GT, bool KV8, bool APPEND>

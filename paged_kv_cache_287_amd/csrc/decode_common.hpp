@@ -101,44 +101,87 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
   return r;
 }
 
-// End of one (sequence, head group, partition) workgroup. merge(h, d, mx, ls, a) returns the
-// workgroup's combined running max, running sum and weighted value sum for element d of its
-// query row h (the first `rows` of R rows, head dim D). With one partition and no earlier
-// partial the normalised output is written directly; otherwise the partial is published (after
-// the `extra` slots an earlier pass filled) and the workgroup that arrives last merges all slots
-// exactly and resets the arrival counter to zero.
-template <int R, int D, int NTHREADS, typename Merge>
+// Write-through 16-byte store of a partial (system scope: it leaves the writer's L2 for memory,
+// where a workgroup on another XCD reads it with cache-bypassing loads). A vector store.
+__device__ __forceinline__ void publish4(float* p, const float (&v)[4]) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const f4v x = f4v{v[0], v[1], v[2], v[3]};
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" : : "v"(p), "v"(x) : "memory");
+}
+// Two adjacent floats of a partial with one cache-bypassing 8-byte load.
+__device__ __forceinline__ void fetch2(const float* p, float& x, float& y) {
+  const unsigned long long w = __hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_SYSTEM);
+  x = __builtin_bit_cast(float, (uint32_t)w);
+  y = __builtin_bit_cast(float, (uint32_t)(w >> 32));
+}
+
+// End of one (sequence, head group, partition) workgroup. merge(h, d0, mx, ls, a) returns the
+// workgroup's combined running max, running sum and weighted value sums for elements
+// d0 .. d0 + UE - 1 of its query row h (the first `rows` of R rows, head dim D). A thread takes
+// UE consecutive elements at a time and neighbouring threads take neighbouring elements, so
+// every store and load below is contiguous across a wave (UE = 4: 16 bytes per lane). With one
+// partition and no earlier partial the normalised output is written directly; otherwise the
+// partial is published (after the `extra` slots an earlier pass filled) and the workgroup that
+// arrives last merges all slots exactly and resets the arrival counter to zero (or, with
+// deferred_merge, a kernel of its own merges them).
+template <int R, int D, int NTHREADS, int UE, typename Merge>
 __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, int hg, int part,
                                                  int nparts, int extra, int h0, int rows,
                                                  Merge&& merge) {
+  static_assert(UE == 1 || UE == 4, "one element or 16 bytes of partial per item");
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+  constexpr int IPR = D / UE;  // items per row
   const int tid = threadIdx.x;
+  const int items = rows * IPR;
+  // normalised output of one item: one 2-byte or one 8-byte store
+  auto write_out = [&](int h, int d0, const float (&a)[UE], float ls) {
+    _Float16* o = p.out + ((size_t)b * p.num_q_heads + h0 + h) * D + d0;
+    if constexpr (UE == 4) {
+      h4v v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (_Float16)(ls > 0.f ? a[u] / ls : 0.f);
+      *reinterpret_cast<h4v*>(o) = v;
+    } else {
+      o[0] = (_Float16)(ls > 0.f ? a[0] / ls : 0.f);
+    }
+  };
   if (nparts == 1 && extra == 0) {
     // the whole sequence fits one partition: normalise and write the output directly
-    for (int idx = tid; idx < rows * D; idx += NTHREADS) {
-      const int h = idx / D, d = idx - h * D;
-      float mx, ls, a;
-      merge(h, d, mx, ls, a);
-      p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(ls > 0.f ? a / ls : 0.f);
+    for (int it = tid; it < items; it += NTHREADS) {
+      const int h = it / IPR, d0 = (it - h * IPR) * UE;
+      float mx, ls, a[UE];
+      merge(h, d0, mx, ls, a);
+      write_out(h, d0, a, ls);
     }
     return;
   }
   if (nparts == 1) {
     // this launch's only partition of the sequence plus the `extra` partials an earlier launch
     // (the shared-prefix pass) stored: merge them here and write the output, with no publish of
-    // this partition and no arrival count
-    for (int idx = tid; idx < rows * D; idx += NTHREADS) {
-      const int h = idx / D, d = idx - h * D;
-      float mx, ls, a;
-      merge(h, d, mx, ls, a);
+    // this partition and no arrival count (the earlier kernel's stores are visible to plain
+    // loads in this one)
+    for (int it = tid; it < items; it += NTHREADS) {
+      const int h = it / IPR, d0 = (it - h * IPR) * UE;
+      float mx, ls, a[UE];
+      merge(h, d0, mx, ls, a);
       const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
-      float mv[kMaxPrefixSlices], lv[kMaxPrefixSlices], av[kMaxPrefixSlices];
+      float mv[kMaxPrefixSlices], lv[kMaxPrefixSlices], av[kMaxPrefixSlices][UE];
 #pragma unroll
       for (int j = 0; j < kMaxPrefixSlices; ++j) {
         const bool in = j < extra;
         const size_t slot = row0 + (in ? j : 0);
-        mv[j] = in ? fetch(p.ws_ml + slot * 2) : kNegInf;
-        lv[j] = in ? fetch(p.ws_ml + slot * 2 + 1) : 0.f;
-        av[j] = in ? fetch(p.ws_acc + slot * D + d) : 0.f;
+        mv[j] = in ? p.ws_ml[slot * 2] : kNegInf;
+        lv[j] = in ? p.ws_ml[slot * 2 + 1] : 0.f;
+        if constexpr (UE == 4) {
+          const f4v x = *reinterpret_cast<const f4v*>(p.ws_acc + slot * D + d0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) av[j][u] = in ? x[u] : 0.f;  // unused slots: anything
+        } else {
+          av[j][0] = in ? p.ws_acc[slot * D + d0] : 0.f;
+        }
       }
       float mc = mx;
 #pragma unroll
@@ -146,30 +189,46 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
       const float ms = mc == kNegInf ? 0.f : mc;
       const float w0 = fexp2(mx - ms);
       ls *= w0;
-      a *= w0;
+#pragma unroll
+      for (int u = 0; u < UE; ++u) a[u] *= w0;
 #pragma unroll
       for (int j = 0; j < kMaxPrefixSlices; ++j) {
         const float w = fexp2(mv[j] - ms);
         ls = fmaf(w, lv[j], ls);
-        a = fmaf(w, av[j], a);
+#pragma unroll
+        for (int u = 0; u < UE; ++u) a[u] = fmaf(w, av[j][u], a[u]);
       }
-      p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(ls > 0.f ? a / ls : 0.f);
+      write_out(h, d0, a, ls);
     }
     return;
   }
 
   // ---- several partitions: publish this one's (max, sum, value sum) ----------------------
-  for (int idx = tid; idx < rows * D; idx += NTHREADS) {
-    const int h = idx / D, d = idx - h * D;
-    float mx, ls, a;
-    merge(h, d, mx, ls, a);
+  for (int it = tid; it < items; it += NTHREADS) {
+    const int h = it / IPR, d0 = (it - h * IPR) * UE;
+    float mx, ls, a[UE];
+    merge(h, d0, mx, ls, a);
     const size_t slot = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots + extra + part;
-    publish(p.ws_acc + slot * D + d, a);
-    if (d == 0) {
-      publish(p.ws_ml + slot * 2, mx);
-      publish(p.ws_ml + slot * 2 + 1, ls);
+    float* dst = p.ws_acc + slot * D + d0;
+    if (p.deferred_merge) {
+      // the merge kernel that follows on the stream reads them: plain stores, no counter
+      if constexpr (UE == 4) *reinterpret_cast<f4v*>(dst) = f4v{a[0], a[1], a[2], a[3]};
+      else dst[0] = a[0];
+    } else {
+      if constexpr (UE == 4) publish4(dst, a);
+      else publish(dst, a[0]);
+    }
+    if (d0 == 0) {
+      if (p.deferred_merge) {
+        p.ws_ml[slot * 2] = mx;
+        p.ws_ml[slot * 2 + 1] = ls;
+      } else {
+        publish(p.ws_ml + slot * 2, mx);
+        publish(p.ws_ml + slot * 2 + 1, ls);
+      }
     }
   }
+  if (p.deferred_merge) return;
   // Count arrivals once the partial is stored. The workgroup that arrives last merges every
   // partition of this (sequence, head group) and resets the counter to zero, so no second
   // kernel is needed and the counters are zero again for the next call. The partials go
@@ -190,93 +249,72 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
   if (!s_last) return;
 
   // exact merge: out = sum_p 2^(m_p - M) a_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
-  // Partitions are taken kChunk at a time with all their loads in flight together (each round
-  // trip is a full memory latency: the loads bypass the caches) and merged into a running
-  // (max, sum, value) exactly as the tiles were.
-  constexpr int kChunk = 8;
+  // A thread takes IPT items of 4 consecutive dims (neighbouring threads, neighbouring dims).
+  // The partitions are taken KC at a time with the loads of all IPT items in flight together
+  // (each round trip is a full memory latency: the loads bypass the caches), and merged into a
+  // running (max, sum, value) exactly as the tiles were.
+  constexpr int IT_ROW = D / 4;
+  constexpr int IPT = (R * IT_ROW + NTHREADS - 1) / NTHREADS;
+  constexpr int KC = IPT >= 4 ? 4 : 8;
   const int nslots = nparts + extra;
-  if constexpr (R >= 16) {
-    // many rows: a thread takes UE dims of one row (d0, d0 + TPR, ...), so the (max, sum)
-    // loads and the merge weights are shared by its UE elements, neighbouring lanes still read
-    // neighbouring dims, and each pass over R / RPP rows is one round trip
-    constexpr int UE = (R * D) / NTHREADS < 8 ? (R * D) / NTHREADS : 8;
-    constexpr int TPR = D / UE;            // threads per row
-    constexpr int RPP = NTHREADS / TPR;    // rows per pass
-    static_assert(D % UE == 0 && NTHREADS % TPR == 0 && R % RPP == 0, "merge tiling");
-    for (int h = tid / TPR; h < rows; h += RPP) {
-      const int d0 = tid % TPR;
-      const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
-      const float* ml = p.ws_ml + row0 * 2;
-      const float* ac = p.ws_acc + row0 * D + d0;
-      float mx = kNegInf, ls = 0.f, a[UE];
+  int hs[IPT], ds[IPT];
+  bool act[IPT];
 #pragma unroll
-      for (int u = 0; u < UE; ++u) a[u] = 0.f;
-      for (int i0 = 0; i0 < nslots; i0 += kChunk) {
-        float mv[kChunk], lv[kChunk], av[kChunk][UE];
+  for (int k = 0; k < IPT; ++k) {
+    const int it = tid + k * NTHREADS;
+    act[k] = it < rows * IT_ROW;
+    hs[k] = act[k] ? it / IT_ROW : 0;
+    ds[k] = act[k] ? (it - hs[k] * IT_ROW) * 4 : 0;
+  }
+  float mx[IPT], ls[IPT], a[IPT][4];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const bool in = i0 + j < nslots;
-          const int i = in ? i0 + j : i0;
-          mv[j] = fetch(ml + 2 * i);
-          lv[j] = fetch(ml + 2 * i + 1);
+  for (int k = 0; k < IPT; ++k) {
+    mx[k] = kNegInf;
+    ls[k] = 0.f;
 #pragma unroll
-          for (int u = 0; u < UE; ++u) av[j][u] = fetch(ac + (size_t)i * D + u * TPR);
-          if (!in) mv[j] = kNegInf;
-        }
-        float mc = mx;
+    for (int u = 0; u < 4; ++u) a[k][u] = 0.f;
+  }
+  for (int i0 = 0; i0 < nslots; i0 += KC) {
+    float mv[IPT][KC], lv[IPT][KC], av[IPT][KC][4];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
-        const float r = fexp2(mx - mc);  // mx = -inf only before the first chunk: r = 0
-        ls *= r;
+    for (int k = 0; k < IPT; ++k) {
+      const size_t row0 = ((size_t)b * p.num_q_heads + h0 + hs[k]) * p.part_slots;
 #pragma unroll
-        for (int u = 0; u < UE; ++u) a[u] *= r;
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const float w = fexp2(mv[j] - mc);
-          ls = fmaf(w, lv[j], ls);
-#pragma unroll
-          for (int u = 0; u < UE; ++u) a[u] = fmaf(w, av[j][u], a[u]);
-        }
-        mx = mc;
+      for (int j = 0; j < KC; ++j) {
+        const bool in = i0 + j < nslots;
+        const size_t slot = row0 + (in ? i0 + j : i0);
+        fetch2(p.ws_ml + slot * 2, mv[k][j], lv[k][j]);
+        fetch2(p.ws_acc + slot * D + ds[k], av[k][j][0], av[k][j][1]);
+        fetch2(p.ws_acc + slot * D + ds[k] + 2, av[k][j][2], av[k][j][3]);
+        if (!in) mv[k][j] = kNegInf;
       }
-      _Float16* o = p.out + ((size_t)b * p.num_q_heads + h0 + h) * D + d0;
-#pragma unroll
-      for (int u = 0; u < UE; ++u) o[u * TPR] = (_Float16)(a[u] / ls);
     }
-  } else {
-    for (int idx = tid; idx < rows * D; idx += NTHREADS) {
-      const int h = idx / D, d = idx - h * D;
-      const size_t row0 = ((size_t)b * p.num_q_heads + h0 + h) * p.part_slots;
-      const float* ml = p.ws_ml + row0 * 2;
-      const float* ac = p.ws_acc + row0 * D + d;
-      float mx = kNegInf, ls = 0.f, a = 0.f;
-      for (int i0 = 0; i0 < nslots; i0 += kChunk) {
-        float mv[kChunk], lv[kChunk], av[kChunk];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const bool in = i0 + j < nslots;
-          const int i = in ? i0 + j : i0;
-          mv[j] = fetch(ml + 2 * i);
-          lv[j] = fetch(ml + 2 * i + 1);
-          av[j] = fetch(ac + (size_t)i * D);
-          if (!in) mv[j] = kNegInf;
-        }
-        float mc = mx;
+    for (int k = 0; k < IPT; ++k) {
+      float mc = mx[k];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, mv[j]);
-        const float r = fexp2(mx - mc);
-        ls *= r;
-        a *= r;
+      for (int j = 0; j < KC; ++j) mc = fmaxf(mc, mv[k][j]);
+      const float r = fexp2(mx[k] - mc);  // mx = -inf only before the first chunk: r = 0
+      ls[k] *= r;
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          const float w = fexp2(mv[j] - mc);
-          ls = fmaf(w, lv[j], ls);
-          a = fmaf(w, av[j], a);
-        }
-        mx = mc;
+      for (int u = 0; u < 4; ++u) a[k][u] *= r;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float w = fexp2(mv[k][j] - mc);
+        ls[k] = fmaf(w, lv[k][j], ls[k]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[k][u] = fmaf(w, av[k][j][u], a[k][u]);
       }
-      p.out[((size_t)b * p.num_q_heads + h0 + h) * D + d] = (_Float16)(a / ls);
+      mx[k] = mc;
     }
+  }
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    if (!act[k]) continue;
+    h4v v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (_Float16)(a[k][u] / ls[k]);
+    *reinterpret_cast<h4v*>(p.out + ((size_t)b * p.num_q_heads + h0 + hs[k]) * D + ds[k]) = v;
   }
 }
 

@@ -75,7 +75,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   const int lr = lane & 15;  // K/V token row of a load; query row of a score
   const int lq = lane >> 4;  // 8-element group of a 32-dim step; 4-token group of a tile
 
-  // ---- query rows as the B operand: row h0 + 16 nt + lr, dims 32 kk + 8 lq .. +8 ------------
+  // ---- which 8 head dims lane (lr, lq) contributes to 32-dim step kk of QK ------------------
+  // The contraction order is free, so it follows the loads: an fp16 lane loads 16 bytes (8 dims)
+  // per step, dims 32 kk + 8 lq; an E4M3 lane loads 16 bytes (16 dims) for two steps at once,
+  // dims 64 (kk / 2) + 16 lq + 8 (kk % 2), so that every K load instruction still covers 64
+  // contiguous bytes of each of its 16 rows (8-byte loads would cover 32: as many memory
+  // requests as for fp16, for half the bytes). q is gathered in the same order.
+  constexpr int KL = KV8 ? KK / 2 : KK;  // 16-byte K loads per lane per tile
+  auto kdim = [&](int kk) -> int {
+    return KV8 ? 64 * (kk >> 1) + 16 * lq + 8 * (kk & 1) : 32 * kk + 8 * lq;
+  };
+
+  // ---- query rows as the B operand: row h0 + 16 nt + lr, dims kdim(kk) .. +8 ----------------
   h8 qb[NT][KK];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -83,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     for (int kk = 0; kk < KK; ++kk)
       qb[nt][kk] = 16 * nt + lr < rows
                        ? *reinterpret_cast<const h8*>(p.q + ((size_t)b * p.num_q_heads + h0 +
-                                                             16 * nt + lr) * D + 32 * kk + 8 * lq)
+                                                             16 * nt + lr) * D + kdim(kk))
                        : h8{0, 0, 0, 0, 0, 0, 0, 0};
 
   // ---- fused append: threads 0 .. 2 NEWC - 1 load the new K row's, then the new V row's
@@ -119,6 +130,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     my_id = p.block_tables[(size_t)b * p.max_blocks_per_seq + lb];
     my_id = min(max(my_id, 0), p.num_blocks - 1);
   }
+  // E4M3: lane j also holds block j's K and V scales, loaded once with the ids (a scale load
+  // inside the tile loop would put one more memory round trip into every tile)
+  float my_ks = 1.f, my_vs = 1.f;
+  if constexpr (KV8) {
+    if (wbase < L) {
+      my_ks = p.k_scale[(size_t)my_id * p.num_kv_heads + kvh];
+      my_vs = p.v_scale[(size_t)my_id * p.num_kv_heads + kvh];
+    }
+  }
   // block of token (16 i + t) of tile i: uniform for BS >= 16; for BS = 8 the tile's second
   // half lies in the next block
   auto block_of = [&](int i, int t) -> int {
@@ -129,6 +149,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       const int a = __builtin_amdgcn_readlane(my_id, j0);
       const int c = __builtin_amdgcn_readlane(my_id, j0 + 1);
       return t >= BS ? c : a;
+    }
+  };
+  // the same lookup for a per-lane float (the block scales)
+  auto lane_value_of = [&](float v, int i, int t) -> float {
+    const int j0 = (woff + kTileTokens * i) / BS;
+    const int vi = __builtin_bit_cast(int, v);
+    if constexpr (BS >= kTileTokens) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, j0));
+    } else {
+      const int a = __builtin_amdgcn_readlane(vi, j0);
+      const int c = __builtin_amdgcn_readlane(vi, j0 + 1);
+      return __builtin_bit_cast(float, t >= BS ? c : a);
     }
   };
 
@@ -146,8 +178,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // LDS: a per-wave transposed V tile ([dim][token]), reused after the loop for the merge
-  constexpr int kMergeFloats = kWaves * R * (D + 2);
+  // LDS: a per-wave transposed V tile ([dim][token]), reused after the loop for the merge. The
+  // merge area holds each wave's R x D partial with a row stride of D + 4 floats, so that the
+  // 16 rows a wave writes with one instruction fall on different banks
+  constexpr int DP = D + 4;
+  constexpr int kMergeFloats = kWaves * R * (DP + 2);
   static_assert(kWaves * D * VTS * 2 <= kMergeFloats * 4, "staging fits the merge area");
   __shared__ __align__(16) float smem[kMergeFloats];
   _Float16* vt = reinterpret_cast<_Float16*>(smem) + wave * D * VTS;
@@ -156,14 +191,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   // lane, so that it is stored transposed with one TPL-half store per dim
   const int vch = lane / (16 / TPL);   // 8-dim chunk
   const int vtg = lane % (16 / TPL);   // token group: tokens TPL vtg .. +TPL-1
-  Chunk<NWORDS> ka[KK], va[TPL], kb[KK], vb[TPL];
+  Chunk<4> ka[KL], kb[KL];
+  Chunk<NWORDS> va[TPL], vb[TPL];
 
-  auto issue_tile = [&](int i, Chunk<NWORDS>(&kc)[KK], Chunk<NWORDS>(&vc)[TPL]) {
+  auto issue_tile = [&](int i, Chunk<4>(&kc)[KL], Chunk<NWORDS>(&vc)[TPL]) {
     const int id = block_of(i, lr);
-    const size_t off = (size_t)id * blk_stride +
-                       (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES + lq * LANE_BYTES);
+    const size_t off =
+        (size_t)id * blk_stride + (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES);
+    // load c holds the dims of steps c (fp16) or 2c and 2c + 1 (E4M3)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kc[kk] = load_chunk<NWORDS, true>(kbase + off + kk * 32 * ESZ);
+    for (int c = 0; c < KL; ++c)
+      kc[c] = load_chunk<4, true>(kbase + off + kdim(KV8 ? 2 * c : c) * ESZ);
     // a lane's TPL tokens start at a multiple of TPL, so they share one block
     const int vid = block_of(i, TPL * vtg);
     const size_t voff = (size_t)vid * blk_stride +
@@ -190,25 +228,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     return __builtin_bit_cast(h8, w);
   };
 
-  auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[KK], const Chunk<NWORDS>(&vc)[TPL],
+  auto consume_tile = [&](int i, const Chunk<4>(&kc)[KL], const Chunk<NWORDS>(&vc)[TPL],
                           bool masked) {
     const int tok0 = wbase + kTileTokens * i;
     // per-token multipliers: softmax scale (and the K / V block scales of an E4M3 cache) for
     // this lane's four score tokens 4 lq + ii
     float kmul = p.scale_log2, vmul = 1.f;
     if constexpr (KV8) {
-      const int id = block_of(i, 4 * lq);
-      kmul *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
-      vmul = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+      kmul *= lane_value_of(my_ks, i, 4 * lq);
+      vmul = lane_value_of(my_vs, i, 4 * lq);
     }
     h8 kA[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kA[kk] = to_h8(kc[kk]);
+    for (int kk = 0; kk < KK; ++kk) {
+      if constexpr (KV8) {
+        Chunk<NWORDS> half;  // the 8 codes of step kk
+        half.w[0] = kc[kk >> 1].w[2 * (kk & 1)];
+        half.w[1] = kc[kk >> 1].w[2 * (kk & 1) + 1];
+        kA[kk] = to_h8(half);
+      } else {
+        kA[kk] = to_h8(kc[kk]);
+      }
+    }
     if constexpr (APPEND) {
       if (masked && tok0 + lr == newtok) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          kA[kk] = *reinterpret_cast<const h8*>(s_new + (32 * kk + 8 * lq) * 2);
+          kA[kk] = *reinterpret_cast<const h8*>(s_new + kdim(kk) * 2);
       }
     }
     h4 pB[NT];
@@ -330,16 +376,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 
   // ---- merge the kWaves waves through LDS (the staging area is reused) ----------------------
   __syncthreads();
-  float* s_acc = smem;                              // [kWaves][R][D]
-  float* s_ml = smem + kWaves * R * D;              // [kWaves][R][2]
+  float* s_acc = smem;                              // [kWaves][R][DP]
+  float* s_ml = smem + kWaves * R * DP;             // [kWaves][R][2]
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = 16 * nt + lr;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        s_acc[(wave * R + row) * D + 16 * mt + 4 * lq + ii] = o[nt][mt][ii];
+      *reinterpret_cast<f4*>(s_acc + (wave * R + row) * DP + 16 * mt + 4 * lq) = o[nt][mt];
     if (lq == 0) {
       s_ml[(wave * R + row) * 2] = m[nt];
       s_ml[(wave * R + row) * 2 + 1] = l[nt];
@@ -369,14 +413,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   }
   __syncthreads();
 
-  auto local_merge = [&](int h, int d, float& mx, float& ls, float& a) {
+  // dims d0 .. d0 + 3 of row h: one 16-byte LDS read per wave
+  auto local_merge = [&](int h, int d0, float& mx, float& ls, float (&a)[4]) {
     mx = s_row[h][0];
     ls = s_row[h][1];
-    a = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) a = fmaf(s_wt[w][h], s_acc[(w * R + h) * D + d], a);
+    for (int u = 0; u < 4; ++u) a[u] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = s_wt[w][h];
+      const f4 x = *reinterpret_cast<const f4*>(s_acc + (w * R + h) * DP + d0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = fmaf(wt, x[u], a[u]);
+    }
   };
-  finish_partition<R, D, kThreads>(p, b, hg, part, nparts, sr.extra, h0, rows, local_merge);
+  finish_partition<R, D, kThreads, 4>(p, b, hg, part, nparts, sr.extra, h0, rows, local_merge);
 }
 
 template <int D, int BS, int NT, bool KV8, bool APPEND>

@@ -241,6 +241,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.group = group;
   p.head_groups = group / gt;
   p.scale_log2 = scale * 1.4426950408889634f;
+  // Split sequences of the vector-ALU kernel are merged by a kernel of its own (block-size sweep
+  // at 128 x [32, 8192] tokens: 145 against 150 us with the last-arriving workgroup merging);
+  // the matrix-core kernel's workgroups merge in-kernel (MQA at 64 x 2,048 tokens: 20.5 against
+  // 22.2 us with the separate merge).
+  p.deferred_merge = ws.total > 0 && max_parts > 1 && !pa::decode_uses_mfma(group);
   const hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (groups && prefix_blocks > 0) {
@@ -283,9 +288,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       p.slot_mapping = app->slot_mapping;
       p.k_cache_w = static_cast<uint8_t*>(const_cast<void*>(k_cache));
       p.v_cache_w = static_cast<uint8_t*>(const_cast<void*>(v_cache));
-      if (pa::decode_uses_mfma(group))
-        return hip_status(pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, st));
-      return hip_status(pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, st));
+      const hipError_t e =
+          pa::decode_uses_mfma(group)
+              ? pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, st)
+              : pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, st);
+      if (e != hipSuccess || !p.deferred_merge) return hip_status(e);
+      return hip_status(pa::launch_decode_merge(p, num_seqs, head_dim, block_size, st));
     }
     // the append kernel first (E4M3 caches: with the block-scale policy), then the decode
     const hipError_t e =
@@ -299,9 +307,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     const int rc = hip_status(e);
     if (rc != PA_OK) return rc;
   }
-  if (pa::decode_uses_mfma(group))
-    return hip_status(pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8, st));
-  return hip_status(pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8, st));
+  const hipError_t e = pa::decode_uses_mfma(group)
+                           ? pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8, st)
+                           : pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8, st);
+  if (e != hipSuccess || !p.deferred_merge) return hip_status(e);
+  return hip_status(pa::launch_decode_merge(p, num_seqs, head_dim, block_size, st));
 }
 
 }  // namespace

@@ -165,6 +165,9 @@ struct DecodeParams {
   int32_t group;        // G = Hq / Hkv
   int32_t head_groups;  // G / GT workgroups per KV head
   float scale_log2;     // softmax scale * log2(e)
+  // 1: partitions only store their partials (plain stores, no arrival counter) and a second
+  // kernel (launch_decode_merge) merges them; 0: the last workgroup to arrive merges in-kernel
+  int32_t deferred_merge;
   // Fused append (pa_decode_append, fp16 caches): the new token of sequence b sits at position
   // context_lens[b] - 1; its rows k_new/v_new[b] ([S, Hkv, D]) are attended in place of the
   // cache's and stored at slot_mapping[b] (< 0: no append). Null for plain decode.
@@ -234,6 +237,10 @@ hipError_t launch_decode_mfma_append(const DecodeParams& p, int num_seqs, int he
                                      int block_size, int rows, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                               int rows, bool kv_fp8, hipStream_t stream);
+// Merge of the partition partials of every sequence that spans more than one partition (after a
+// decode launch with deferred_merge = 1, on the same stream).
+hipError_t launch_decode_merge(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
+                               hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,
                           bool kv_fp8, hipStream_t stream);
 hipError_t launch_prefix_pass(const PrefillParams& p, int num_groups, int head_dim, int block_size,
