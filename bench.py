@@ -77,6 +77,10 @@ def parse():
                     help="fused: the step's append runs inside the decode call (pa_decode_append) "
                          "wherever the step is one token per sequence at its newest position; "
                          "separate: pa_kv_write, then the decode call")
+    ap.add_argument("--seq-order", choices=["longest", "natural"], default="longest",
+                    help="dispatch order passed to the decode call: longest contexts first (the "
+                         "host knows the lengths; no order is passed when it is the batch order) "
+                         "or the batch order")
     ap.add_argument("--decode", choices=["auto", "plain", "shared_prefix"], default="auto",
                     help="decode entry point: shared_prefix reads each group's shared blocks once "
                          "(auto: whenever the workload has prefix groups)")
@@ -454,6 +458,11 @@ def main():
         max_prefix = max(1, int(case.group_prefix_blocks.max()))
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # longest contexts first (stable, so equal lengths keep the batch order); an identity order
+    # is not passed at all
+    order = np.argsort(-np.asarray(case.context_lens), kind="stable").astype(np.int32)
+    use_order = args.seq_order == "longest" and not np.array_equal(order, np.arange(case.num_seqs))
+    g_order = dev(order) if use_order else None
     # pa_decode_append takes one new row per sequence, at its newest position L - 1
     newest = [int(case.block_tables[b, (int(L) - 1) // case.block_size]) * case.block_size
               + (int(L) - 1) % case.block_size if int(L) > 0 else -1
@@ -466,16 +475,17 @@ def main():
             pa.pa_decode_append(out, q, g_nk, g_nv, kc, vc, g_slots, tables, lens,
                                 float(case.scale), k_scale=ks, v_scale=vs,
                                 max_context_len=max_ctx, partition_tokens=part_tokens,
-                                workspace=ws)
+                                workspace=ws, seq_order=g_order)
         elif shared:
             pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, g_gs, g_gpb, float(case.scale),
                                        max_group_seqs=max_group,
                                        max_prefix_blocks=max_prefix, k_scale=ks, v_scale=vs,
                                        max_context_len=max_ctx, partition_tokens=part_tokens,
-                                       workspace=ws)
+                                       workspace=ws, seq_order=g_order)
         else:
             pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
-                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws)
+                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws,
+                         seq_order=g_order)
 
     def step():
         if g_pairs.shape[0]:
@@ -570,7 +580,8 @@ def main():
                 pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
             pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
             pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
-                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws)
+                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws,
+                         seq_order=g_order)
 
         # its own warm-up: the append kernel has not run in this process yet (its first
         # launch loads the code object)
@@ -686,6 +697,7 @@ def main():
                            "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
                    "partition_tokens": part_tokens,
                    "decode": "shared_prefix" if shared else "plain",
+                   "seq_order": "longest first" if use_order else "batch order",
                    "append": "fused" if fused else "separate"},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attainable_read_gbs": attainable,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
   PA_OK = 0,
@@ -141,6 +141,15 @@ int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* str
  * decode(code) * scale[block, g] before use. context_lens counts every token to attend,
  * including one appended by this step's pa_kv_write.
  *
+ *   seq_order        NULL, or [num_seqs] int32 device array, a permutation of 0 .. num_seqs-1:
+ *                    the order in which sequences are dispatched (grid row y decodes sequence
+ *                    seq_order[y]); out stays in batch order. With uneven lengths, putting the
+ *                    longest contexts first lets their partitions start first instead of forming
+ *                    the tail of the grid ("serving-paged-attention", section "블록 크기는 어떻게
+ *                    정하나": requests of very different lengths share one batch). Results are
+ *                    bit-identical for any order. An entry outside [0, num_seqs) is clamped; a
+ *                    non-permutation gives wrong outputs (and may leave counters that
+ *                    pa_decode_workspace_reset clears), never an access outside the buffers.
  *   max_context_len  host-side upper bound on context_lens[] used to size the grid;
  *                    <= 0 means max_blocks_per_seq * block_size.
  *   partition_tokens 0 = automatic, else an explicit split size (see
@@ -161,14 +170,16 @@ int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* str
  * but no access outside the buffers: block ids are clamped into [0, num_blocks), tokens beyond
  * the grid's partitions are dropped.
  * Validated: non-NULL pointers (k_scale/v_scale must be NULL for fp16 and non-NULL for E4M3),
- * 16-byte alignment of q, out, k_cache, v_cache; 4-byte alignment of the int arrays and scales;
+ * 16-byte alignment of q, out, k_cache, v_cache; 4-byte alignment of the int arrays (seq_order
+ * included) and scales;
  * positive sizes; Hq % Hkv == 0; supported head_dim, block_size and dtype; partition_tokens
  * (PA_ERR_UNSUPPORTED if it is not a valid explicit size); workspace size and alignment.
  * Deterministic: results depend only on logical token positions, not on physical ids.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
-              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              const int32_t* context_lens,
+              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
               int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_tokens,
               float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes,
@@ -207,7 +218,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
                      void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                      const int64_t* slot_mapping, const int32_t* block_tables,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     const int32_t* context_lens,
+              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                      int32_t partition_tokens, float scale, int32_t kv_dtype, void* workspace,
@@ -241,7 +253,8 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
 int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                              const int64_t* slot_mapping, const int32_t* block_tables,
-                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             const int32_t* context_lens,
+              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t max_blocks_per_seq,
                              int32_t max_context_len, int32_t partition_tokens, float scale,
@@ -297,6 +310,7 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const float* k_scale, const float* v_scale,
                             const int32_t* block_tables, const int32_t* context_lens,
+              const int32_t* seq_order,
                             const int32_t* group_start, const int32_t* group_prefix_blocks,
                             int32_t num_groups, int32_t max_group_seqs,
                             int32_t max_prefix_blocks, int32_t num_seqs,

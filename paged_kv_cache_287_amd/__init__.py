@@ -28,7 +28,7 @@ __all__ = [
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 PA_KV_F16, PA_KV_FP8_E4M3 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
@@ -41,15 +41,15 @@ EXPORTED_SYMBOLS = {
     "pa_last_hip_error": (ctypes.c_int, []),
     "pa_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
-                                 _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
-    "pa_decode_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
-                                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p,
-                                        _sz, _p]),
+    "pa_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "pa_decode_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                        _i32, _p, _sz, _p]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
+    "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                               _i32, _i32, _f32, _i32, _p, _sz, _p]),
+                                               _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -59,9 +59,9 @@ EXPORTED_SYMBOLS = {
                                       _i32, _i32, _i32, _p]),
     "pa_stream_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
     "pa_decode_workspace_reset": (ctypes.c_int, [_p, _sz, _p]),
-    "pa_decode_append_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
+    "pa_decode_append_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                                _f32, _i32, _p]),
+                                                _i32, _f32, _i32, _p]),
 }
 
 #: bytes of the library's own per-GPU decode workspace (pa_decode_append_noalloc)
@@ -116,6 +116,14 @@ def _check(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _check_order(seq_order: Optional[torch.Tensor], num_seqs: int) -> None:
+    if seq_order is None:
+        return
+    _check(seq_order, "seq_order", (torch.int32,), 1)
+    if seq_order.shape[0] != num_seqs:
+        raise ValueError("seq_order must have one entry per sequence")
+
+
 def _kv_dtype(cache: torch.Tensor) -> int:
     if cache.dtype == torch.float16:
         return PA_KV_F16
@@ -154,8 +162,12 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
               k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
               max_context_len: int = 0, partition_tokens: int = 0,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+              workspace: Optional[torch.Tensor] = None, seq_order: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
     """Enqueue paged decode attention; writes ``out`` [S, Hq, D] fp16 and returns it.
+
+    ``seq_order`` (optional int32 device tensor [S], a permutation) is the dispatch order of the
+    sequences, e.g. longest first; ``out`` stays in batch order.
 
     ``workspace`` (uint8 device tensor, zero-filled before its first use) is allocated here,
     zero-filled, when omitted and needed.
@@ -185,8 +197,9 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check_order(seq_order, num_seqs)
     st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-                       _ptr(block_tables), _ptr(context_lens), num_seqs, num_q_heads, num_kv_heads,
+                       _ptr(block_tables), _ptr(context_lens), _ptr(seq_order), num_seqs, num_q_heads, num_kv_heads,
                        head_dim, block_size, nb, mbps, max_context_len, partition_tokens,
                        float(scale), kvt,
                        _ptr(workspace), ws_bytes, _stream(stream))
@@ -200,7 +213,8 @@ def pa_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_
                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                      max_context_len: int = 0, partition_tokens: int = 0,
-                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                     workspace: Optional[torch.Tensor] = None,
+                     seq_order: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Enqueue one decode step: store each sequence's new K/V row ``k_new/v_new[b]`` at
     ``slot_mapping[b]`` and attend over the cache including it; writes ``out`` and returns it.
 
@@ -238,9 +252,11 @@ def pa_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check_order(seq_order, num_seqs)
     st = lib.pa_decode_append(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
-                              _ptr(block_tables), _ptr(context_lens), num_seqs, num_q_heads,
+                              _ptr(block_tables), _ptr(context_lens), _ptr(seq_order), num_seqs,
+                              num_q_heads,
                               num_kv_heads, head_dim, block_size, nb, mbps, max_context_len,
                               partition_tokens, float(scale), kvt, _ptr(workspace), ws_bytes,
                               _stream(stream))
@@ -255,7 +271,8 @@ def pa_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Te
                              context_lens: torch.Tensor, scale: float, *,
                              k_scale: Optional[torch.Tensor] = None,
                              v_scale: Optional[torch.Tensor] = None, max_context_len: int = 0,
-                             partition_tokens: int = 0, stream=None) -> torch.Tensor:
+                             partition_tokens: int = 0, seq_order: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
     """``pa_decode_append`` whose workspace is the library's own per-GPU device array: neither
     this binding nor the library allocates. Calls that overlap on one GPU race on that array."""
     _check(q, "q", (torch.float16,), 3)
@@ -282,10 +299,11 @@ def pa_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Te
     if (block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs
             or slot_mapping.shape[0] != num_seqs):
         raise ValueError("block_tables / context_lens / slot_mapping must have one row per sequence")
+    _check_order(seq_order, num_seqs)
     st = lib.pa_decode_append_noalloc(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                       _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                       _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens),
-                                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, nb,
+                                      _ptr(seq_order), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, nb,
                                       block_tables.shape[1], max_context_len, partition_tokens,
                                       float(scale), kvt, _stream(stream))
     if st != PA_OK:
@@ -309,7 +327,7 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
                             max_group_seqs: int, max_prefix_blocks: int, k_scale: Optional[torch.Tensor] = None,
                             v_scale: Optional[torch.Tensor] = None, max_context_len: int = 0,
                             partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
-                            stream=None) -> torch.Tensor:
+                            seq_order: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Enqueue decode attention whose shared prefix blocks are read once per group and KV head;
     writes ``out`` [S, Hq, D] fp16 and returns it.
 
@@ -346,9 +364,10 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     if workspace is None:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    _check_order(seq_order, num_seqs)
     st = lib.pa_decode_shared_prefix(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                      _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
-                                     _ptr(group_start), _ptr(group_prefix_blocks), num_groups,
+                                     _ptr(seq_order), _ptr(group_start), _ptr(group_prefix_blocks), num_groups,
                                      int(max_group_seqs), int(max_prefix_blocks), num_seqs, num_q_heads, num_kv_heads,
                                      head_dim, block_size, nb, mbps, max_context_len,
                                      partition_tokens, float(scale), kvt, _ptr(workspace),

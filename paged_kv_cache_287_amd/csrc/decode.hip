@@ -154,7 +154,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   // With 8 or more KV heads, head groups of one KV head are kvh, kvh + Hkv, ...: workgroup ids
   // are dealt round-robin over the 8 XCDs, so all of them read that KV head through one L2.
   const int hg = blockIdx.x;
-  const int b = blockIdx.y;
+  // grid row y decodes sequence seq_order[y] when the caller gives an order (clamped, so a bad
+  // entry reads a wrong sequence, never outside the arrays)
+  const int b = p.seq_order != nullptr ? min(max(p.seq_order[blockIdx.y], 0), (int)gridDim.y - 1)
+                                       : (int)blockIdx.y;
   // partitions are dispatched in order, partition 0 of every sequence first: that is the
   // full-size piece of every long context, while higher indices exist only for long contexts
   // and end with their partial last piece. Dispatching the last ones first left those full

@@ -53,7 +53,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   static_assert(BS % kRows == 0, "block size");
 
   const int hg = blockIdx.x;
-  const int b = blockIdx.y;
+  // grid row y decodes sequence seq_order[y] when the caller gives an order (clamped, so a bad
+  // entry reads a wrong sequence, never outside the arrays)
+  const int b = p.seq_order != nullptr ? min(max(p.seq_order[blockIdx.y], 0), (int)gridDim.y - 1)
+                                       : (int)blockIdx.y;
   // partitions are dispatched last first: only long contexts have high partition indices, so
   // their full workgroups start early instead of forming the tail of the grid
   const int part = p.max_parts - 1 - (int)blockIdx.z;

@@ -143,7 +143,8 @@ struct AppendArgs {
 // (app != nullptr).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                 const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                const int32_t* context_lens, const AppendArgs* app, const int32_t* group_start,
+                const int32_t* context_lens, const int32_t* seq_order, const AppendArgs* app,
+                const int32_t* group_start,
                 const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_seqs,
                 int32_t max_prefix_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -161,7 +162,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const bool fp8 = kv_dtype == PA_KV_FP8_E4M3;
   if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return PA_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4) || (fp8 && (!aligned(k_scale, 4) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(seq_order, 4) ||
+      (fp8 && (!aligned(k_scale, 4) ||
       !aligned(v_scale, 4))))
     return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535) return PA_ERR_INVALID_ARG;
@@ -221,6 +223,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.v_scale = v_scale;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.seq_order = seq_order;
   char* wsb = static_cast<char*>(workspace);
   const size_t zone = pa::ws_counter_zone(workspace_bytes_given);
   p.counters = ws.total ? reinterpret_cast<int32_t*>(wsb) : nullptr;
@@ -320,13 +323,14 @@ extern "C" {
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_tables,
-              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              const int32_t* context_lens,
+              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
               int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_tokens,
               float scale, int32_t kv_dtype, void* workspace, size_t workspace_bytes_given,
               void* stream) {
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     nullptr, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
+                     seq_order, nullptr, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
                      partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
 }
@@ -334,14 +338,15 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
                      void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                      const int64_t* slot_mapping, const int32_t* block_tables,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     const int32_t* context_lens,
+              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                      int32_t partition_tokens, float scale, int32_t kv_dtype, void* workspace,
                      size_t workspace_bytes_given, void* stream) {
   const AppendArgs app{k_new, v_new, slot_mapping, k_scale, v_scale};
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
+                     seq_order, &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
                      partition_tokens, scale, kv_dtype, workspace, workspace_bytes_given, stream);
 }
@@ -349,7 +354,8 @@ int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_
 int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                              const int64_t* slot_mapping, const int32_t* block_tables,
-                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             const int32_t* context_lens,
+              const int32_t* seq_order, int32_t num_seqs, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t max_blocks_per_seq,
                              int32_t max_context_len, int32_t partition_tokens, float scale,
@@ -373,7 +379,7 @@ int pa_decode_append_noalloc(void* out, const void* q, const void* k_new, const 
   }
   const AppendArgs app{k_new, v_new, slot_mapping, k_scale, v_scale};
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
+                     seq_order, &app, nullptr, nullptr, 0, 0, 0, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
                      partition_tokens, scale, kv_dtype, ws, ws_bytes, stream);
 }
@@ -396,6 +402,7 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const float* k_scale, const float* v_scale,
                             const int32_t* block_tables, const int32_t* context_lens,
+              const int32_t* seq_order,
                             const int32_t* group_start, const int32_t* group_prefix_blocks,
                             int32_t num_groups, int32_t max_group_seqs,
                             int32_t max_prefix_blocks, int32_t num_seqs,
@@ -406,7 +413,7 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                             void* stream) {
   if (!group_start) return PA_ERR_INVALID_ARG;
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                     nullptr, group_start, group_prefix_blocks, num_groups, max_group_seqs,
+                     seq_order, nullptr, group_start, group_prefix_blocks, num_groups, max_group_seqs,
                      max_prefix_blocks, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, partition_tokens, scale, kv_dtype,

@@ -144,6 +144,9 @@ struct DecodeParams {
   const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  // [S] grid row y decodes sequence seq_order[y] (a permutation: the caller may put the longest
+  // contexts first, so that their workgroups start first); null = natural order
+  const int32_t* seq_order;
   int32_t* counters;  // [S, HG_total] arrival counters; zero before and after every call
   float* ws_ml;       // [S, Hq, part_slots, 2] (running max in log2 units, running sum)
   float* ws_acc;      // [S, Hq, part_slots, D] unnormalised weighted value sums

@@ -53,7 +53,7 @@ def case_to_device(case):
 
 
 def gpu_decode(d, scale, *, block_tables=None, context_lens=None, max_context_len=0,
-               partition_tokens=0) -> torch.Tensor:
+               partition_tokens=0, seq_order=None) -> torch.Tensor:
     import paged_kv_cache_287_amd as pa
 
     q = d["q"]
@@ -62,8 +62,15 @@ def gpu_decode(d, scale, *, block_tables=None, context_lens=None, max_context_le
                  d["block_tables"] if block_tables is None else block_tables,
                  d["context_lens"] if context_lens is None else context_lens, float(scale),
                  k_scale=d["k_scale"], v_scale=d["v_scale"], max_context_len=max_context_len,
-                 partition_tokens=partition_tokens)
+                 partition_tokens=partition_tokens, seq_order=seq_order)
     return out
+
+
+def longest_first(case) -> torch.Tensor:
+    """Dispatch order with the longest contexts first (ties in batch order), on the device."""
+    import numpy as np
+
+    return dev(np.argsort(-np.asarray(case.context_lens), kind="stable").astype(np.int32))
 
 
 def oracle_decode(case, *, seqs=None, k_cache=None, v_cache=None, block_tables=None,

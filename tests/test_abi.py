@@ -42,7 +42,7 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_version_and_status_strings():
-    assert pa.lib.pa_abi_version() == 1
+    assert pa.lib.pa_abi_version() == 2
     for st in range(5):
         assert pa.lib.pa_status_str(st)
     assert pa.lib.pa_status_str(99) == b"unknown status"
@@ -97,8 +97,9 @@ def test_partition_choice_and_workspace_size():
 
 def decode_args(**over):
     a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
-             block_tables=FAKE, context_lens=FAKE, num_seqs=4, num_q_heads=8, num_kv_heads=2,
-             head_dim=128, block_size=16, num_blocks=10, max_blocks_per_seq=4, max_context_len=0,
+             block_tables=FAKE, context_lens=FAKE, seq_order=None, num_seqs=4, num_q_heads=8,
+             num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10, max_blocks_per_seq=4,
+             max_context_len=0,
              partition_tokens=0, scale=0.125,
              kv_dtype=0, workspace=None, workspace_bytes=0, stream=None)
     a.update(over)
@@ -121,6 +122,7 @@ def decode_args(**over):
     (dict(q=FAKE + 8), pa.PA_ERR_INVALID_ARG),  # misaligned
     (dict(k_cache=FAKE + 4), pa.PA_ERR_INVALID_ARG),
     (dict(context_lens=FAKE + 2), pa.PA_ERR_INVALID_ARG),
+    (dict(seq_order=FAKE + 2), pa.PA_ERR_INVALID_ARG),
     (dict(max_context_len=65), pa.PA_ERR_INVALID_ARG),  # longer than the table allows
     (dict(num_seqs=70000), pa.PA_ERR_INVALID_ARG),
     (dict(max_blocks_per_seq=64), pa.PA_ERR_WORKSPACE),  # 1024 tokens -> 4 partitions of 256
@@ -138,7 +140,8 @@ def test_decode_rejects_bad_arguments(over, expect):
 
 def append_args(**over):
     a = dict(out=FAKE, q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None,
-             v_scale=None, slot_mapping=FAKE, block_tables=FAKE, context_lens=FAKE, num_seqs=2,
+             v_scale=None, slot_mapping=FAKE, block_tables=FAKE, context_lens=FAKE,
+             seq_order=None, num_seqs=2,
              num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10,
              max_blocks_per_seq=4, max_context_len=0, partition_tokens=0, scale=0.125, kv_dtype=0,
              workspace=None, workspace_bytes=0, stream=None)
@@ -290,7 +293,8 @@ def test_prefill_with_no_rows_returns_ok_without_launching():
 
 def shared_args(**over):
     a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, k_scale=None, v_scale=None,
-             block_tables=FAKE, context_lens=FAKE, group_start=FAKE, group_prefix_blocks=FAKE,
+             block_tables=FAKE, context_lens=FAKE, seq_order=None, group_start=FAKE,
+             group_prefix_blocks=FAKE,
              num_groups=2, max_group_seqs=3, max_prefix_blocks=2, num_seqs=4, num_q_heads=8, num_kv_heads=2,
              head_dim=128, block_size=16, num_blocks=10, max_blocks_per_seq=4, max_context_len=0,
              partition_tokens=0, scale=0.125, kv_dtype=0, workspace=None, workspace_bytes=0,
@@ -342,6 +346,6 @@ def test_noalloc_rejects_calls_beyond_its_array_before_touching_the_device():
     need = pa.decode_workspace_bytes(512, 32, 8, 128, 16, 4096, pa.PA_KV_F16, 256)
     assert need > pa.NOALLOC_SCRATCH_BYTES == 16 << 20
     st = pa.lib.pa_decode_append_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
-                                         FAKE, FAKE, 512, 32, 8, 128, 16, 40000, 256, 4096, 256,
+                                         FAKE, FAKE, None, 512, 32, 8, 128, 16, 40000, 256, 4096, 256,
                                          0.088, pa.PA_KV_F16, None)
     assert st == pa.PA_ERR_WORKSPACE

@@ -294,3 +294,32 @@ def test_append_with_empty_sequences(hq, hkv):
     assert slots[0] == -1 and slots[3] == -1
     got = bits(out)
     assert (got[0] == 0).all() and (got[3] == 0).all()
+
+
+@pytest.mark.parametrize("hq,hkv,kv", [(32, 8, "f16"), (32, 1, "f16"), (32, 8, "fp8_e4m3")])
+def test_append_with_longest_first_order(hq, hkv, kv):
+    """pa_decode_append with a longest-first dispatch order: caches equal the oracle's append
+    and outputs are bit-identical to the natural order (256-token partitions, so long sequences
+    are split and merged)."""
+    import paged_kv_cache_287_amd as pa
+    from parity_helpers import longest_first
+
+    case = workloads.random_case(760 + hq + hkv, LENS, hq, hkv, 128, 16, kv_dtype=kv,
+                                 name=f"append_order_{hq}q_{hkv}kv_{kv}")
+    nk, nv, slots = new_rows(case, 761, skip=(4,))
+    ek, ev, eks, evs, ref = expected(case, nk, nv, slots)
+    outs, devs = [], []
+    for order in (None, longest_first(case)):
+        d = case_to_device(case)
+        out = torch.full_like(d["q"], float("nan"))
+        pa.pa_decode_append(out, d["q"], dev(nk), dev(nv), d["k_cache"], d["v_cache"], dev(slots),
+                            d["block_tables"], d["context_lens"], float(case.scale),
+                            k_scale=d["k_scale"], v_scale=d["v_scale"], partition_tokens=256,
+                            seq_order=order)
+        outs.append(out)
+        devs.append(d)
+    torch.cuda.synchronize()
+    assert_attention_close(outs[1], ref, f"append longest-first {hq}q/{hkv}kv {kv}")
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    for name, e in (("k_cache", ek), ("v_cache", ev)):
+        assert np.array_equal(bits(devs[1][name]), host_bits(e)), name

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 
 def gpu_shared(case, d, *, partition_tokens=0, workspace=None, max_context_len=0,
-               max_prefix_blocks=None):
+               max_prefix_blocks=None, seq_order=None):
     import paged_kv_cache_287_amd as pa
 
     gs = case.group_start
@@ -32,7 +32,8 @@ def gpu_shared(case, d, *, partition_tokens=0, workspace=None, max_context_len=0
                                max(1, int(case.group_prefix_blocks.max())),
                                k_scale=d["k_scale"], v_scale=d["v_scale"],
                                max_context_len=max_context_len or int(case.context_lens.max()),
-                               partition_tokens=partition_tokens, workspace=workspace)
+                               partition_tokens=partition_tokens, workspace=workspace,
+                               seq_order=seq_order)
     torch.cuda.synchronize()
     return out
 
@@ -136,3 +137,18 @@ def test_negative_scale():
     case.scale = np.float32(-0.05)
     out = gpu_shared(case, case_to_device(case))
     assert_attention_close(out, oracle_decode(case), "shared-prefix scale<0")
+
+
+@pytest.mark.parametrize("pt", [0, 256])
+def test_longest_first_order_is_bit_identical(pt):
+    """A longest-first dispatch order over groups of uneven tails: bit-identical outputs, and
+    within tolerance of the oracle (the merge kernel and the in-kernel merge both see the prefix
+    partials in the same slots)."""
+    from parity_helpers import longest_first
+
+    case = workloads.prefix_groups(130 + pt, GROUPS, 32, 8, 128, 16)
+    d = case_to_device(case)
+    a = gpu_shared(case, d, partition_tokens=pt)
+    b = gpu_shared(case, d, partition_tokens=pt, seq_order=longest_first(case))
+    assert_attention_close(b, oracle_decode(case), f"shared-prefix longest-first pt={pt}")
+    assert np.array_equal(bits(a), bits(b))
