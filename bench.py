@@ -467,11 +467,19 @@ def main():
     newest = [int(case.block_tables[b, (int(L) - 1) // case.block_size]) * case.block_size
               + (int(L) - 1) % case.block_size if int(L) > 0 else -1
               for b, L in enumerate(case.context_lens)]
-    fused = (args.append == "fused" and not shared and nk.shape[0] == case.num_seqs
+    fused = (args.append == "fused" and nk.shape[0] == case.num_seqs
              and np.array_equal(np.asarray(slots, np.int64), np.asarray(newest, np.int64)))
 
     def decode():
-        if fused:
+        if fused and shared:
+            pa.pa_decode_shared_prefix_append(out, q, g_nk, g_nv, kc, vc, g_slots, tables, lens,
+                                              g_gs, g_gpb, float(case.scale),
+                                              max_group_seqs=max_group,
+                                              max_prefix_blocks=max_prefix, k_scale=ks,
+                                              v_scale=vs, max_context_len=max_ctx,
+                                              partition_tokens=part_tokens, workspace=ws,
+                                              seq_order=g_order)
+        elif fused:
             pa.pa_decode_append(out, q, g_nk, g_nv, kc, vc, g_slots, tables, lens,
                                 float(case.scale), k_scale=ks, v_scale=vs,
                                 max_context_len=max_ctx, partition_tokens=part_tokens,
@@ -579,9 +587,16 @@ def main():
             if g_pairs.shape[0]:
                 pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
             pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
-            pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks, v_scale=vs,
-                         max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws,
-                         seq_order=g_order)
+            if shared:
+                pa.pa_decode_shared_prefix(out, q, kc, vc, tables, lens, g_gs, g_gpb,
+                                           float(case.scale), max_group_seqs=max_group,
+                                           max_prefix_blocks=max_prefix, k_scale=ks, v_scale=vs,
+                                           max_context_len=max_ctx, partition_tokens=part_tokens,
+                                           workspace=ws, seq_order=g_order)
+            else:
+                pa.pa_decode(out, q, kc, vc, tables, lens, float(case.scale), k_scale=ks,
+                             v_scale=vs, max_context_len=max_ctx, partition_tokens=part_tokens,
+                             workspace=ws, seq_order=g_order)
 
         # its own warm-up: the append kernel has not run in this process yet (its first
         # launch loads the code object)
@@ -659,7 +674,9 @@ def main():
             traffic = tr.get("hbm_bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": ("pa_decode_shared_prefix (prefix pass prefill_kernel<PREFIX> + decode "
+                "kernel": ("pa_decode_shared_prefix_append (prefix pass prefill_kernel<PREFIX> + "
+                           "decode partition kernel with the step's append fused)") if shared and fused else
+                          ("pa_decode_shared_prefix (prefix pass prefill_kernel<PREFIX> + decode "
                            "partition kernel, merge fused)") if shared else
                           ("pa_decode_append (decode partition kernel with the step's append and "
                            "the cross-partition merge fused)") if fused else

@@ -321,6 +321,36 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                             void* stream);
 
 /*
+ * pa_decode_shared_prefix_append — one decode step for batches with shared prefixes: the new
+ * token of every sequence is stored into the paged cache at its slot and the batch is decoded
+ * as by pa_decode_shared_prefix, in one call. It computes exactly
+ *     pa_kv_write(k_new, v_new, ..., slot_mapping, num_tokens = num_seqs, ...);
+ *     pa_decode_shared_prefix(out, q, ...);
+ * with bit-identical out and caches: a step of 100 requests behind one system prompt appends
+ * one token to each private tail and attends over the shared prompt and the tail
+ * ("serving-paged-attention", section "공유는 표를 베끼는 일이 된다"). For fp16 caches the decode
+ * launch stores and attends the new rows itself (as pa_decode_append); for E4M3 caches the
+ * append kernel runs first.
+ * Arguments: those of pa_decode_append (k_new, v_new, slot_mapping, writable scales) and of
+ * pa_decode_shared_prefix (group_start, group_prefix_blocks, num_groups, max_group_seqs,
+ * max_prefix_blocks; same workspace size: pa_decode_shared_prefix_workspace_bytes).
+ * Precondition (not checked), beyond those two: an appending sequence's new position
+ * context_lens[b] - 1 lies after its group's shared blocks (group_prefix_blocks[g] *
+ * block_size <= context_lens[b] - 1): a token is never written into a shared block (copy it
+ * first, pa_copy_blocks). Violations give wrong values, never an access outside the buffers.
+ * Validated: as pa_decode_append and pa_decode_shared_prefix.
+ */
+int pa_decode_shared_prefix_append(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    float* k_scale, float* v_scale, const int64_t* slot_mapping, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* seq_order, const int32_t* group_start,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_seqs,
+    int32_t max_prefix_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t partition_tokens, float scale, int32_t kv_dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill — causal attention of a chunk of new tokens per sequence over its paged KV cache
  * (prefill, or one chunk of a chunked prefill).
  *

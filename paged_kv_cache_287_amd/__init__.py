@@ -22,7 +22,8 @@ __all__ = [
     "PA_KV_F16", "PA_KV_FP8_E4M3", "PaError", "LIB_PATH", "lib", "EXPORTED_SYMBOLS",
     "decode_workspace_bytes", "decode_workspace_reset", "decode_partition_tokens", "pa_decode",
     "pa_decode_append", "pa_decode_append_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_prefill", "pa_kv_write",
+    "shared_prefix_workspace_bytes", "pa_decode_shared_prefix", "pa_decode_shared_prefix_append",
+    "pa_prefill", "pa_kv_write",
     "pa_copy_blocks", "pa_swap_blocks", "stream_read_probe",
 ]
 
@@ -50,6 +51,10 @@ EXPORTED_SYMBOLS = {
     "pa_decode_shared_prefix": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]),
+    "pa_decode_shared_prefix_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                      _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                      _f32, _i32, _p, _sz, _p]),
     "pa_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p]),
     "pa_kv_write": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -374,6 +379,70 @@ def pa_decode_shared_prefix(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
                                      ws_bytes, _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_shared_prefix")
+    return out
+
+
+def pa_decode_shared_prefix_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                   v_new: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   group_start: torch.Tensor, group_prefix_blocks: torch.Tensor,
+                                   scale: float, *, max_group_seqs: int, max_prefix_blocks: int,
+                                   k_scale: Optional[torch.Tensor] = None,
+                                   v_scale: Optional[torch.Tensor] = None,
+                                   max_context_len: int = 0, partition_tokens: int = 0,
+                                   workspace: Optional[torch.Tensor] = None,
+                                   seq_order: Optional[torch.Tensor] = None,
+                                   stream=None) -> torch.Tensor:
+    """Enqueue one decode step for a batch with shared prefixes: store each sequence's new K/V
+    row at ``slot_mapping[b]`` and decode as ``pa_decode_shared_prefix``; equal, bit for bit, to
+    ``pa_kv_write`` of the new rows followed by ``pa_decode_shared_prefix``."""
+    _check(q, "q", (torch.float16,), 3)
+    _check(out, "out", (torch.float16,), 3)
+    _check(k_new, "k_new", (torch.float16,), 3)
+    _check(v_new, "v_new", (torch.float16,), 3)
+    _check(k_cache, "k_cache", (torch.float16, torch.uint8, torch.float8_e4m3fn), 4)
+    _check(v_cache, "v_cache", (k_cache.dtype,), 4)
+    _check(slot_mapping, "slot_mapping", (torch.int64,), 1)
+    _check(block_tables, "block_tables", (torch.int32,), 2)
+    _check(context_lens, "context_lens", (torch.int32,), 1)
+    _check(group_start, "group_start", (torch.int32,), 1)
+    _check(group_prefix_blocks, "group_prefix_blocks", (torch.int32,), 1)
+    kvt = _kv_dtype(k_cache)
+    if kvt == PA_KV_FP8_E4M3:
+        for n, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None:
+                raise ValueError(f"{n} is required for an 8-bit cache")
+            _check(s, n, (torch.float32,), 2)
+    num_seqs, num_q_heads, head_dim = q.shape
+    nb, num_kv_heads, block_size, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != head_dim or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if k_new.shape != (num_seqs, num_kv_heads, head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [num_seqs, Hkv, head_dim]")
+    if (block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs
+            or slot_mapping.shape[0] != num_seqs):
+        raise ValueError("block_tables / context_lens / slot_mapping must have one row per sequence")
+    num_groups = group_prefix_blocks.shape[0]
+    if group_start.shape[0] != num_groups + 1:
+        raise ValueError("group_start must have one entry per group plus one")
+    _check_order(seq_order, num_seqs)
+    mbps = block_tables.shape[1]
+    if workspace is None:
+        need = shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size,
+                                             max_context_len if max_context_len > 0 else mbps * block_size,
+                                             kvt, partition_tokens)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.pa_decode_shared_prefix_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), _ptr(seq_order),
+        _ptr(group_start), _ptr(group_prefix_blocks), num_groups, int(max_group_seqs),
+        int(max_prefix_blocks), num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, nb, mbps,
+        max_context_len, partition_tokens, float(scale), kvt, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_shared_prefix_append")
     return out
 
 

@@ -420,6 +420,24 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
                      workspace, workspace_bytes, stream);
 }
 
+int pa_decode_shared_prefix_append(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    float* k_scale, float* v_scale, const int64_t* slot_mapping, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* seq_order, const int32_t* group_start,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_seqs,
+    int32_t max_prefix_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t partition_tokens, float scale, int32_t kv_dtype,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!group_start) return PA_ERR_INVALID_ARG;
+  const AppendArgs app{k_new, v_new, slot_mapping, k_scale, v_scale};
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                     seq_order, &app, group_start, group_prefix_blocks, num_groups,
+                     max_group_seqs, max_prefix_blocks, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                     partition_tokens, scale, kv_dtype, workspace, workspace_bytes, stream);
+}
+
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const float* k_scale, const float* v_scale, const int32_t* block_tables,
                const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,

@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads
 from parity_helpers import (assert_attention_close, bits, case_to_device, dev, gen, gpu_decode,
-                            log, oracle_decode)
+                            host_bits, log, oracle_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,3 +152,81 @@ def test_longest_first_order_is_bit_identical(pt):
     b = gpu_shared(case, d, partition_tokens=pt, seq_order=longest_first(case))
     assert_attention_close(b, oracle_decode(case), f"shared-prefix longest-first pt={pt}")
     assert np.array_equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("fork", [False, True])
+def test_fused_append_step_equals_two_calls(fork):
+    """The shared-prefix workloads' step with the append fused into the shared-prefix decode
+    call: the pool equals the oracle's copy-on-write + append bit for bit, the output is within
+    tolerance of the oracle and bit-identical to pa_kv_write followed by
+    pa_decode_shared_prefix."""
+    import paged_kv_cache_287_amd as pa
+    from parity_helpers import longest_first
+
+    case = gen(workloads.shared_prefix, fork)
+    st = case.step
+    kc, vc, _, _ = oracle.copy_blocks(case.k_cache, case.v_cache, st.block_mapping)
+    ek, ev = oracle.kv_write(st.new_k, st.new_v, kc, vc, st.slot_mapping)
+    ref = oracle_decode(case, k_cache=ek, v_cache=ev)
+    order = longest_first(case)
+    d2, _, _ = apply_step(case)
+    two = gpu_shared(case, d2, seq_order=order)
+    d = case_to_device(case)
+    pa.pa_copy_blocks(d["k_cache"], d["v_cache"], dev(st.block_mapping.reshape(-1, 2)))
+    gs = case.group_start
+    out = torch.full_like(d["q"], float("nan"))
+    pa.pa_decode_shared_prefix_append(
+        out, d["q"], dev(st.new_k), dev(st.new_v), d["k_cache"], d["v_cache"],
+        dev(st.slot_mapping), d["block_tables"], d["context_lens"], dev(gs),
+        dev(case.group_prefix_blocks), float(case.scale), max_group_seqs=int(np.diff(gs).max()),
+        max_prefix_blocks=int(case.group_prefix_blocks.max()),
+        max_context_len=int(case.context_lens.max()), seq_order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d["k_cache"]), host_bits(ek))
+    assert np.array_equal(bits(d["v_cache"]), host_bits(ev))
+    assert_attention_close(out, ref, f"fused shared-prefix step {case.name}")
+    assert np.array_equal(bits(out), bits(two))
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+def test_fused_append_ragged_groups(kv):
+    """Ragged groups (one-member groups, groups without a prefix, empty tails whose members
+    skip the append): the fused call against the oracle's append then decode."""
+    import paged_kv_cache_287_amd as pa
+
+    case = workloads.prefix_groups(140, GROUPS, 32, 8, 128, 16, kv_dtype=kv)
+    rng = np.random.default_rng(141)
+    s, hkv, d_, bs = case.num_seqs, case.num_kv_heads, case.head_dim, case.block_size
+    nk = rng.standard_normal((s, hkv, d_), dtype=np.float32).astype(np.float16)
+    nv = rng.standard_normal((s, hkv, d_), dtype=np.float32).astype(np.float16)
+    slots = np.full(s, -1, np.int64)
+    gpb = np.repeat(case.group_prefix_blocks, np.diff(case.group_start))
+    for b, L in enumerate(case.context_lens):
+        L = int(L)
+        if L >= 1 and L - 1 >= int(gpb[b]) * bs:  # the new position lies in the private tail
+            slots[b] = int(case.block_tables[b, (L - 1) // bs]) * bs + (L - 1) % bs
+    assert (slots < 0).any() and (slots >= 0).sum() > s // 2
+    if kv == "f16":
+        ek, ev = oracle.kv_write(nk, nv, case.k_cache, case.v_cache, slots)
+        eks = evs = None
+    else:
+        ek, ev, eks, evs = oracle.kv_write_fp8(nk, nv, case.k_cache, case.v_cache, case.k_scale,
+                                               case.v_scale, slots)
+    ref = oracle.decode(case.q, ek, ev, case.block_tables, case.context_lens, case.scale,
+                        kv_dtype=kv, k_scale=eks, v_scale=evs)
+    d = case_to_device(case)
+    gs = case.group_start
+    out = torch.full_like(d["q"], float("nan"))
+    pa.pa_decode_shared_prefix_append(
+        out, d["q"], dev(nk), dev(nv), d["k_cache"], d["v_cache"], dev(slots), d["block_tables"],
+        d["context_lens"], dev(gs), dev(case.group_prefix_blocks), float(case.scale),
+        max_group_seqs=int(np.diff(gs).max()),
+        max_prefix_blocks=max(1, int(case.group_prefix_blocks.max())), k_scale=d["k_scale"],
+        v_scale=d["v_scale"], max_context_len=int(case.context_lens.max()))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d["k_cache"]), host_bits(ek))
+    assert np.array_equal(bits(d["v_cache"]), host_bits(ev))
+    if eks is not None:
+        assert np.array_equal(bits(d["k_scale"]), host_bits(eks))
+        assert np.array_equal(bits(d["v_scale"]), host_bits(evs))
+    assert_attention_close(out, ref, f"fused shared-prefix append, ragged groups, {kv}")
