@@ -45,6 +45,7 @@
 //     head stores the rows from its last partition. The result is bit-identical to appending
 //     first and decoding afterwards.
 #include "decode_common.hpp"
+#include "prefill_body.hpp"
 
 namespace pa {
 namespace {
@@ -134,8 +135,16 @@ __device__ __forceinline__ void merge_lane_states(float (&m)[GT], float (&l)[GT]
   }
 }
 
+// LDS of one decode workgroup: the partial state of its 16 DPP rows (4 per wave) for the merge.
+template <int D, int GT>
+constexpr size_t decode_lds_bytes() {
+  return (size_t)kWaves * (kWave / 16) * GT * (D + 2) * sizeof(float);
+}
+
+// One (head group hg, grid row y, partition) workgroup of a grid with nseq rows.
 template <int D, int BS, int GT, bool KV8, bool APPEND>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y, int part_idx,
+                                            int nseq, uint8_t* lds) {
   static_assert(!(APPEND && KV8), "the fused append covers fp16 caches");
   using Lay = RowLayout<D, BS, GT, KV8>;
   constexpr int LPT = Lay::LPT;
@@ -153,16 +162,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 
   // With 8 or more KV heads, head groups of one KV head are kvh, kvh + Hkv, ...: workgroup ids
   // are dealt round-robin over the 8 XCDs, so all of them read that KV head through one L2.
-  const int hg = blockIdx.x;
   // grid row y decodes sequence seq_order[y] when the caller gives an order (clamped, so a bad
   // entry reads a wrong sequence, never outside the arrays)
-  const int b = p.seq_order != nullptr ? min(max(p.seq_order[blockIdx.y], 0), (int)gridDim.y - 1)
-                                       : (int)blockIdx.y;
+  const int b = p.seq_order != nullptr ? min(max(p.seq_order[y], 0), nseq - 1) : y;
   // partitions are dispatched in order, partition 0 of every sequence first: that is the
   // full-size piece of every long context, while higher indices exist only for long contexts
   // and end with their partial last piece. Dispatching the last ones first left those full
   // pieces for the end of the grid (uneven lengths at 128 x [32, 8192] tokens: 153 -> 148.5 us)
-  const int part = (int)blockIdx.z;
+  const int part = part_idx;
   const int kvh = hg % p.num_kv_heads;
   const int h0 = kvh * p.group + (hg / p.num_kv_heads) * GT;
   const SeqRange sr = seq_range<BS>(p, b);
@@ -420,8 +427,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   // ---- merge the 4 DPP rows x kWaves waves of this workgroup through LDS ---------------
   // Lanes 0 .. LPT-1 of each DPP row now hold the whole row's state.
   constexpr int kDppRows = kWave / 16;
-  __shared__ float s_acc[kWaves * kDppRows][GT][D];
-  __shared__ float s_ml[kWaves * kDppRows][GT][2];
+  auto s_acc = reinterpret_cast<float (*)[GT][D]>(lds);  // [kWaves * kDppRows][GT][D]
+  auto s_ml = reinterpret_cast<float (*)[GT][2]>(lds + sizeof(float) * kWaves * kDppRows * GT * D);
   const int sub = wave * kDppRows + (lane >> 4);
   if ((lane & 15) < LPT) {
 #pragma unroll
@@ -457,6 +464,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 }
 
 template <int D, int BS, int GT, bool KV8, bool APPEND>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
+  __shared__ __align__(16) uint8_t lds[decode_lds_bytes<D, GT>()];
+  decode_body<D, BS, GT, KV8, APPEND>(p, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y, lds);
+}
+
+template <int D, int BS, int GT, bool KV8, bool APPEND>
 hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.head_groups, num_seqs, p.max_parts);
   decode_partition_kernel<D, BS, GT, KV8, APPEND><<<grid, kThreads, 0, stream>>>(p);
@@ -473,6 +486,67 @@ hipError_t dispatch_gt(const DecodeParams& p, int num_seqs, int gt, hipStream_t 
     case 8:
       if constexpr (!KV8) return launch_one<D, BS, 8, KV8, APPEND>(p, num_seqs, stream);  // E4M3: at most 4
       break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---- shared-prefix decode in one launch ---------------------------------------------------
+// The first n_prefix workgroups are the prefix pass (the prefill body in its PREFIX form: each
+// group's shared blocks once per KV head for the query rows of all members), the rest are the
+// decode grid over the private tails (head group fastest, then grid row, then partition, as in
+// decode_partition_kernel). The two kinds run side by side instead of one launch after the
+// other; every partial goes to the workspace (deferred_merge = 2) and the merge kernel that
+// follows on the stream combines them exactly.
+template <int D, int BS, int GT, bool KV8, bool APPEND>
+__global__ __launch_bounds__(kThreads, 2) void shared_prefix_decode_kernel(DecodeParams p,
+                                                                        PrefillParams f,
+                                                                        int n_prefix, int nseq) {
+  constexpr size_t kPrefixLds = pf::prefill_lds_bytes<D>();
+  constexpr size_t kDecodeLds = decode_lds_bytes<D, GT>();
+  __shared__ __align__(16) uint8_t lds[kPrefixLds > kDecodeLds ? kPrefixLds : kDecodeLds];
+  const int id = blockIdx.x;
+  if (id < n_prefix) {
+    pf::prefill_body<D, BS, KV8, true>(f, id, n_prefix, lds);
+    return;
+  }
+  const int r = id - n_prefix;
+  const int nx = p.num_kv_heads * p.head_groups;
+  const int yz = r / nx;
+  decode_body<D, BS, GT, KV8, APPEND>(p, r - yz * nx, yz % nseq, yz / nseq, nseq, lds);
+}
+
+template <int D, int BS, int GT, bool KV8, bool APPEND>
+hipError_t launch_sp(const DecodeParams& p, const PrefillParams& f, int n_prefix, int num_seqs,
+                     hipStream_t stream) {
+  const long long n = n_prefix + (long long)p.num_kv_heads * p.head_groups * num_seqs * p.max_parts;
+  shared_prefix_decode_kernel<D, BS, GT, KV8, APPEND>
+      <<<dim3((unsigned)n), kThreads, 0, stream>>>(p, f, n_prefix, num_seqs);
+  return hipGetLastError();
+}
+
+template <int D, int BS, bool KV8, bool APPEND>
+hipError_t sp_dispatch_gt(const DecodeParams& p, const PrefillParams& f, int n_prefix,
+                          int num_seqs, int gt, hipStream_t stream) {
+  switch (gt) {
+    case 1: return launch_sp<D, BS, 1, KV8, APPEND>(p, f, n_prefix, num_seqs, stream);
+    case 2: return launch_sp<D, BS, 2, KV8, APPEND>(p, f, n_prefix, num_seqs, stream);
+    case 3: return launch_sp<D, BS, 3, KV8, APPEND>(p, f, n_prefix, num_seqs, stream);
+    case 4: return launch_sp<D, BS, 4, KV8, APPEND>(p, f, n_prefix, num_seqs, stream);
+    case 8:
+      if constexpr (!KV8) return launch_sp<D, BS, 8, KV8, APPEND>(p, f, n_prefix, num_seqs, stream);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool KV8, bool APPEND>
+hipError_t sp_dispatch_bs(const DecodeParams& p, const PrefillParams& f, int n_prefix,
+                          int num_seqs, int bs, int gt, hipStream_t stream) {
+  switch (bs) {
+    case 8: return sp_dispatch_gt<D, 8, KV8, APPEND>(p, f, n_prefix, num_seqs, gt, stream);
+    case 16: return sp_dispatch_gt<D, 16, KV8, APPEND>(p, f, n_prefix, num_seqs, gt, stream);
+    case 32: return sp_dispatch_gt<D, 32, KV8, APPEND>(p, f, n_prefix, num_seqs, gt, stream);
+    case 64: return sp_dispatch_gt<D, 64, KV8, APPEND>(p, f, n_prefix, num_seqs, gt, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -498,6 +572,23 @@ hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int 
   if (head_dim == 64)
     return kv_fp8 ? dispatch_bs<64, true, false>(p, num_seqs, block_size, head_tile, stream)
                   : dispatch_bs<64, false, false>(p, num_seqs, block_size, head_tile, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_shared_prefix_decode(const DecodeParams& p, const PrefillParams& f,
+                                       int n_prefix, int num_seqs, int head_dim, int block_size,
+                                       int head_tile, bool kv_fp8, bool append,
+                                       hipStream_t stream) {
+  if (head_dim == 128) {
+    if (kv_fp8) return sp_dispatch_bs<128, true, false>(p, f, n_prefix, num_seqs, block_size, head_tile, stream);
+    return append ? sp_dispatch_bs<128, false, true>(p, f, n_prefix, num_seqs, block_size, head_tile, stream)
+                  : sp_dispatch_bs<128, false, false>(p, f, n_prefix, num_seqs, block_size, head_tile, stream);
+  }
+  if (head_dim == 64) {
+    if (kv_fp8) return sp_dispatch_bs<64, true, false>(p, f, n_prefix, num_seqs, block_size, head_tile, stream);
+    return append ? sp_dispatch_bs<64, false, true>(p, f, n_prefix, num_seqs, block_size, head_tile, stream)
+                  : sp_dispatch_bs<64, false, false>(p, f, n_prefix, num_seqs, block_size, head_tile, stream);
+  }
   return hipErrorInvalidValue;
 }
 

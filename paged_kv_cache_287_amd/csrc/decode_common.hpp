@@ -158,7 +158,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, int b, i
     }
     return;
   }
-  if (nparts == 1) {
+  if (nparts == 1 && p.deferred_merge != 2) {
     // this launch's only partition of the sequence plus the `extra` partials an earlier launch
     // (the shared-prefix pass) stored: merge them here and write the output, with no publish of
     // this partition and no arrival count (the earlier kernel's stores are visible to plain

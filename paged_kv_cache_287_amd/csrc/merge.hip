@@ -46,7 +46,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int b
   const int span = L - start;
   const int nparts =
       min(span > 0 ? (span + p.part_tokens - 1) / p.part_tokens : 1, p.max_parts);
-  if (nparts == 1) return;  // written by the decode kernel
+  // sequences the decode kernel finished itself: one partition and no prefix partial, or (prefix
+  // pass in an earlier launch) one partition merged there with the prefix partials
+  if (nparts == 1 && (extra == 0 || p.deferred_merge != 2)) return;
   const int nslots = nparts + extra;
 
   const size_t row0 = ((size_t)b * p.num_q_heads + row) * p.part_slots;

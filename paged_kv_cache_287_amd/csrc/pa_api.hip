@@ -249,11 +249,17 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // the matrix-core kernel's workgroups merge in-kernel (MQA at 64 x 2,048 tokens: 20.5 against
   // 22.2 us with the separate merge).
   p.deferred_merge = ws.total > 0 && max_parts > 1 && !pa::decode_uses_mfma(group);
+  // Shared prefixes with the vector-ALU decode: the prefix pass and the decode run in one launch
+  // and every partial is merged by the merge kernel (shared-prefix step of 100 sequences: see
+  // launch_shared_prefix_decode); with the matrix-core decode the prefix pass is a launch of its
+  // own before it.
+  const bool one_launch = groups && prefix_blocks > 0 && !pa::decode_uses_mfma(group);
+  if (one_launch) p.deferred_merge = 2;
   const hipStream_t st = static_cast<hipStream_t>(stream);
 
+  pa::PrefillParams f{};
   if (groups && prefix_blocks > 0) {
     // prefix pass: every group's shared blocks once per KV head, for all member queries
-    pa::PrefillParams f{};
     f.q = p.q;
     f.k_cache = p.k_cache;
     f.v_cache = p.v_cache;
@@ -280,8 +286,33 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     f.max_prefix_blocks = prefix_blocks;
     f.prefix_split = prefix_split;
     f.prefix_slices = prefix_slices;
-    const int rc = hip_status(pa::launch_prefix_pass(f, num_groups, head_dim, block_size, fp8, st));
-    if (rc != PA_OK) return rc;
+    if (!one_launch) {
+      const int rc = hip_status(pa::launch_prefix_pass(f, num_groups, head_dim, block_size, fp8, st));
+      if (rc != PA_OK) return rc;
+    }
+  }
+  if (one_launch) {
+    const long long n_prefix = prefix_tiles * num_kv_heads * num_groups * prefix_slices;
+    if (n_prefix + (long long)num_kv_heads * (group / gt) * num_seqs * max_parts >= (1LL << 31))
+      return PA_ERR_INVALID_ARG;
+    if (app && fp8) {
+      // E4M3: the append kernel (with the block-scale policy) first
+      const int rc = hip_status(pa::launch_kv_write_fp8(
+          app->k_new, app->v_new, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+          app->k_scale_w, app->v_scale_w, app->slot_mapping, num_seqs, num_kv_heads, head_dim,
+          block_size, num_blocks, st));
+      if (rc != PA_OK) return rc;
+    } else if (app) {
+      p.k_new = static_cast<const uint8_t*>(app->k_new);
+      p.v_new = static_cast<const uint8_t*>(app->v_new);
+      p.slot_mapping = app->slot_mapping;
+      p.k_cache_w = static_cast<uint8_t*>(const_cast<void*>(k_cache));
+      p.v_cache_w = static_cast<uint8_t*>(const_cast<void*>(v_cache));
+    }
+    const hipError_t e = pa::launch_shared_prefix_decode(p, f, (int)n_prefix, num_seqs, head_dim,
+                                                         block_size, gt, fp8, app && !fp8, st);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(pa::launch_decode_merge(p, num_seqs, head_dim, block_size, st));
   }
   if (app) {
     if (!fp8) {

@@ -169,7 +169,9 @@ struct DecodeParams {
   int32_t head_groups;  // G / GT workgroups per KV head
   float scale_log2;     // softmax scale * log2(e)
   // 1: partitions only store their partials (plain stores, no arrival counter) and a second
-  // kernel (launch_decode_merge) merges them; 0: the last workgroup to arrive merges in-kernel
+  // kernel (launch_decode_merge) merges them; 0: the last workgroup to arrive merges in-kernel;
+  // 2: as 1, and sequences with prefix partials publish theirs too (the prefix pass runs in the
+  // same launch, so nothing may read its partials before the merge kernel)
   int32_t deferred_merge;
   // Fused append (pa_decode_append, fp16 caches): the new token of sequence b sits at position
   // context_lens[b] - 1; its rows k_new/v_new[b] ([S, Hkv, D]) are attended in place of the
@@ -240,8 +242,15 @@ hipError_t launch_decode_mfma_append(const DecodeParams& p, int num_seqs, int he
                                      int block_size, int rows, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                               int rows, bool kv_fp8, hipStream_t stream);
+// Shared-prefix decode in one launch: n_prefix prefix-pass workgroups (f) and the vector-ALU
+// decode grid (p, with deferred_merge = 2); launch_decode_merge must follow.
+hipError_t launch_shared_prefix_decode(const DecodeParams& p, const PrefillParams& f,
+                                       int n_prefix, int num_seqs, int head_dim, int block_size,
+                                       int head_tile, bool kv_fp8, bool append,
+                                       hipStream_t stream);
 // Merge of the partition partials of every sequence that spans more than one partition (after a
-// decode launch with deferred_merge = 1, on the same stream).
+// decode launch with deferred_merge = 1, on the same stream), and with deferred_merge = 2 also
+// of every sequence that has prefix partials.
 hipError_t launch_decode_merge(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                                hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int num_seqs, int head_dim, int block_size,

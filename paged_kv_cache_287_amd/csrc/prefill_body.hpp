@@ -1,0 +1,388 @@
+// Prefill workgroup body (see prefill_mfma.hip for the algorithm), shared by the prefill
+// kernel and by the shared-prefix decode kernel, which runs prefix-pass workgroups in the same
+// launch as the decode workgroups.
+#pragma once
+
+#include "decode_common.hpp"
+
+namespace pa {
+namespace pf {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaveRows = 32;                        // query rows per wave (two 16-row tiles)
+constexpr float kRescaleSlack = 8.f;                 // log2 units
+constexpr int kTileTok = 64;                         // attended tokens per LDS tile
+static_assert(kPrefillRows == kWaves * kWaveRows, "rows per workgroup");
+
+// Column of tile token t (0..63) in the transposed V tile. Within each half of 32 tokens, tokens
+// 4c..4c+3 go to columns 8c..8c+3 and tokens 16+4c..16+4c+3 to columns 8c+4..8c+7: exactly the
+// tokens whose scores lane group c holds after the two 16-token S^T products of that half, so
+// those eight scores and the matching eight V^T values meet in the same contraction slots.
+__device__ __forceinline__ int vt_col(int t) {
+  const int half = t & 32, u = t & 31;
+  return half + ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
+}
+
+// Bank swizzle of the transposed V tile: in row d, the 4-column unit k is stored at unit
+// k ^ (2 * ((d >> 4) & 7)). A staging write instruction has 16 lanes writing the same unit of
+// rows 8c + e (c = 0..15); the unpadded row stride would put pairs of those rows on the same
+// banks, the swizzle spreads them over all 64. The XOR keeps even unit pairs together, so a
+// reader's 16-byte operand (units 2i, 2i + 1 of one row) stays contiguous.
+__device__ __forceinline__ int vt_swz(int d, int col) {
+  return col ^ (((d >> 4) & 7) << 3);
+}
+
+template <int NWORDS>
+__device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
+  uint32_t w[4];
+  if constexpr (NWORDS == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = c.w[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      w[2 * i] = e4m3x2_to_f16x2<false>(c.w[i]);
+      w[2 * i + 1] = e4m3x2_to_f16x2<true>(c.w[i]);
+    }
+  }
+  return __builtin_bit_cast(h8, w);
+}
+
+// PREFIX selects the prefix pass of shared-prefix decode: the "sequences" are groups of decode
+// sequences that share leading blocks, each member contributes its G query rows, every row sees
+// all prefix tokens, and the prefix is cut into slices of prefix_split tokens, one workgroup
+// each, whose unnormalised (max, sum, value sum) go to slots 0.. of the decode workspace.
+// LDS of one prefill workgroup: the 64-token K tile, the transposed V tile and the block ids of
+// the attended range.
+template <int D>
+constexpr size_t prefill_lds_bytes() {
+  return (size_t)(kTileTok * (D + 8) + D * (kTileTok + 8)) * 2 + (size_t)kPrefillMaxBlocks * 4;
+}
+
+template <int D, int BS, bool KV8, bool PREFIX>
+__device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in, int nwg,
+                                             uint8_t* lds) {
+  constexpr int NT = kWaveRows / 16;
+  constexpr int KK = D / 32;              // 32-dim steps of S^T = K Q^T
+  constexpr int MT = D / 16;              // 16-dim tiles of O^T
+  constexpr int ESZ = KV8 ? 1 : 2;
+  constexpr int ROW_BYTES = D * ESZ;
+  constexpr int TILE_BYTES = BS * ROW_BYTES;  // one block of one KV head
+  constexpr int NWORDS = 2 * ESZ;         // 32-bit words per 8-element chunk
+  constexpr int DCH = D / 8;              // 8-element chunks per token row
+  constexpr int TPT = kTileTok * DCH / kThreads;  // consecutive tokens staged per thread (4 or 2)
+  constexpr int KRS = D + 8;              // LDS row stride of K (halves)
+  constexpr int VRS = kTileTok + 8;       // LDS row stride of V^T (halves)
+  static_assert(TPT == 4 || TPT == 2, "staging shape");
+
+  // LDS (prefill_lds_bytes<D>()): [K tile][V^T tile][block ids]
+  _Float16* k_lds = reinterpret_cast<_Float16*>(lds);
+  _Float16* vt_lds = k_lds + kTileTok * KRS;
+  int32_t* ids = reinterpret_cast<int32_t*>(vt_lds + D * VRS);
+
+  // ---- which (sequence, KV head, row tile): consecutive ids on one XCD share a KV range ------
+  int wid = wid_in;
+  const int per_xcd = nwg / kNumXcds;
+  if (wid < per_xcd * kNumXcds) wid = (wid % kNumXcds) * per_xcd + wid / kNumXcds;
+  const int qt = wid % p.q_tiles;
+  const int kvh = (wid / p.q_tiles) % p.num_kv_heads;
+  const int unit = wid / (p.q_tiles * p.num_kv_heads);
+  // prefix pass: a unit is (group, slice of prefix_split tokens of its prefix)
+  const int b = PREFIX ? unit / p.prefix_slices : unit;
+  const int slice = PREFIX ? unit - b * p.prefix_slices : 0;
+
+  const int T = p.num_tokens;
+  const int qs = min(max(p.query_start[b], 0), T);
+  const int qe = min(max(p.query_start[b + 1], qs), T);
+  const int n = min(qe - qs, p.max_query_len);
+  const int G = p.group;
+  const int nrows = n * G;
+  const int row0 = qt * kPrefillRows;
+  if (row0 >= nrows) return;  // uniform over the workgroup
+  int base, kv_begin = 0, kv_end;
+  if constexpr (PREFIX) {
+    // the decode pass derives the same clamp and slice count from the same inputs
+    const int total = min(p.group_prefix_blocks[b], p.max_prefix_blocks) * BS;
+    kv_begin = slice * p.prefix_split;
+    if (kv_begin >= total) return;  // no prefix, or fewer slices than the grid allows for
+    kv_end = min(total, kv_begin + p.prefix_split);
+    base = total - 1;     // every row sees the whole prefix
+  } else {
+    const int L = min(max(p.context_lens[b], 0), p.max_context_len);
+    base = L - n;         // position of the chunk's first token
+    kv_end = max(0, min(L, base + (min(row0 + kPrefillRows, nrows) - 1) / G + 1));
+  }
+  // table row: the sequence's own, or (prefix pass) the group's first member's
+  const int32_t* table = p.block_tables + (size_t)(PREFIX ? qs : b) * p.max_blocks_per_seq;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+
+  // ---- block ids of the attended range ------------------------------------------------------
+  // (kv_begin is a multiple of the 64-token tile, hence of the block size)
+  const int blk0 = kv_begin / BS;
+  const int nblk = (kv_end + BS - 1) / BS - blk0;
+  for (int i = tid; i < nblk; i += kThreads) {
+    ids[i] = min(max(table[blk0 + i], 0), p.num_blocks - 1);
+  }
+
+  // ---- this wave's query rows as the B operand of S^T = K Q^T -------------------------------
+  // A negative softmax scale is applied as |scale| with the query negated (exact in fp16), so
+  // the per-score multiplier is positive and the row max can be taken before scaling.
+  const float qscale = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const int wrow0 = row0 + wave * kWaveRows;
+  h8 qb[NT][KK];
+  int pos[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = wrow0 + 16 * nt + lr;
+    const bool ok = r < nrows;
+    const int j = ok ? r / G : 0;
+    const int h = kvh * G + (ok ? r - j * G : 0);
+    pos[nt] = ok ? (PREFIX ? base : base + j) : -1;
+    const _Float16* qrow = p.q + ((size_t)(qs + j) * p.num_q_heads + h) * D + 8 * lq;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk) : u32x4{0, 0, 0, 0};
+      w ^= qsign;
+      qb[nt][kk] = __builtin_bit_cast(h8, w);
+    }
+  }
+  // positions of the wave's first and last valid rows (rows are in token order)
+  const int wpos_lo = PREFIX ? base : base + wrow0 / G;
+  const int wpos_hi =
+      wrow0 < nrows ? (PREFIX ? base : base + (min(wrow0 + kWaveRows, nrows) - 1) / G) : -1;
+
+  float m[NT], l[NT];
+  f4 o[NT][MT], osum[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = kNegInf;
+    l[nt] = 0.f;
+    osum[nt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  // A operand whose row 0 is all ones (lanes lr == 0 hold row 0's eight slots)
+  const _Float16 one = lr == 0 ? (_Float16)1.f : (_Float16)0.f;
+  const h8 ones = h8{one, one, one, one, one, one, one, one};
+
+  // ---- staging: thread -> (TPT consecutive tokens, one 8-element chunk of d) ------------------
+  const int sch = tid % DCH;
+  const int st0 = (tid / DCH) * TPT;
+  const uint8_t* kbase = p.k_cache + (size_t)kvh * TILE_BYTES + sch * 8 * ESZ;
+  const uint8_t* vbase = p.v_cache + (size_t)kvh * TILE_BYTES + sch * 8 * ESZ;
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE_BYTES;
+  Chunk<NWORDS> kr[TPT], vr[TPT];
+
+  // A thread's TPT tokens start at a multiple of 4, so they share one block (block sizes are
+  // multiples of 8): one id lookup per tile. Tokens past kv_end re-read the last token before
+  // it (in bounds; masked later).
+  auto issue = [&](int tile) {
+    const int t0 = tile * kTileTok + st0;
+    const int tc = min(t0, kv_end - 1);
+    const int last = max(0, kv_end - 1 - t0);
+    const size_t off = (size_t)ids[tc / BS - blk0] * blk_stride + (size_t)(tc % BS) * ROW_BYTES;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const size_t o = off + (size_t)min(u, last) * ROW_BYTES;
+      kr[u] = load_chunk<NWORDS>(kbase + o);
+      vr[u] = load_chunk<NWORDS>(vbase + o);
+    }
+  };
+
+  auto stage = [&]() {
+    h8 vv[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      *reinterpret_cast<h8*>(k_lds + (st0 + u) * KRS + 8 * sch) = to_h8(kr[u]);
+      vv[u] = to_h8(vr[u]);
+    }
+    const int col = vt_col(st0);  // st0 .. st0 + TPT - 1 land in consecutive columns
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * sch + e;
+      _Float16* dst = vt_lds + d * VRS + vt_swz(d, col);
+      if constexpr (TPT == 4)
+        *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
+      else
+        *reinterpret_cast<h2*>(dst) = h2{vv[0][e], vv[1][e]};
+    }
+  };
+
+  // masked: the tile reaches some row's causal limit (a uniform branch around the selects)
+  auto compute = [&](int tile, bool masked) {
+    const int tok0 = tile * kTileTok;
+    float kmul[4], vmul[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kmul[s] = qscale;
+      vmul[s] = 1.f;
+      if constexpr (KV8) {
+        // a lane's four tokens 16s + 4lq .. +3 share one block (block sizes are multiples of 4)
+        const int id = ids[min(tok0 + 16 * s + 4 * lq, kv_end - 1) / BS - blk0];
+        kmul[s] *= p.k_scale[(size_t)id * p.num_kv_heads + kvh];
+        vmul[s] = p.v_scale[(size_t)id * p.num_kv_heads + kvh];
+      }
+    }
+    // S^T for the four 16-token sub-tiles and both row tiles
+    f4 sacc[NT][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8 kA[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kA[kk] = *reinterpret_cast<const h8*>(k_lds + (16 * s + lr) * KRS + 32 * kk + 8 * lq);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qb[nt][kk], acc, 0, 0, 0);
+        sacc[nt][s] = acc;
+      }
+    }
+    // online softmax per row (lane lr's row; its 16 tokens of the tile are spread over lq)
+    h8 pB[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // raw scores; the multiplier goes into the exponent's fma (and, with one multiplier for
+      // the whole tile, after the max)
+      float sv[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sv[s][ii] = sacc[nt][s][ii];
+      if (masked) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            if (tok0 + 16 * s + 4 * lq + ii > pos[nt]) sv[s][ii] = kNegInf;
+      }
+      float tm = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) tm = fmaxf(tm, KV8 ? sv[s][ii] * kmul[s] : sv[s][ii]);
+      if constexpr (!KV8) tm *= qscale;
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      // the running max is the reference of l and o; it moves (with a rescale) only when a
+      // score passes it by more than kRescaleSlack (wave-uniform decision), so most tiles skip
+      // the rescale; probabilities stay below 2^kRescaleSlack
+      if (__builtin_amdgcn_ballot_w64(tm > m[nt] + kRescaleSlack) != 0) {
+        const float mn = fmaxf(m[nt], tm);
+        const float alpha = fexp2(m[nt] - (mn == kNegInf ? 0.f : mn));
+        l[nt] *= alpha;
+        if constexpr (!KV8) osum[nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+        m[nt] = mn;
+      }
+      const float nms = m[nt] == kNegInf ? 0.f : -m[nt];
+      float pw[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) pw[s][ii] = fexp2(fmaf(sv[s][ii], kmul[s], nms));
+      if constexpr (KV8) {
+        // the probabilities going to the matrix cores carry the V scale, so the row sums are
+        // taken here; without it they come out of the P.V product (osum)
+        float ps = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) ps += pw[s][ii];
+        l[nt] += ps;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int s0 = 2 * ks, s1 = 2 * ks + 1;
+        pB[nt][ks] = h8{(_Float16)(pw[s0][0] * vmul[s0]), (_Float16)(pw[s0][1] * vmul[s0]),
+                        (_Float16)(pw[s0][2] * vmul[s0]), (_Float16)(pw[s0][3] * vmul[s0]),
+                        (_Float16)(pw[s1][0] * vmul[s1]), (_Float16)(pw[s1][1] * vmul[s1]),
+                        (_Float16)(pw[s1][2] * vmul[s1]), (_Float16)(pw[s1][3] * vmul[s1])};
+      }
+    }
+    // O^T += V^T P^T, 32 tokens per product; for an fp16 cache one more product with an
+    // all-ones row in place of V^T accumulates the row sums of P (osum, element 0 of lanes
+    // lq == 0), on the matrix cores instead of 32 adds per tile
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int d = 16 * mt + lr;
+        const h8 vA = *reinterpret_cast<const h8*>(vt_lds + d * VRS + vt_swz(d, 32 * ks + 8 * lq));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vA, pB[nt][ks], o[nt][mt], 0, 0, 0);
+      }
+      if constexpr (!KV8) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          osum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pB[nt][ks], osum[nt], 0, 0, 0);
+      }
+    }
+  };
+
+  __syncthreads();  // ids visible
+  const int tile_lo = kv_begin / kTileTok;
+  const int tile_hi = (kv_end + kTileTok - 1) / kTileTok;
+  if (tile_lo < tile_hi) issue(tile_lo);
+  for (int i = tile_lo; i < tile_hi; ++i) {
+    __syncthreads();  // every wave is done reading the previous tile
+    stage();
+    __syncthreads();
+    if (i + 1 < tile_hi) issue(i + 1);
+    const int tok0 = i * kTileTok;
+    if (tok0 > wpos_hi) continue;  // every token of the tile is in this wave's causal future
+    compute(i, tok0 + kTileTok - 1 > wpos_lo);
+  }
+
+  // ---- normalise and write this wave's rows ------------------------------------------------
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float lt;
+    if constexpr (KV8) {
+      lt = l[nt];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+    } else {
+      lt = __shfl(osum[nt][0], lr);  // row lr's sum sits in lane lr (lq == 0), element 0
+    }
+    const int r = wrow0 + 16 * nt + lr;
+    if (r >= nrows) continue;
+    const int j = r / G;
+    const int h = kvh * G + (r - j * G);
+    if constexpr (PREFIX) {
+      // slot `slice` of (member qs + j, head h), for the decode pass that follows on the same
+      // stream to merge; the kernel boundary makes these plain stores visible to it
+      const size_t slot = ((size_t)(qs + j) * p.num_q_heads + h) * p.part_slots + slice;
+      float* acc = p.ws_acc + slot * D + 4 * lq;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f4*>(acc + 16 * mt) = o[nt][mt];
+      if (lq == 0) *reinterpret_cast<f2*>(p.ws_ml + slot * 2) = f2{m[nt], lt};
+      continue;
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    _Float16* orow = p.out + ((size_t)(qs + j) * p.num_q_heads + h) * D + 4 * lq;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<h4*>(orow + 16 * mt) =
+          h4{(_Float16)(o[nt][mt][0] * inv), (_Float16)(o[nt][mt][1] * inv),
+             (_Float16)(o[nt][mt][2] * inv), (_Float16)(o[nt][mt][3] * inv)};
+  }
+}
+
+}  // namespace pf
+}  // namespace pa
