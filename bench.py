@@ -710,12 +710,15 @@ def main():
                    "kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
                    "block_size": case.block_size, "kv_dtype": case.kv_dtype,
                    "step": ("copy_blocks(pairs) + decode_append (kv_write of 1 token/seq fused "
-                            "into the decode launch)") if fused else
+                            "into the decode launch)" if case.kv_dtype == "f16" else
+                            "copy_blocks(pairs) + decode_append (E4M3 kv_write of 1 token/seq, "
+                            "then decode, in one call)") if fused else
                            "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
                    "partition_tokens": part_tokens,
                    "decode": "shared_prefix" if shared else "plain",
                    "seq_order": "longest first" if use_order else "batch order",
-                   "append": "fused" if fused else "separate"},
+                   "append": ("separate" if not fused else "fused" if case.kv_dtype == "f16"
+                              else "in the call (E4M3: append kernel, then decode kernel)")},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attainable_read_gbs": attainable,
         "frac_of_attainable": None if attainable is None else value / attainable,
