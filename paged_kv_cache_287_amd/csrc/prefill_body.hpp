@@ -17,6 +17,11 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 constexpr int kWaveRows = 32;                        // query rows per wave (two 16-row tiles)
 constexpr float kRescaleSlack = 8.f;                 // log2 units
 constexpr int kTileTok = 64;                         // attended tokens per LDS tile
+// Row padding (halves) of the K and V^T tiles in LDS. A 16-byte operand read takes 4 cycles per
+// wave when its 64 addresses are spread over the banks and 8 when they pair up; rows of 256 + 32
+// bytes (K, D = 128), 128 + 32 (K, D = 64) and 128 + 32 (V^T) measured 4, rows padded by 16
+// bytes measured 8.
+constexpr int kRowPad = 16;
 static_assert(kPrefillRows == kWaves * kWaveRows, "rows per workgroup");
 
 // Column of tile token t (0..63) in the transposed V tile. Within each half of 32 tokens, tokens
@@ -30,11 +35,23 @@ __device__ __forceinline__ int vt_col(int t) {
 
 // Bank swizzle of the transposed V tile: in row d, the 4-column unit k is stored at unit
 // k ^ (2 * ((d >> 4) & 7)). A staging write instruction has 16 lanes writing the same unit of
-// rows 8c + e (c = 0..15); the unpadded row stride would put pairs of those rows on the same
-// banks, the swizzle spreads them over all 64. The XOR keeps even unit pairs together, so a
-// reader's 16-byte operand (units 2i, 2i + 1 of one row) stays contiguous.
+// rows 8c + e (c = 0..15), which without the XOR all start on the same bank (measured 64 cycles
+// per 512-byte write instead of 8). The XOR keeps even unit pairs together, so a reader's
+// 16-byte operand (units 2i, 2i + 1 of one row) stays contiguous, and with the padded row
+// stride those reads stay conflict-free.
 __device__ __forceinline__ int vt_swz(int d, int col) {
   return col ^ (((d >> 4) & 7) << 3);
+}
+
+// Maximum of x over the four 16-lane rows of the wave (lanes lr, lr + 16, lr + 32, lr + 48),
+// returned in every lane: two cross-row swaps, no LDS round trip.
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int NWORDS>
@@ -61,7 +78,7 @@ __device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
 // the attended range.
 template <int D>
 constexpr size_t prefill_lds_bytes() {
-  return (size_t)(kTileTok * (D + 8) + D * (kTileTok + 8)) * 2 + (size_t)kPrefillMaxBlocks * 4;
+  return (size_t)(kTileTok * (D + kRowPad) + D * (kTileTok + kRowPad)) * 2 + (size_t)kPrefillMaxBlocks * 4;
 }
 
 template <int D, int BS, bool KV8, bool PREFIX>
@@ -76,8 +93,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   constexpr int NWORDS = 2 * ESZ;         // 32-bit words per 8-element chunk
   constexpr int DCH = D / 8;              // 8-element chunks per token row
   constexpr int TPT = kTileTok * DCH / kThreads;  // consecutive tokens staged per thread (4 or 2)
-  constexpr int KRS = D + 8;              // LDS row stride of K (halves)
-  constexpr int VRS = kTileTok + 8;       // LDS row stride of V^T (halves)
+  constexpr int KRS = D + kRowPad;        // LDS row stride of K (halves)
+  constexpr int VRS = kTileTok + kRowPad; // LDS row stride of V^T (halves)
   static_assert(TPT == 4 || TPT == 2, "staging shape");
 
   // LDS (prefill_lds_bytes<D>()): [K tile][V^T tile][block ids]
@@ -275,8 +292,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) tm = fmaxf(tm, KV8 ? sv[s][ii] * kmul[s] : sv[s][ii]);
       if constexpr (!KV8) tm *= qscale;
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      tm = row4_max(tm);
       // the running max is the reference of l and o; it moves (with a rescale) only when a
       // score passes it by more than kRescaleSlack (wave-uniform decision), so most tiles skip
       // the rescale; probabilities stay below 2^kRescaleSlack
