@@ -9,6 +9,7 @@
 //   베끼는 일이 된다"). In the [NB, Hkv, BS, D] layout every (block, head) tile is one
 //   contiguous run of BS * D elements, so a workgroup per (pair, head) streams it with 16-byte
 //   loads and stores; per-(block, head) scales of an 8-bit cache travel with it.
+#include "fp8_append.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
@@ -44,29 +45,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint4* __restrict__
 }
 
 // ---- append into an 8-bit (OCP E4M3) cache --------------------------------------------------
-// The pages say only that the KV cache may be kept in 8 bits ("serving-paged-attention", section
-// "실무에서 만지는 지점"). Each (block, KV head) carries one fp32 scale; the append keeps it an
-// upper bound of the block's content over 448:
-//   s_prev = scale[blk, h], or 0 when the token is the block's first (offset 0);
-//   a = max |x| over the token's row; s = a / 448 if a > s_prev * 448 else s_prev; s = 1 if 0;
-//   if s changed and earlier tokens exist, their codes c become enc((dec(c) * s_prev) / s);
-//   the token is stored as enc(x / s); enc clamps to +-448 and rounds to nearest-even.
-// All arithmetic is fp32 with IEEE division. Tokens of one call that land in the same block are
-// applied in call order (they must be consecutive in the call: a decode step's single token, or
-// a prefill chunk's tokens in order); sequences never write into a shared block.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float e4m3_max() { return 448.f; }
-
-// Clamp two floats to the E4M3 range and convert them, round-to-nearest-even, into bytes 0-1
-// (HI = false) or 2-3 (HI = true) of `old`.
-template <bool HI>
-__device__ __forceinline__ uint32_t enc_pair(float a, float b, uint32_t old) {
-  a = fminf(fmaxf(a, -e4m3_max()), e4m3_max());
-  b = fminf(fmaxf(b, -e4m3_max()), e4m3_max());
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
-}
-
+// The block-scale policy and the encoding are in fp8_append.hpp. Tokens of one call that land
+// in the same block are applied in call order (they must be consecutive in the call: a decode
+// step's single token, or a prefill chunk's tokens in order); sequences never write into a
+// shared block.
 // Launched with two waves per (token, KV head): wave 0 appends K, wave 1 appends V (each cache
 // has its own scales, so the two are independent and run side by side).
 template <int D>
@@ -116,8 +98,7 @@ __global__ __launch_bounds__(128) void kv_write_fp8_kernel(
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
       const float s_prev = off == 0 ? 0.f : (t == t0 ? s_stored : s_cur);
-      float s = amax > s_prev * e4m3_max() ? amax / e4m3_max() : s_prev;
-      if (s == 0.f) s = 1.f;
+      const float s = fp8_append_scale(amax, s_prev);
       if (s != s_prev && off > 0) {
         // re-encode the codes already in the block (this lane's bytes of rows 0 .. off-1)
         for (int r = 0; r < off; ++r) {
@@ -125,12 +106,12 @@ __global__ __launch_bounds__(128) void kv_write_fp8_kernel(
           if constexpr (PER == 2) {
             const uint32_t w = *reinterpret_cast<const uint16_t*>(p);
             const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-            *reinterpret_cast<uint16_t*>(p) =
-                (uint16_t)(enc_pair<false>((c.x * s_prev) / s, (c.y * s_prev) / s, 0u) & 0xFFFFu);
+            *reinterpret_cast<uint16_t*>(p) = (uint16_t)(enc_pair<false>(
+                fp8_rescaled(c.x, s_prev, s), fp8_rescaled(c.y, s_prev, s), 0u) & 0xFFFFu);
           } else {
             const uint32_t w = *p;
             const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-            *p = (uint8_t)(enc_pair<false>((c.x * s_prev) / s, 0.f, 0u) & 0xFFu);
+            *p = (uint8_t)(enc_pair<false>(fp8_rescaled(c.x, s_prev, s), 0.f, 0u) & 0xFFu);
           }
         }
       }

@@ -43,8 +43,13 @@
 //     workgroup that covers position L - 1 takes that token's K/V from the new rows instead of
 //     the cache, so no workgroup depends on another's store; the first head group of each KV
 //     head stores the rows from its last partition. The result is bit-identical to appending
-//     first and decoding afterwards.
+//     first and decoding afterwards. With an 8-bit cache (one head group per KV head, so one
+//     workgroup reads the last block) that workgroup also applies the block-scale policy: the
+//     new rows are encoded under the updated scale, and when the scale grows the block's
+//     earlier codes are re-encoded as they are read (the tiles of the last block take the
+//     masked path) and stored back with the new scales.
 #include "decode_common.hpp"
+#include "fp8_append.hpp"
 #include "prefill_body.hpp"
 
 namespace pa {
@@ -66,6 +71,20 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   if constexpr (LPT >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: pairs the quads of a half-row
   if constexpr (LPT >= 16) x += dpp_mov<0x140>(x); // row_mirror: pairs the two half-rows
   return x;
+}
+
+// Maximum over the same lane groups.
+template <int LPT>
+__device__ __forceinline__ float lane_group_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  if constexpr (LPT >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+  if constexpr (LPT >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
+  return x;
+}
+
+__device__ __forceinline__ float uniform(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -148,7 +167,6 @@ constexpr size_t decode_lds_bytes() {
 template <int D, int BS, int GT, bool KV8, bool APPEND, bool KV_NT = true>
 __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y, int part_idx,
                                             int nseq, uint8_t* lds) {
-  static_assert(!(APPEND && KV8), "the fused append covers fp16 caches");
   using Lay = RowLayout<D, BS, GT, KV8>;
   constexpr int LPT = Lay::LPT;
   constexpr int E = Lay::E;
@@ -196,7 +214,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
   Chunk<NWORDS> knew{}, vnew{};
   int64_t new_slot = -1;
   int newtok = -1;
-  if constexpr (APPEND) {
+  // E4M3: the last block's scales before (s_pk, s_pv) and after (s_k, s_v) the append, whether
+  // its earlier codes are re-encoded (rk, rv), and its first position (last_start)
+  float s_pk = 0.f, s_pv = 0.f, s_k = 1.f, s_v = 1.f;
+  bool rk = false, rv = false;
+  int last_start = 0x7fffffff;
+  if constexpr (APPEND && !KV8) {
     const size_t nrow = ((size_t)b * p.num_kv_heads + kvh) * ROW_BYTES + col * LANE_BYTES;
     knew = load_chunk<NWORDS>(p.k_new + nrow);
     vnew = load_chunk<NWORDS>(p.v_new + nrow);
@@ -204,6 +227,54 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
     if (new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS) newtok = L - 1;
     else new_slot = -1;  // skipped token, or a slot outside the pool: no append
   }
+  if constexpr (APPEND && KV8) {
+    // the lane's E fp16 elements of the new rows (E = 4 * NWORDS, 2E bytes)
+    constexpr int NC = E / 8;  // 16-byte chunks
+    const size_t nrow = (((size_t)b * p.num_kv_heads + kvh) * D + col * E) * 2;
+    Chunk<4> kx[NC], vx[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kx[c] = load_chunk<4>(p.k_new + nrow + 16 * c);
+      vx[c] = load_chunk<4>(p.v_new + nrow + 16 * c);
+    }
+    new_slot = p.slot_mapping[b];
+    if (new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS) newtok = L - 1;
+    else new_slot = -1;
+    if (newtok >= 0) {
+      const int64_t blk = new_slot / BS;
+      const int off = (int)(new_slot - blk * BS);
+      last_start = newtok - off;
+      if (off > 0) {
+        s_pk = p.k_scale[(size_t)blk * p.num_kv_heads + kvh];
+        s_pv = p.v_scale[(size_t)blk * p.num_kv_heads + kvh];
+      }
+      float xk[E], xv[E];
+      float ak = 0.f, av = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t wk = kx[e / 8].w[(e % 8) / 2], wv = vx[e / 8].w[(e % 8) / 2];
+        xk[e] = (float)__builtin_bit_cast(half2_t, wk)[e % 2];
+        xv[e] = (float)__builtin_bit_cast(half2_t, wv)[e % 2];
+        ak = fmaxf(ak, fabsf(xk[e]));
+        av = fmaxf(av, fabsf(xv[e]));
+      }
+      // every lane group holds the whole row, so the row maximum is wave-uniform
+      s_k = uniform(fp8_append_scale(lane_group_max<LPT>(ak), s_pk));
+      s_v = uniform(fp8_append_scale(lane_group_max<LPT>(av), s_pv));
+      rk = s_k != s_pk && off > 0;
+      rv = s_v != s_pv && off > 0;
+#pragma unroll
+      for (int w = 0; w < NWORDS; ++w) {
+        knew.w[w] = enc_pair<true>(xk[4 * w + 2] / s_k, xk[4 * w + 3] / s_k,
+                                   enc_pair<false>(xk[4 * w] / s_k, xk[4 * w + 1] / s_k, 0u));
+        vnew.w[w] = enc_pair<true>(xv[4 * w + 2] / s_v, xv[4 * w + 3] / s_v,
+                                   enc_pair<false>(xv[4 * w] / s_v, xv[4 * w + 1] / s_v, 0u));
+      }
+    }
+  }
+  // the workgroup that stores the step's append: the first head group's last partition
+  const bool appender = APPEND && new_slot >= 0 && (!KV8 || newtok >= 0) && hg < p.num_kv_heads &&
+                        part == nparts - 1;
 
   // ---- query rows of this head group: E fp16 per lane per head -------------------------
   uint32_t qw[GT][NH2];
@@ -273,6 +344,22 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
     }
   };
 
+  // E4M3 append: a step of the last block whose scale grew re-encodes its codes; the appending
+  // workgroup stores them back (positions before the new token: the new row is stored once
+  // below). Every lane writes only the bytes it loaded, and no other workgroup reads the block.
+  auto fix_step = [&](Chunk<NWORDS>& c, int t, float s_prev, float s_new, uint8_t* cache_w) {
+    Chunk<NWORDS> r;
+#pragma unroll
+    for (int w = 0; w < NWORDS; ++w) r.w[w] = fp8_reencode_word(c.w[w], s_prev, s_new);
+    c = r;
+    if (appender && wbase + t + row < newtok) {
+      const int id = __builtin_amdgcn_readlane(my_id, (woff + t) / BS);
+      const size_t off = (size_t)kvh * TILE_BYTES + (size_t)id * blk_stride +
+                         (size_t)(((woff + t) % BS) * ROW_BYTES + lane_off);
+      store_chunk(cache_w + off, r);
+    }
+  };
+
   auto consume_tile = [&](int i, const Chunk<NWORDS>(&kc)[NSTEP],
                           const Chunk<NWORDS>(&vc)[NSTEP], bool masked) {
     const int tok0 = wbase + TT * i;
@@ -282,14 +369,19 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
     for (int s = 0; s < NSTEP; ++s) {
       kmul[s] = p.scale_log2;
       vmul[s] = 1.f;
+      // (wave-uniform; the tiles holding the last block are consumed as masked tiles)
+      const bool in_last = APPEND && KV8 && masked && tok0 + RW * s >= last_start;
       if constexpr (KV8) {
         const int t = TT * i + RW * s;
         const int j = (woff + t) / BS;
-        kmul[s] *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), j));
-        vmul[s] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), j));
+        kmul[s] *= in_last ? s_k : __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), j));
+        vmul[s] = in_last ? s_v : __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), j));
       }
       uint32_t kh[NH2];
       Chunk<NWORDS> kcs = kc[s];
+      if constexpr (APPEND && KV8) {
+        if (in_last && rk) fix_step(kcs, TT * i + RW * s, s_pk, s_k, p.k_cache_w);
+      }
       if constexpr (APPEND) {
         if (masked && tok0 + RW * s + row == newtok) kcs = knew;
       }
@@ -344,6 +436,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       Chunk<NWORDS> vcs = vc[s];
+      if constexpr (APPEND && KV8) {
+        if (masked && tok0 + RW * s >= last_start && rv)
+          fix_step(vcs, TT * i + RW * s, s_pv, s_v, p.v_cache_w);
+      }
       if constexpr (APPEND) {
         if (masked && tok0 + RW * s + row == newtok) vcs = vnew;
       }
@@ -395,31 +491,65 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
   int i = 0;
-  for (; i + 2 < n_tiles; i += 2) {
-    issue_tile(i + 1, kb, vb);
-    consume_tile(i, ka, va, false);
-    issue_tile(i + 2, ka, va);
-    consume_tile(i + 1, kb, vb, false);
-  }
-  if (i + 1 < n_tiles) {
-    issue_tile(i + 1, kb, vb);
-    consume_tile(i, ka, va, false);
-    consume_tile(i + 1, kb, vb, has_tail);
-  } else if (i < n_tiles) {
-    consume_tile(i, ka, va, has_tail);
+  if constexpr (APPEND && KV8) {
+    // E4M3 append: every tile holding a position of the last block goes through the masked
+    // path (blocks of up to 64 tokens, tiles of 16 or more tokens, aligned to the blocks)
+    const int first_masked = max(0, (last_start - wbase) / TT);
+    for (; i + 2 < n_tiles && i + 2 <= first_masked; i += 2) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, false);
+      issue_tile(i + 2, ka, va);
+      consume_tile(i + 1, kb, vb, false);
+    }
+    const bool last_has_tail = has_tail;
+    auto masked_at = [&](int t) {
+      return t >= first_masked || (t == n_tiles - 1 && last_has_tail);
+    };
+    for (; i + 2 < n_tiles; i += 2) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, masked_at(i));
+      issue_tile(i + 2, ka, va);
+      consume_tile(i + 1, kb, vb, masked_at(i + 1));
+    }
+    if (i + 1 < n_tiles) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, masked_at(i));
+      consume_tile(i + 1, kb, vb, masked_at(i + 1));
+    } else if (i < n_tiles) {
+      consume_tile(i, ka, va, masked_at(i));
+    }
+  } else {
+    for (; i + 2 < n_tiles; i += 2) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, false);
+      issue_tile(i + 2, ka, va);
+      consume_tile(i + 1, kb, vb, false);
+    }
+    if (i + 1 < n_tiles) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, false);
+      consume_tile(i + 1, kb, vb, has_tail);
+    } else if (i < n_tiles) {
+      consume_tile(i, ka, va, has_tail);
+    }
   }
 
   // ---- fused append: store the new rows at their slot ----------------------------------
   // Once per (sequence, KV head): the first head group's last partition, lanes 0 .. LPT-1 of
-  // wave 0 (one row). Nothing in this launch reads the slot's cached bytes for position L - 1.
+  // wave 0 (one row), and (E4M3) lane 0 the block's scales. Nothing in this launch reads the
+  // slot's cached bytes for position L - 1, or those scales.
   if constexpr (APPEND) {
-    if (new_slot >= 0 && hg < p.num_kv_heads && part == nparts - 1 && wave == 0 && lane < LPT) {
+    if (appender && wave == 0 && lane < LPT) {
       const int64_t blk = new_slot / BS;
       const int off = (int)(new_slot - blk * BS);
       const size_t dst = ((size_t)blk * p.num_kv_heads + kvh) * TILE_BYTES +
                          (size_t)off * ROW_BYTES + (size_t)col * LANE_BYTES;
       store_chunk(p.k_cache_w + dst, knew);
       store_chunk(p.v_cache_w + dst, vnew);
+      if (KV8 && lane == 0) {
+        p.k_scale_w[(size_t)blk * p.num_kv_heads + kvh] = s_k;
+        p.v_scale_w[(size_t)blk * p.num_kv_heads + kvh] = s_v;
+      }
     }
   }
 
@@ -599,9 +729,13 @@ hipError_t launch_shared_prefix_decode(const DecodeParams& p, const PrefillParam
 }
 
 hipError_t launch_decode_append(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
-                                int head_tile, hipStream_t stream) {
-  if (head_dim == 128) return dispatch_bs<128, false, true>(p, num_seqs, block_size, head_tile, stream);
-  if (head_dim == 64) return dispatch_bs<64, false, true>(p, num_seqs, block_size, head_tile, stream);
+                                int head_tile, bool kv_fp8, hipStream_t stream) {
+  if (head_dim == 128)
+    return kv_fp8 ? dispatch_bs<128, true, true>(p, num_seqs, block_size, head_tile, stream)
+                  : dispatch_bs<128, false, true>(p, num_seqs, block_size, head_tile, stream);
+  if (head_dim == 64)
+    return kv_fp8 ? dispatch_bs<64, true, true>(p, num_seqs, block_size, head_tile, stream)
+                  : dispatch_bs<64, false, true>(p, num_seqs, block_size, head_tile, stream);
   return hipErrorInvalidValue;
 }
 

@@ -173,14 +173,18 @@ struct DecodeParams {
   // 2: as 1, and sequences with prefix partials publish theirs too (the prefix pass runs in the
   // same launch, so nothing may read its partials before the merge kernel)
   int32_t deferred_merge;
-  // Fused append (pa_decode_append, fp16 caches): the new token of sequence b sits at position
-  // context_lens[b] - 1; its rows k_new/v_new[b] ([S, Hkv, D]) are attended in place of the
-  // cache's and stored at slot_mapping[b] (< 0: no append). Null for plain decode.
+  // Fused append (pa_decode_append): the new token of sequence b sits at position
+  // context_lens[b] - 1; its rows k_new/v_new[b] ([S, Hkv, D] fp16) are attended in place of
+  // the cache's and stored at slot_mapping[b] (< 0: no append). Null for plain decode. With an
+  // E4M3 cache the rows are encoded under the block's updated scale, and when that scale grows
+  // the block's earlier codes are re-encoded as they are read and stored back.
   const uint8_t* k_new;
   const uint8_t* v_new;
   const int64_t* slot_mapping;
   uint8_t* k_cache_w;   // writable views of k_cache / v_cache for that store
   uint8_t* v_cache_w;
+  float* k_scale_w;     // writable views of k_scale / v_scale (E4M3 caches)
+  float* v_scale_w;
 };
 
 // ---- prefill geometry ------------------------------------------------------------------
@@ -237,7 +241,7 @@ struct PrefillParams {
 hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                          int head_tile, bool kv_fp8, hipStream_t stream);
 hipError_t launch_decode_append(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
-                                int head_tile, hipStream_t stream);
+                                int head_tile, bool kv_fp8, hipStream_t stream);
 hipError_t launch_decode_mfma_append(const DecodeParams& p, int num_seqs, int head_dim,
                                      int block_size, int rows, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,

@@ -75,10 +75,13 @@ def run_two_calls(d, g_nk, g_nv, g_slots, scale, partition_tokens=0):
     return out
 
 
-def check_case(case, seed, *, skip=(), partition_tokens=0, what=""):
+def check_case(case, seed, *, skip=(), partition_tokens=0, what="", gain=1.0):
     log(f"[append] {what}: S={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
         f"D={case.head_dim} BS={case.block_size} kv={case.kv_dtype} part={partition_tokens}")
     nk, nv, slots = new_rows(case, seed, skip)
+    if gain != 1.0:
+        nk = (nk.astype(np.float32) * gain).astype(np.float16)
+        nv = (nv.astype(np.float32) * gain).astype(np.float16)
     ek, ev, eks, evs, ref = expected(case, nk, nv, slots)
     g_nk, g_nv, g_slots = dev(nk), dev(nv), dev(slots)
 
@@ -100,6 +103,9 @@ def check_case(case, seed, *, skip=(), partition_tokens=0, what=""):
         f"{what}: fused output differs from pa_kv_write + pa_decode"
     for name in ("k_cache", "v_cache"):
         assert torch.equal(d1[name].view(torch.uint8), d2[name].view(torch.uint8)), name
+    if eks is not None:
+        for name in ("k_scale", "v_scale"):
+            assert torch.equal(d1[name].view(torch.int32), d2[name].view(torch.int32)), name
     return nk, nv, slots, out1
 
 
@@ -131,11 +137,39 @@ def test_append_head_groupings(hq, hkv):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq", [8, 64])
 def test_append_fp8_cache(d, hq):
-    """E4M3 caches: the block-scale append, then the decode (two launches), on the vector-ALU
-    (G 4) and matrix-core (G 32) kernels."""
+    """E4M3 caches: the block-scale append fused into the vector-ALU decode launch (G 4), and the
+    append kernel followed by the matrix-core decode (G 32)."""
     case = workloads.random_case(740 + d + hq, LENS, hq, 2, d, 16, kv_dtype="fp8_e4m3",
                                  name=f"append_fp8_d{d}_{hq}q")
     check_case(case, 741 + d, skip=(3,), what=f"append E4M3 D{d} {hq}q")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
+@pytest.mark.parametrize("partition_tokens", [0, 256])
+def test_append_fp8_fused_block_sizes(d, bs, partition_tokens):
+    """The fused E4M3 append at every block size (a last block spanning several tiles or two
+    waves' ranges at BS 64; 8-byte lanes at D 64, BS 8), with whole and split sequences: codes and
+    scales equal the oracle's append, the output the oracle's decode, and both are bit-identical
+    to the append kernel followed by the decode."""
+    case = workloads.random_case(780 + d + bs, LENS, 8, 2, d, bs, kv_dtype="fp8_e4m3",
+                                 name=f"append_fp8_d{d}_bs{bs}")
+    check_case(case, 781 + bs, skip=(2,), partition_tokens=partition_tokens,
+               what=f"append E4M3 D{d} BS{bs} part{partition_tokens}")
+
+
+@pytest.mark.parametrize("gain", [0.01, 8.0])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (35, 1)])
+def test_append_fp8_scale_kept_or_grown(gain, hq, hkv):
+    """New rows 100 times smaller than the cached ones keep every block's scale (no re-encoding);
+    8 times larger ones grow it (every earlier code of the last block re-encoded). G = 1, 2, 3, 4
+    take the fused launch; G = 35 (one-head tiles, several workgroups per KV head) takes the
+    append kernel and then the decode."""
+    case = workloads.random_case(800 + hq + hkv, LENS, hq, hkv, 128, 16, kv_dtype="fp8_e4m3",
+                                 name=f"append_fp8_gain_{hq}q_{hkv}kv")
+    check_case(case, 801 + hq, skip=(4,), gain=gain, what=f"append E4M3 gain {gain} {hq}q/{hkv}kv")
+    check_case(case, 802 + hq, partition_tokens=256, gain=gain,
+               what=f"append E4M3 gain {gain} {hq}q/{hkv}kv part256")
 
 
 def test_append_reuses_workspace_and_repeats_bit_exactly():
