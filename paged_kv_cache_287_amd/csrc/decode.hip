@@ -186,11 +186,14 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
   // grid row y decodes sequence seq_order[y] when the caller gives an order (clamped, so a bad
   // entry reads a wrong sequence, never outside the arrays)
   const int b = p.seq_order != nullptr ? min(max(p.seq_order[y], 0), nseq - 1) : y;
-  // partitions are dispatched in order, partition 0 of every sequence first: that is the
-  // full-size piece of every long context, while higher indices exist only for long contexts
-  // and end with their partial last piece. Dispatching the last ones first left those full
-  // pieces for the end of the grid (uneven lengths at 128 x [32, 8192] tokens: 153 -> 148.5 us)
-  const int part = part_idx;
+  // Dispatch order of the partitions (grid z). In batch order, partition 0 of every sequence
+  // goes first: that is the full-size piece of every long context, while higher indices exist
+  // only for long contexts and end with their partial last piece; the reverse left full pieces
+  // for the end of the grid (uneven lengths at 128 x [32, 8192] tokens: 153 -> 148.5 us). With
+  // a caller's longest-first order the last partitions go first instead: the grid then ends
+  // with partition 0 of the shortest contexts, the smallest pieces of all (same lengths: 145 ->
+  // 138 us).
+  const int part = p.seq_order != nullptr ? p.max_parts - 1 - part_idx : part_idx;
   const int kvh = hg % p.num_kv_heads;
   const int h0 = kvh * p.group + (hg / p.num_kv_heads) * GT;
   const SeqRange sr = seq_range<BS>(p, b);

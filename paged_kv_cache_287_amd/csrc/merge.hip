@@ -10,7 +10,8 @@
 // 16-byte store and its value loads are two 16-byte loads per slot; the slots are taken 8 at a
 // time with all their loads in flight, merged into a running (max, sum, value) in slot order,
 // the same arithmetic as the in-kernel merge of the last-arriving workgroup. Sequences that fit
-// one partition were written by the decode kernel itself and are skipped.
+// one partition were written by the decode kernel itself and are skipped (their first-chunk
+// loads, issued before the slot count is known, read stale slots and are discarded).
 #include "decode_common.hpp"
 
 namespace pa {
@@ -25,6 +26,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int b
   const int row = (int)((blockIdx.x * 256u + threadIdx.x) / TPR);  // query head
   if (row >= p.num_q_heads) return;
   const int d0 = (int)(threadIdx.x % TPR) * 8;
+  constexpr int kChunk = 8;
+  typedef f32x4 f32x4x2[2];
+
+  // The first chunk of slots is loaded before the slot count is known (in bounds: slot indices
+  // are clamped to the row's part_slots), so those loads and the context length travel together.
+  const size_t row0 = ((size_t)b * p.num_q_heads + row) * p.part_slots;
+  const float* ml = p.ws_ml + row0 * 2;
+  const float* ac = p.ws_acc + row0 * D + d0;
+  float mv0[kChunk], lv0[kChunk];
+  f32x4x2 av0[kChunk];
+#pragma unroll
+  for (int j = 0; j < kChunk; ++j) {
+    const int i = min(j, p.part_slots - 1);
+    mv0[j] = ml[2 * i];
+    lv0[j] = ml[2 * i + 1];
+    av0[j][0] = *reinterpret_cast<const f32x4*>(ac + (size_t)i * D);
+    av0[j][1] = *reinterpret_cast<const f32x4*>(ac + (size_t)i * D + 4);
+  }
 
   // the decode kernel's partition count for this sequence (see seq_range)
   const int L = p.context_lens[b];
@@ -51,10 +70,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int b
   if (nparts == 1 && (extra == 0 || p.deferred_merge != 2)) return;
   const int nslots = nparts + extra;
 
-  const size_t row0 = ((size_t)b * p.num_q_heads + row) * p.part_slots;
-  const float* ml = p.ws_ml + row0 * 2;
-  const float* ac = p.ws_acc + row0 * D + d0;
-  constexpr int kChunk = 8;
   float mx = kNegInf, ls = 0.f, a[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) a[u] = 0.f;
@@ -64,11 +79,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int b
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       const bool in = i0 + j < nslots;
-      const int i = in ? i0 + j : i0;
-      mv[j] = in ? ml[2 * i] : kNegInf;
-      lv[j] = ml[2 * i + 1];
-      av[j][0] = *reinterpret_cast<const f32x4*>(ac + (size_t)i * D);
-      av[j][1] = *reinterpret_cast<const f32x4*>(ac + (size_t)i * D + 4);
+      if (i0 == 0) {
+        // slots past nslots may hold anything (even non-finite values): zero weight and zeros
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        mv[j] = in ? mv0[j] : kNegInf;
+        lv[j] = in ? lv0[j] : 0.f;
+        av[j][0] = in ? av0[j][0] : z;
+        av[j][1] = in ? av0[j][1] : z;
+      } else {
+        const int i = in ? i0 + j : i0;
+        mv[j] = in ? ml[2 * i] : kNegInf;
+        lv[j] = ml[2 * i + 1];
+        av[j][0] = *reinterpret_cast<const f32x4*>(ac + (size_t)i * D);
+        av[j][1] = *reinterpret_cast<const f32x4*>(ac + (size_t)i * D + 4);
+      }
     }
     float mc = mx;
 #pragma unroll
