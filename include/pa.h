@@ -146,7 +146,9 @@ int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* str
  *                    seq_order[y]); out stays in batch order. With uneven lengths, putting the
  *                    longest contexts first lets their partitions start first instead of forming
  *                    the tail of the grid ("serving-paged-attention", section "블록 크기는 어떻게
- *                    정하나": requests of very different lengths share one batch). Results are
+ *                    정하나": requests of very different lengths share one batch); with an order
+ *                    given, the vector-ALU kernel also dispatches the last partitions of the
+ *                    split contexts first, so the grid ends with the shortest pieces. Results are
  *                    bit-identical for any order. An entry outside [0, num_seqs) is clamped; a
  *                    non-permutation gives wrong outputs (and may leave counters that
  *                    pa_decode_workspace_reset clears), never an access outside the buffers.
