@@ -5,6 +5,11 @@ Two modes, both reading only what rocprofv3 wrote:
 * ``trace DIR``: the ``*kernel_stats.csv`` of a ``--kernel-trace --stats`` run becomes a table
   of calls and average / min / max duration per kernel, plus the decode kernel's algorithmic
   bandwidth (bytes per call taken from the bench JSON line the same run printed).
+* ``sq DIR [DIR ...]``: the ``*counter_collection.csv`` of shader-sequencer counter passes
+  (``SQ_*`` and ``GRBM_GUI_ACTIVE``) become per-dispatch medians for the dominant kernel and
+  the ratios read from them: instructions per wave and per KiB (or per GFLOP), the matrix-core
+  and vector-ALU issue shares, the LDS bank-conflict share, and how the waves' time splits into
+  issuing, waiting to issue and waiting on memory or barriers.
 * ``traffic FETCH_DIR WRITE_DIR``: the ``*counter_collection.csv`` of a ``--pmc FETCH_SIZE``
   run and of a ``--pmc WRITE_SIZE`` run (both with ``bench.py --calibrate``) become HBM bytes
   per dispatch. Each counter is scaled by what it reads for the calibration copy (a plain
@@ -17,6 +22,8 @@ Usage (from the repository root):
     python rocprof_summary.py trace <dir> --bench-log <log> --command "<cmd>" --out <md>
     python rocprof_summary.py traffic <fetch_dir> <write_dir> --bench-log <log> \\
         --command "<fetch cmd>" --command "<write cmd>" --out <md> --json <json>
+    python rocprof_summary.py sq <dir_a> <dir_b> --bench-log <log> --kernel <name prefix> \\
+        --command "<cmd a>" --command "<cmd b>" --out <md>
 """
 from __future__ import annotations
 
@@ -174,9 +181,94 @@ def traffic(args) -> None:
         open(args.json, "a").write("\n")
 
 
+# MI355X: 256 compute units of 4 SIMDs in 8 XCDs. GRBM_GUI_ACTIVE counts GPU-busy cycles once
+# per XCD; a wave64 vector-ALU instruction occupies its SIMD for 4 cycles (16 lanes per cycle).
+N_SIMDS, N_XCDS, N_CUS, VALU_CYCLES = 1024, 8, 256, 4
+
+
+def sq_counters(d: str, prefix: str):
+    """{counter: median over the dominant kernel's dispatches}, and the median duration (ns)."""
+    path = find_one(d, "counter_collection.csv")
+    per, dur = {}, {}
+    for r in csv.DictReader(open(path)):
+        if not is_dominant(r["Kernel_Name"], prefix):
+            continue
+        disp = r["Dispatch_Id"]
+        per.setdefault(r["Counter_Name"], {}).setdefault(disp, 0.0)
+        per[r["Counter_Name"]][disp] += float(r["Counter_Value"])
+        dur[disp] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        sys.exit(f"kernel {prefix!r} not found in {path}")
+    return ({k: statistics.median(v.values()) for k, v in per.items()},
+            statistics.median(dur.values()), len(dur))
+
+
+def sq(args) -> None:
+    vals, durs, ndisp = {}, [], 0
+    for d in args.dirs:
+        v, t, n = sq_counters(d, args.kernel)
+        vals.update(v)
+        durs.append(t)
+        ndisp = max(ndisp, n)
+    b = bench_line(args.bench_log)
+    wl = b["config"]["workload"].split(":")[0]
+    out = [f"# Shader counters: {wl}", "",
+           f"Kernel `{args.kernel}`; one rocprofv3 pass per command (from the repository root "
+           f"on one MI355X):", ""]
+    out += [f"    {c}" for c in args.command]
+    out += ["", f"Per-dispatch medians over {ndisp} dispatches; median duration "
+            f"{statistics.median(durs) / 1e3:.1f} us under the counters.", "",
+            "| counter | value |", "|---|---:|"]
+    for k in sorted(vals):
+        out.append(f"| `{k}` | {vals[k]:.0f} |")
+    out += ["", "| ratio | value | definition |", "|---|---:|---|"]
+    g = vals.get
+    dur_ns = statistics.median(durs)
+    cyc = g("GRBM_GUI_ACTIVE", 0) / N_XCDS
+    if cyc:
+        out.append(f"| clock | {cyc / dur_ns:.2f} GHz | GRBM_GUI_ACTIVE / 8 XCDs / duration |")
+    waves = g("SQ_WAVES")
+    roof = b.get("roofline", {})
+    per_kib = roof.get("algorithmic_bytes_per_call")
+    flops = b.get("flops_per_call")
+    for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+        if g(name) is None:
+            continue
+        if waves:
+            out.append(f"| {name[9:]} per wave | {g(name) / waves:.0f} | {name} / SQ_WAVES |")
+        if flops:
+            out.append(f"| {name[9:]} per GFLOP | {g(name) / (flops / 1e9):.0f} | "
+                       f"{name} / algorithmic GFLOP per call |")
+        elif per_kib:
+            out.append(f"| {name[9:]} per KiB | {g(name) / (per_kib / 1024):.1f} | "
+                       f"{name} / algorithmic KiB per call |")
+    if cyc and g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+        out.append(f"| matrix-core busy | {g('SQ_VALU_MFMA_BUSY_CYCLES') / (N_SIMDS * cyc):.3f} | "
+                   f"SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) |")
+    if cyc and g("SQ_INSTS_VALU") is not None:
+        out.append(f"| vector-ALU issue share | "
+                   f"{VALU_CYCLES * g('SQ_INSTS_VALU') / (N_SIMDS * cyc):.3f} | "
+                   f"4 cycles x SQ_INSTS_VALU / (1024 SIMDs x cycles) |")
+    if cyc and g("SQ_LDS_IDX_ACTIVE"):
+        out.append(f"| LDS active | {g('SQ_LDS_IDX_ACTIVE') / (N_CUS * cyc):.3f} | "
+                   f"SQ_LDS_IDX_ACTIVE / (256 CUs x cycles) |")
+        out.append(f"| LDS bank-conflict share | "
+                   f"{g('SQ_LDS_BANK_CONFLICT', 0) / g('SQ_LDS_IDX_ACTIVE'):.3f} | "
+                   f"SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE |")
+    if g("SQ_WAVE_CYCLES"):
+        for name, what in (("SQ_ACTIVE_INST_ANY", "issuing"),
+                           ("SQ_WAIT_INST_ANY", "waiting to issue (dependencies, busy units)"),
+                           ("SQ_WAIT_ANY", "waiting on memory counters or barriers")):
+            if g(name) is not None:
+                out.append(f"| wave time {what} | {g(name) / g('SQ_WAVE_CYCLES'):.3f} | "
+                           f"{name} / SQ_WAVE_CYCLES |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("mode", choices=["trace", "traffic"])
+    ap.add_argument("mode", choices=["trace", "traffic", "sq"])
     ap.add_argument("dirs", nargs="+", help="rocprofv3 output directories")
     ap.add_argument("--bench-log", required=True, help="stdout of the profiled bench.py run")
     ap.add_argument("--command", action="append", default=[], help="command that made the data")
@@ -188,7 +280,7 @@ def main() -> None:
     ap.add_argument("--out", required=True)
     ap.add_argument("--json", default=None)
     args = ap.parse_args()
-    (trace if args.mode == "trace" else traffic)(args)
+    {"trace": trace, "traffic": traffic, "sq": sq}[args.mode](args)
 
 
 if __name__ == "__main__":

@@ -80,3 +80,41 @@ def test_trace_reports_the_dominant_kernel(tmp_path):
     run("trace", str(d), "--bench-log", str(tmp_path / "b.log"), "--command", "cmd", "--also",
         "other", "--out", out)
     assert "6136 GB/s (76.7 % of 8 TB/s)" in open(out).read()
+
+
+def sq_csv(path, kernel, values, start=0, end=100_000):
+    """One dispatch of `kernel` with the given {counter: value}, plus an unrelated kernel."""
+    lines = [COUNTER_HEADER]
+    for i, (name, v) in enumerate(values.items()):
+        lines.append(f'{i},1,"Agent 1",1,1,1,131072,1,"{kernel}",256,0,0,8,0,32,"{name}",'
+                     f'{v},{start},{end}')
+    lines.append(f'99,2,"Agent 1",1,1,1,512,2,"other",256,0,0,8,0,32,"SQ_WAVES",5,0,1')
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(lines) + "\n")
+
+
+def test_sq_ratios_from_two_counter_passes(tmp_path):
+    # 100 us at 2.0 GHz: GRBM_GUI_ACTIVE counts 200,000 cycles in each of the 8 XCDs
+    cyc = 200_000
+    sq_csv(str(tmp_path / "a" / "a_counter_collection.csv"), DECODE,
+           {"SQ_WAVES": 2048, "SQ_INSTS_VALU": 1024 * cyc // 8, "SQ_INSTS_MFMA": 0,
+            "SQ_VALU_MFMA_BUSY_CYCLES": 0, "GRBM_GUI_ACTIVE": 8 * cyc})
+    sq_csv(str(tmp_path / "b" / "b_counter_collection.csv"), DECODE,
+           {"SQ_WAVE_CYCLES": 1000, "SQ_ACTIVE_INST_ANY": 250, "SQ_WAIT_INST_ANY": 500,
+            "SQ_WAIT_ANY": 250, "SQ_LDS_IDX_ACTIVE": 256 * cyc // 4, "SQ_LDS_BANK_CONFLICT": 16_000_000 // 4,
+            "GRBM_GUI_ACTIVE": 8 * cyc})
+    bench_log(str(tmp_path / "b.log"), 1 << 30)
+    out = str(tmp_path / "sq.md")
+    run("sq", str(tmp_path / "a"), str(tmp_path / "b"), "--bench-log", str(tmp_path / "b.log"),
+        "--kernel", "decode_partition_kernel", "--command", "ca", "--command", "cb", "--out", out)
+    text = open(out).read()
+    assert "ca" in text and "cb" in text
+    assert "| clock | 2.00 GHz |" in text
+    # 1024 * cyc / 8 VALU instructions, 4 cycles each, over 1024 SIMDs x cyc cycles
+    assert "| vector-ALU issue share | 0.500 |" in text
+    assert f"| VALU per wave | {1024 * cyc // 8 // 2048} |" in text
+    # 1 GiB per call = 1,048,576 KiB
+    assert f"| VALU per KiB | {1024 * cyc / 8 / 1048576:.1f} |" in text
+    assert "| LDS active | 0.250 |" in text
+    assert "| LDS bank-conflict share | 0.312 |" in text
+    assert "| wave time waiting to issue (dependencies, busy units) | 0.500 |" in text
