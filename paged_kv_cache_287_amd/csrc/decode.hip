@@ -55,12 +55,6 @@
 namespace pa {
 namespace {
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-
 // Sum over groups of LPT consecutive lanes (4, 8 or 16) of a DPP row; every lane of a group
 // receives the same bits.
 template <int LPT>
@@ -71,20 +65,6 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   if constexpr (LPT >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: pairs the quads of a half-row
   if constexpr (LPT >= 16) x += dpp_mov<0x140>(x); // row_mirror: pairs the two half-rows
   return x;
-}
-
-// Maximum over the same lane groups.
-template <int LPT>
-__device__ __forceinline__ float lane_group_max(float x) {
-  x = fmaxf(x, dpp_mov<0xB1>(x));
-  x = fmaxf(x, dpp_mov<0x4E>(x));
-  if constexpr (LPT >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
-  if constexpr (LPT >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
-  return x;
-}
-
-__device__ __forceinline__ float uniform(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -402,7 +382,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int hg, int y
       const bool valid = !masked || (tok0 + RW * s + row < L);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float x = lane_group_sum<LPT>(sc[s][h]) * kmul[s];
+        const float x = mul_nc(lane_group_sum<LPT>(sc[s][h]), kmul[s]);
         sc[s][h] = valid ? x : kNegInf;
       }
     }

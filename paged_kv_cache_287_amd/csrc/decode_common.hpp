@@ -12,6 +12,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A product the compiler may not fuse with a later add. A score s * k feeds both the running
+// maximum and the exponent 2^(s * k - m); fused into the exponent in unmasked tiles but not in
+// masked ones (where a select sits between them), the same token would round differently
+// depending on the tile's path. Kept separate, the result depends only on the values, and the
+// exponent of the maximum's own token is exactly 0.
+__device__ __forceinline__ float mul_nc(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // Two OCP E4M3 codes (bytes 0-1, or 2-3 with hi) -> two fp16, exactly: every E4M3 value,
 // subnormals included, is representable in fp16, and the NaN code decodes to NaN. gfx950's
 // conversion uses the OCP encoding (checked against the format's definition for all 256 codes).
@@ -29,6 +39,29 @@ __device__ __forceinline__ void publish(float* p, float v) {
 }
 __device__ __forceinline__ float fetch(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum over groups of LPT consecutive lanes (4, 8 or 16) of a DPP row; every lane of a group
+// receives it.
+template <int LPT>
+__device__ __forceinline__ float lane_group_max(float x) {
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16, "lane group");
+  x = fmaxf(x, dpp_mov<0xB1>(x));                           // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));                           // quad_perm [2,3,0,1]
+  if constexpr (LPT >= 8) x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+  if constexpr (LPT >= 16) x = fmaxf(x, dpp_mov<0x140>(x)); // row_mirror
+  return x;
+}
+
+// A value every lane of the wave holds, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
 template <int NWORDS>

@@ -27,6 +27,7 @@
 // staged once in LDS (512 bytes at D 128), where the lanes of position L - 1 read them in the
 // last tile: holding them in registers would cost the 16-row tile a wave per SIMD.
 #include "decode_common.hpp"
+#include "fp8_append.hpp"
 
 namespace pa {
 namespace {
@@ -38,7 +39,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 template <int D, int BS, int NT, bool KV8, bool APPEND>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p) {
-  static_assert(!(APPEND && KV8), "the fused append covers fp16 caches");
   constexpr int R = 16 * NT;         // query rows of one KV head handled by a workgroup
   constexpr int TPL = D / 32;        // consecutive V tokens a lane loads (one 8-dim chunk)
   constexpr int VTS = 20;            // V^T row stride in halves (16 tokens + 4): the staging
@@ -101,19 +101,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                        : h8{0, 0, 0, 0, 0, 0, 0, 0};
 
   // ---- fused append: threads 0 .. 2 NEWC - 1 load the new K row's, then the new V row's
-  // 16-byte chunks (the rows exist for every sequence; the slot decides whether they are used)
-  constexpr int NEWC = ROW_BYTES / 16;
-  __shared__ __align__(16) uint8_t s_new[APPEND ? 2 * ROW_BYTES : 16];
+  // 16-byte chunks of fp16 (the rows exist for every sequence; the slot decides whether they
+  // are used). s_new holds the rows as the cache stores them (fp16, or E4M3 codes under the
+  // block's updated scale), then (E4M3) the scales before and after the append.
+  constexpr int NEWC = D * 2 / 16;     // 16-byte fp16 chunks per new row
+  constexpr int CODEB = ROW_BYTES / NEWC;  // cache bytes of one such chunk (16, or 8 for E4M3)
+  __shared__ __align__(16) uint8_t s_new[APPEND ? 2 * ROW_BYTES + 16 : 16];
   Chunk<4> nrow{};
   int64_t new_slot = -1;
   int newtok = -1;  // position whose K/V come from s_new instead of the cache
+  // E4M3: the last block's scales before (s_pk, s_pv) and after (s_k, s_v) the append, whether
+  // its earlier codes are re-encoded (rk, rv), and its first position (last_start)
+  float s_pk = 0.f, s_pv = 0.f, s_k = 1.f, s_v = 1.f;
+  bool rk = false, rv = false;
+  int last_start = 0x7fffffff;
   if constexpr (APPEND) {
-    const size_t roff = ((size_t)b * p.num_kv_heads + kvh) * ROW_BYTES + (tid % NEWC) * 16;
+    const size_t roff = (((size_t)b * p.num_kv_heads + kvh) * D + (tid % NEWC) * 8) * 2;
     if (tid < 2 * NEWC) nrow = load_chunk<4>((tid < NEWC ? p.k_new : p.v_new) + roff);
     new_slot = p.slot_mapping[b];
     if (new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS) newtok = L - 1;
     else new_slot = -1;  // skipped token, or a slot outside the pool: no append
+    if (KV8 && newtok >= 0 && new_slot % BS > 0 && wave == 0) {
+      const size_t si = (size_t)(new_slot / BS) * p.num_kv_heads + kvh;
+      s_pk = p.k_scale[si];
+      s_pv = p.v_scale[si];
+    }
   }
+  // the workgroup that stores the step's append: the first head group's last partition
+  const bool appender = APPEND && new_slot >= 0 && (!KV8 || newtok >= 0) &&
+                        hg == kvh * p.head_groups && part == nparts - 1;
 
   // ---- block ids of this wave's tokens: lane j holds logical block wbase / BS + j ------------
   // The partition's tokens [p0, p0 + pn) are split evenly over the waves in whole tiles, so a
@@ -238,22 +254,49 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // this lane's four score tokens 4 lq + ii
     float kmul = p.scale_log2, vmul = 1.f;
     if constexpr (KV8) {
-      kmul *= lane_value_of(my_ks, i, 4 * lq);
-      vmul = lane_value_of(my_vs, i, 4 * lq);
+      // (E4M3 append: tokens of the last block use its updated scales; its tiles are masked)
+      const bool last = APPEND && masked && tok0 + 4 * lq >= last_start;
+      kmul *= last ? s_k : lane_value_of(my_ks, i, 4 * lq);
+      vmul = last ? s_v : lane_value_of(my_vs, i, 4 * lq);
+    }
+    Chunk<4> kcs[KL];
+#pragma unroll
+    for (int c = 0; c < KL; ++c) kcs[c] = kc[c];
+    if constexpr (APPEND && KV8) {
+      // E4M3 append: the K codes of a token of the last block are re-encoded under its grown
+      // scale, and stored back by the appending workgroup (positions before the new token);
+      // the new token's codes come from s_new
+      const int t = tok0 + lr;
+      if (masked && rk && t >= last_start && t < newtok) {
+        const int id = block_of(i, lr);
+        const size_t off =
+            (size_t)id * blk_stride + (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES);
+#pragma unroll
+        for (int c = 0; c < KL; ++c) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) kcs[c].w[w] = fp8_reencode_word(kcs[c].w[w], s_pk, s_k);
+          if (appender)
+            store_chunk(p.k_cache_w + (size_t)kvh * TILE_BYTES + off + kdim(2 * c), kcs[c]);
+        }
+      }
+      if (masked && t == newtok) {
+#pragma unroll
+        for (int c = 0; c < KL; ++c) kcs[c] = load_chunk<4>(s_new + kdim(2 * c));
+      }
     }
     h8 kA[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if constexpr (KV8) {
         Chunk<NWORDS> half;  // the 8 codes of step kk
-        half.w[0] = kc[kk >> 1].w[2 * (kk & 1)];
-        half.w[1] = kc[kk >> 1].w[2 * (kk & 1) + 1];
+        half.w[0] = kcs[kk >> 1].w[2 * (kk & 1)];
+        half.w[1] = kcs[kk >> 1].w[2 * (kk & 1) + 1];
         kA[kk] = to_h8(half);
       } else {
-        kA[kk] = to_h8(kc[kk]);
+        kA[kk] = to_h8(kcs[kk]);
       }
     }
-    if constexpr (APPEND) {
+    if constexpr (APPEND && !KV8) {
       if (masked && tok0 + lr == newtok) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
@@ -268,10 +311,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       for (int kk = 0; kk < KK; ++kk)
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qb[nt][kk], s, 0, 0, 0);
       float sc[4];
+      bool valid[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const bool valid = !masked || (tok0 + 4 * lq + ii < L);
-        sc[ii] = valid ? s[ii] * kmul : kNegInf;
+        valid[ii] = !masked || (tok0 + 4 * lq + ii < L);
+        sc[ii] = valid[ii] ? mul_nc(s[ii], kmul) : kNegInf;
       }
       // online softmax for query row 16 nt + lr across the tile's 16 tokens
       float tm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -295,8 +339,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     h8 vv[TPL];
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
-      vv[u] = to_h8(vc[u]);
-      if constexpr (APPEND) {
+      Chunk<NWORDS> vcs = vc[u];
+      if constexpr (APPEND && KV8) {
+        const int t = tok0 + TPL * vtg + u;
+        if (masked && rv && t >= last_start && t < newtok) {
+#pragma unroll
+          for (int w = 0; w < NWORDS; ++w) vcs.w[w] = fp8_reencode_word(vcs.w[w], s_pv, s_v);
+          if (appender) {
+            const int vid = block_of(i, TPL * vtg);
+            const size_t voff = (size_t)vid * blk_stride +
+                                (size_t)(((woff + kTileTokens * i + TPL * vtg) % BS) * ROW_BYTES +
+                                         vch * LANE_BYTES);
+            store_chunk(p.v_cache_w + (size_t)kvh * TILE_BYTES + voff + (size_t)u * ROW_BYTES, vcs);
+          }
+        }
+        if (masked && t == newtok) vcs = load_chunk<NWORDS>(s_new + ROW_BYTES + vch * LANE_BYTES);
+      }
+      vv[u] = to_h8(vcs);
+      if constexpr (APPEND && !KV8) {
         if (masked && tok0 + TPL * vtg + u == newtok)
           vv[u] = *reinterpret_cast<const h8*>(s_new + ROW_BYTES + vch * 16);
       }
@@ -336,37 +396,116 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   }
   const int n_tiles = n_full + (has_tail ? 1 : 0);
   if (n_tiles > 0) issue_tile(0, ka, va);
-  if constexpr (APPEND) {
+  if constexpr (APPEND && !KV8) {
     // after the first tile's loads: the block-id wait before them has already retired the
     // new-row loads, so staging them costs no extra round trip
     if (tid < 2 * NEWC)
       *reinterpret_cast<u32x4*>(s_new + tid * 16) = u32x4{nrow.w[0], nrow.w[1], nrow.w[2], nrow.w[3]};
     __syncthreads();
   }
-  int i = 0;
-  for (; i + 2 < n_tiles; i += 2) {
-    issue_tile(i + 1, kb, vb);
-    consume_tile(i, ka, va, false);
-    issue_tile(i + 2, ka, va);
-    consume_tile(i + 1, kb, vb, false);
+  if constexpr (APPEND && KV8) {
+    // wave 0 applies the block-scale policy to the new rows: row maxima over the NEWC lanes of
+    // each row (one DPP row or half-row), the scales, and the codes under them
+    if (wave == 0 && newtok >= 0) {
+      float x[8], a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = (float)__builtin_bit_cast(h2v, nrow.w[e / 2])[e % 2];
+        a = fmaxf(a, fabsf(x[e]));
+      }
+      a = lane_group_max<NEWC>(a);
+      const float sk = uniform(fp8_append_scale(a, s_pk));
+      const float sv = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fp8_append_scale(a, s_pv)), NEWC));
+      const float s = tid < NEWC ? sk : sv;
+      u32x2 c;
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+        c[w] = enc_pair<true>(x[4 * w + 2] / s, x[4 * w + 3] / s,
+                              enc_pair<false>(x[4 * w] / s, x[4 * w + 1] / s, 0u));
+      if (tid < 2 * NEWC)
+        *reinterpret_cast<u32x2*>(s_new + (tid < NEWC ? 0 : ROW_BYTES) + (tid % NEWC) * CODEB) = c;
+      if (tid == 0)
+        *reinterpret_cast<f4*>(s_new + 2 * ROW_BYTES) = f4{s_pk, sk, s_pv, sv};
+    }
+    __syncthreads();
   }
-  if (i + 1 < n_tiles) {
-    issue_tile(i + 1, kb, vb);
-    consume_tile(i, ka, va, false);
-    consume_tile(i + 1, kb, vb, has_tail);
-  } else if (i < n_tiles) {
-    consume_tile(i, ka, va, has_tail);
+  if constexpr (APPEND && KV8) {
+    if (newtok >= 0) {
+      const f4 sc = *reinterpret_cast<const f4*>(s_new + 2 * ROW_BYTES);
+      const int off = (int)(new_slot % BS);
+      s_pk = uniform(sc[0]);
+      s_k = uniform(sc[1]);
+      s_pv = uniform(sc[2]);
+      s_v = uniform(sc[3]);
+      rk = s_k != s_pk && off > 0;
+      rv = s_v != s_pv && off > 0;
+      last_start = newtok - off;
+    }
+  }
+
+  int i = 0;
+  if constexpr (APPEND && KV8) {
+    // E4M3 append: every tile holding a position of the last block takes the masked path
+    const int first_masked = max(0, (last_start - wbase) / kTileTokens);
+    for (; i + 2 < n_tiles && i + 2 <= first_masked; i += 2) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, false);
+      issue_tile(i + 2, ka, va);
+      consume_tile(i + 1, kb, vb, false);
+    }
+    const bool last_has_tail = has_tail;
+    auto masked_at = [&](int t) {
+      return t >= first_masked || (t == n_tiles - 1 && last_has_tail);
+    };
+    for (; i + 2 < n_tiles; i += 2) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, masked_at(i));
+      issue_tile(i + 2, ka, va);
+      consume_tile(i + 1, kb, vb, masked_at(i + 1));
+    }
+    if (i + 1 < n_tiles) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, masked_at(i));
+      consume_tile(i + 1, kb, vb, masked_at(i + 1));
+    } else if (i < n_tiles) {
+      consume_tile(i, ka, va, masked_at(i));
+    }
+  } else {
+    for (; i + 2 < n_tiles; i += 2) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, false);
+      issue_tile(i + 2, ka, va);
+      consume_tile(i + 1, kb, vb, false);
+    }
+    if (i + 1 < n_tiles) {
+      issue_tile(i + 1, kb, vb);
+      consume_tile(i, ka, va, false);
+      consume_tile(i + 1, kb, vb, has_tail);
+    } else if (i < n_tiles) {
+      consume_tile(i, ka, va, has_tail);
+    }
   }
 
   // fused append: the first head group's last partition stores the new rows at their slot
+  // (E4M3: and the block's scales)
   if constexpr (APPEND) {
-    if (new_slot >= 0 && hg == kvh * p.head_groups && part == nparts - 1 && tid < 2 * NEWC) {
+    if (appender && tid < 2 * NEWC) {
       const int64_t blk = new_slot / BS;
       const int off = (int)(new_slot - blk * BS);
       const size_t dst = ((size_t)blk * p.num_kv_heads + kvh) * TILE_BYTES +
-                         (size_t)off * ROW_BYTES + (size_t)(tid % NEWC) * 16;
-      *reinterpret_cast<u32x4*>((tid < NEWC ? p.k_cache_w : p.v_cache_w) + dst) =
-          *reinterpret_cast<const u32x4*>(s_new + tid * 16);
+                         (size_t)off * ROW_BYTES + (size_t)(tid % NEWC) * CODEB;
+      uint8_t* cache = tid < NEWC ? p.k_cache_w : p.v_cache_w;
+      const uint8_t* src = s_new + (tid < NEWC ? 0 : ROW_BYTES) + (tid % NEWC) * CODEB;
+      if constexpr (KV8) {
+        *reinterpret_cast<u32x2*>(cache + dst) = *reinterpret_cast<const u32x2*>(src);
+        if (tid == 0) {
+          p.k_scale_w[(size_t)blk * p.num_kv_heads + kvh] = s_k;
+          p.v_scale_w[(size_t)blk * p.num_kv_heads + kvh] = s_v;
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(cache + dst) = *reinterpret_cast<const u32x4*>(src);
+      }
     }
   }
 
@@ -471,9 +610,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim,
 }
 
 hipError_t launch_decode_mfma_append(const DecodeParams& p, int num_seqs, int head_dim,
-                                     int block_size, int rows, hipStream_t stream) {
-  if (head_dim == 128) return dispatch_rows<128, false, true>(p, num_seqs, block_size, rows, stream);
-  if (head_dim == 64) return dispatch_rows<64, false, true>(p, num_seqs, block_size, rows, stream);
+                                     int block_size, int rows, bool kv_fp8, hipStream_t stream) {
+  if (head_dim == 128)
+    return kv_fp8 ? dispatch_rows<128, true, true>(p, num_seqs, block_size, rows, stream)
+                  : dispatch_rows<128, false, true>(p, num_seqs, block_size, rows, stream);
+  if (head_dim == 64)
+    return kv_fp8 ? dispatch_rows<64, true, true>(p, num_seqs, block_size, rows, stream)
+                  : dispatch_rows<64, false, true>(p, num_seqs, block_size, rows, stream);
   return hipErrorInvalidValue;
 }
 

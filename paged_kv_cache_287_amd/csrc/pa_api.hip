@@ -315,11 +315,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     return hip_status(pa::launch_decode_merge(p, num_seqs, head_dim, block_size, st));
   }
   if (app) {
-    // One launch: the decode kernel stores and attends the new rows itself. For E4M3 caches the
-    // vector-ALU kernel also applies the block-scale policy when one head group covers the KV
-    // head: the last block of a (sequence, KV head) is then read by one workgroup only, the one
-    // that re-encodes and stores it.
-    if (!fp8 || (!pa::decode_uses_mfma(group) && group == gt)) {
+    // One launch: the decode kernel stores and attends the new rows itself. For E4M3 caches it
+    // also applies the block-scale policy when one head tile covers the KV head's query heads:
+    // the last block of a (sequence, KV head) is then read by one workgroup only, the one that
+    // re-encodes and stores it.
+    if (!fp8 || group == gt) {
       p.k_new = static_cast<const uint8_t*>(app->k_new);
       p.v_new = static_cast<const uint8_t*>(app->v_new);
       p.slot_mapping = app->slot_mapping;
@@ -329,7 +329,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       p.v_scale_w = app->v_scale_w;
       const hipError_t e =
           pa::decode_uses_mfma(group)
-              ? pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, st)
+              ? pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, fp8, st)
               : pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, fp8, st);
       if (e != hipSuccess || !p.deferred_merge) return hip_status(e);
       return hip_status(pa::launch_decode_merge(p, num_seqs, head_dim, block_size, st));

@@ -243,7 +243,7 @@ hipError_t launch_decode(const DecodeParams& p, int num_seqs, int head_dim, int 
 hipError_t launch_decode_append(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                                 int head_tile, bool kv_fp8, hipStream_t stream);
 hipError_t launch_decode_mfma_append(const DecodeParams& p, int num_seqs, int head_dim,
-                                     int block_size, int rows, hipStream_t stream);
+                                     int block_size, int rows, bool kv_fp8, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, int num_seqs, int head_dim, int block_size,
                               int rows, bool kv_fp8, hipStream_t stream);
 // Shared-prefix decode in one launch: n_prefix prefix-pass workgroups (f) and the vector-ALU

@@ -137,34 +137,38 @@ def test_append_head_groupings(hq, hkv):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("hq", [8, 64])
 def test_append_fp8_cache(d, hq):
-    """E4M3 caches: the block-scale append fused into the vector-ALU decode launch (G 4), and the
-    append kernel followed by the matrix-core decode (G 32)."""
+    """E4M3 caches: the block-scale append fused into the vector-ALU (G 4) and matrix-core (G 32)
+    decode launches."""
     case = workloads.random_case(740 + d + hq, LENS, hq, 2, d, 16, kv_dtype="fp8_e4m3",
                                  name=f"append_fp8_d{d}_{hq}q")
     check_case(case, 741 + d, skip=(3,), what=f"append E4M3 D{d} {hq}q")
 
 
+@pytest.mark.parametrize("hq", [8, 16, 64])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [8, 16, 32, 64])
 @pytest.mark.parametrize("partition_tokens", [0, 256])
-def test_append_fp8_fused_block_sizes(d, bs, partition_tokens):
+def test_append_fp8_fused_block_sizes(hq, d, bs, partition_tokens):
     """The fused E4M3 append at every block size (a last block spanning several tiles or two
-    waves' ranges at BS 64; 8-byte lanes at D 64, BS 8), with whole and split sequences: codes and
-    scales equal the oracle's append, the output the oracle's decode, and both are bit-identical
-    to the append kernel followed by the decode."""
-    case = workloads.random_case(780 + d + bs, LENS, 8, 2, d, bs, kv_dtype="fp8_e4m3",
-                                 name=f"append_fp8_d{d}_bs{bs}")
-    check_case(case, 781 + bs, skip=(2,), partition_tokens=partition_tokens,
-               what=f"append E4M3 D{d} BS{bs} part{partition_tokens}")
+    waves' ranges at BS 64; 8-byte lanes at D 64, BS 8), with whole and split sequences, on the
+    vector-ALU kernel (G 4), a padded 16-row matrix-core tile (G 8) and two 16-row tiles (G 32):
+    codes and scales equal the oracle's append, the output the oracle's decode, and both are
+    bit-identical to the append kernel followed by the decode."""
+    case = workloads.random_case(780 + d + bs + hq, LENS, hq, 2, d, bs, kv_dtype="fp8_e4m3",
+                                 name=f"append_fp8_{hq}q_d{d}_bs{bs}")
+    check_case(case, 781 + bs + hq, skip=(2,), partition_tokens=partition_tokens,
+               what=f"append E4M3 {hq}q D{d} BS{bs} part{partition_tokens}")
 
 
 @pytest.mark.parametrize("gain", [0.01, 8.0])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (35, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (16, 2), (24, 2), (32, 1),
+                                    (35, 1), (64, 1)])
 def test_append_fp8_scale_kept_or_grown(gain, hq, hkv):
     """New rows 100 times smaller than the cached ones keep every block's scale (no re-encoding);
     8 times larger ones grow it (every earlier code of the last block re-encoded). G = 1, 2, 3, 4
-    take the fused launch; G = 35 (one-head tiles, several workgroups per KV head) takes the
-    append kernel and then the decode."""
+    (vector-ALU) and 8, 12, 32 (one matrix-core workgroup per KV head) take the fused launch;
+    G = 35 (one-head VALU tiles) and 64 (two 32-row tiles), with several workgroups per KV head,
+    take the append kernel and then the decode."""
     case = workloads.random_case(800 + hq + hkv, LENS, hq, hkv, 128, 16, kv_dtype="fp8_e4m3",
                                  name=f"append_fp8_gain_{hq}q_{hkv}kv")
     check_case(case, 801 + hq, skip=(4,), gain=gain, what=f"append E4M3 gain {gain} {hq}q/{hkv}kv")
