@@ -201,12 +201,13 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * with bit-identical out, caches and scales. For fp16 caches it is one kernel launch: every
  * workgroup covering position context_lens[b] - 1 takes that token's K/V from k_new/v_new[b]
  * instead of the cache, and one workgroup per (sequence, KV head) stores them at
- * slot_mapping[b]. E4M3 caches (whose append may rescale the block) are one launch too when the
- * vector-ALU kernel covers all query heads of a KV head with one head tile (1 to 4 query heads
- * per KV head): the workgroup that reads the sequence's last block applies the block-scale policy
- * of pa_kv_write itself (the rows encoded under the updated scale, the block's earlier codes
- * re-encoded in registers when the scale grows) and stores codes and scales. Other E4M3 head
- * layouts launch the append kernel and then the decode kernel, both on `stream`.
+ * slot_mapping[b]. E4M3 caches (whose append may rescale the block) are one launch too when one
+ * head tile covers all query heads of a KV head (1 to 4 query heads per KV head on the vector
+ * ALU; 5 to 32 in one matrix-core tile): the workgroup that reads the sequence's last block
+ * applies the block-scale policy of pa_kv_write itself (the rows encoded under the updated
+ * scale, the block's earlier codes re-encoded in registers when the scale grows) and stores
+ * codes and scales. Other E4M3 head layouts (several workgroups per KV head) launch the append
+ * kernel and then the decode kernel, both on `stream`.
  *
  *   k_new, v_new   [num_seqs, Hkv, D] fp16, device, 16-byte aligned: row b is sequence b's new
  *                  token (one token per sequence, in sequence order).

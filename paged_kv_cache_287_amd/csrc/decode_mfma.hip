@@ -25,7 +25,10 @@
 // merge through LDS, partial publish / last-arrival merge, the fused append) follows the VALU
 // kernel. For the fused append the new K/V rows of the workgroup's (sequence, KV head) are
 // staged once in LDS (512 bytes at D 128), where the lanes of position L - 1 read them in the
-// last tile: holding them in registers would cost the 16-row tile a wave per SIMD.
+// last tile: holding them in registers would cost the 16-row tile a wave per SIMD. With an 8-bit
+// cache (one workgroup per KV head) wave 0 first applies the block-scale policy to them and
+// stages codes; the tiles of the last block take the masked path, where a grown scale
+// re-encodes the earlier codes as they are read and the appending workgroup stores them back.
 #include "decode_common.hpp"
 #include "fp8_append.hpp"
 
