@@ -163,9 +163,12 @@ def traffic(args) -> None:
     out.append("")
     if dom is None:
         sys.exit(f"kernel {args.kernel!r} not found")
-    alg = b["roofline"]["algorithmic_bytes_per_call"]
-    out.append(f"`{short(dom[0][0], 200)}`: {dom[3]:.6g} HBM bytes per call against {alg} "
-               f"algorithmic bytes (ratio {dom[3] / alg:.4f}).")
+    alg = b["roofline"].get("algorithmic_bytes_per_call")
+    if alg:
+        out.append(f"`{short(dom[0][0], 200)}`: {dom[3]:.6g} HBM bytes per call against {alg} "
+                   f"algorithmic bytes (ratio {dom[3] / alg:.4f}).")
+    else:  # a flop-bound kernel: its bench line prices flops, not bytes
+        out.append(f"`{short(dom[0][0], 200)}`: {dom[3]:.6g} HBM bytes per call.")
     open(args.out, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
     if args.json:
@@ -221,12 +224,15 @@ def sq(args) -> None:
             "| counter | value |", "|---|---:|"]
     for k in sorted(vals):
         out.append(f"| `{k}` | {vals[k]:.0f} |")
-    out += ["", "| ratio | value | definition |", "|---|---:|---|"]
+    out += ["", "Ratios (cycles = GRBM_GUI_ACTIVE / 8, the busy cycles of one XCD during the "
+            "dispatch):", "", "| ratio | value | definition |", "|---|---:|---|"]
     g = vals.get
     dur_ns = statistics.median(durs)
     cyc = g("GRBM_GUI_ACTIVE", 0) / N_XCDS
     if cyc:
-        out.append(f"| clock | {cyc / dur_ns:.2f} GHz | GRBM_GUI_ACTIVE / 8 XCDs / duration |")
+        out.append(f"| busy cycles per ns | {cyc / dur_ns:.2f} | GRBM_GUI_ACTIVE / 8 XCDs / duration "
+                   f"(the clock while busy; above it for dispatches of a few tens of us, whose "
+                   f"busy count includes their start-up and drain) |")
     waves = g("SQ_WAVES")
     roof = b.get("roofline", {})
     per_kib = roof.get("algorithmic_bytes_per_call")

@@ -109,7 +109,7 @@ def test_sq_ratios_from_two_counter_passes(tmp_path):
         "--kernel", "decode_partition_kernel", "--command", "ca", "--command", "cb", "--out", out)
     text = open(out).read()
     assert "ca" in text and "cb" in text
-    assert "| clock | 2.00 GHz |" in text
+    assert "| busy cycles per ns | 2.00 |" in text
     # 1024 * cyc / 8 VALU instructions, 4 cycles each, over 1024 SIMDs x cyc cycles
     assert "| vector-ALU issue share | 0.500 |" in text
     assert f"| VALU per wave | {1024 * cyc // 8 // 2048} |" in text
