@@ -244,11 +244,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.group = group;
   p.head_groups = group / gt;
   p.scale_log2 = scale * 1.4426950408889634f;
-  // Split sequences of the vector-ALU kernel are merged by a kernel of its own (block-size sweep
-  // at 128 x [32, 8192] tokens: 145 against 150 us with the last-arriving workgroup merging);
-  // the matrix-core kernel's workgroups merge in-kernel (MQA at 64 x 2,048 tokens: 20.5 against
-  // 22.2 us with the separate merge).
-  p.deferred_merge = ws.total > 0 && max_parts > 1 && !pa::decode_uses_mfma(group);
+  // Split sequences of the vector-ALU kernel in batch order are merged by a kernel of its own
+  // (block-size sweep at 128 x [32, 8192] tokens: 145 against 150 us with the last-arriving
+  // workgroup merging). With a caller's dispatch order the last partitions go first and the
+  // last-arriving workgroup merges in-kernel, inside the grid's tail (same lengths, longest
+  // first: 136 against 139.5 us). The matrix-core kernel's workgroups always merge in-kernel
+  // (MQA at 64 x 2,048 tokens: 20.5 against 22.2 us with the separate merge). Both merges take
+  // the partials in the same order with the same arithmetic.
+  p.deferred_merge =
+      ws.total > 0 && max_parts > 1 && !pa::decode_uses_mfma(group) && seq_order == nullptr;
   // Shared prefixes with the vector-ALU decode: the prefix pass and the decode run in one launch
   // and every partial is merged by the merge kernel (shared-prefix step of 100 sequences: see
   // launch_shared_prefix_decode); with the matrix-core decode the prefix pass is a launch of its
