@@ -272,17 +272,21 @@ def test_append_full_size_workloads(name):
     assert_attention_close(out1[seqs], ref, f"append, {name}")
 
 
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 1)])
-def test_append_captured_in_a_graph_replays_exactly(hq, hkv):
+def test_append_captured_in_a_graph_replays_exactly(hq, hkv, kv):
     """pa_decode_append captured once into a HIP graph (256-token partitions, so every replay
     also runs the cross-partition merge and returns the arrival counters to zero) and replayed
     several times with eager work between the replays: every replay matches the eager call bit
-    for bit. The workspace is passed in, so nothing inside the capture allocates or clears."""
+    for bit. The workspace is passed in, so nothing inside the capture allocates or clears.
+    Appending the same rows again leaves an E4M3 block's scale and codes as they are, so the
+    replays of the fused E4M3 append (vector ALU at G 4, matrix cores at G 32) repeat too."""
     import paged_kv_cache_287_amd as pa
 
-    case = workloads.random_case(820 + hq, LENS, hq, hkv, 128, 16, name=f"append_graph_{hq}q")
+    case = workloads.random_case(820 + hq, LENS, hq, hkv, 128, 16, kv_dtype=kv,
+                                 name=f"append_graph_{hq}q_{kv}")
     nk, nv, slots = new_rows(case, 821)
-    ek, ev, _, _, ref = expected(case, nk, nv, slots)
+    ek, ev, eks, evs, ref = expected(case, nk, nv, slots)
     d = case_to_device(case)
     g_nk, g_nv, g_slots = dev(nk), dev(nv), dev(slots)
     need = pa.decode_workspace_bytes(case.num_seqs, hq, hkv, 128, 16,
@@ -293,7 +297,8 @@ def test_append_captured_in_a_graph_replays_exactly(hq, hkv):
     def step():
         pa.pa_decode_append(out, d["q"], g_nk, g_nv, d["k_cache"], d["v_cache"], g_slots,
                             d["block_tables"], d["context_lens"], float(case.scale),
-                            partition_tokens=256, workspace=ws)
+                            k_scale=d["k_scale"], v_scale=d["v_scale"], partition_tokens=256,
+                            workspace=ws)
 
     step()
     torch.cuda.synchronize()
@@ -319,6 +324,9 @@ def test_append_captured_in_a_graph_replays_exactly(hq, hkv):
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
     assert np.array_equal(bits(d["k_cache"]), host_bits(ek))
     assert np.array_equal(bits(d["v_cache"]), host_bits(ev))
+    if eks is not None:
+        assert np.array_equal(bits(d["k_scale"]), host_bits(eks))
+        assert np.array_equal(bits(d["v_scale"]), host_bits(evs))
     assert int(ws[:256].count_nonzero()) == 0, "arrival counters not returned to zero"
 
 
