@@ -10,38 +10,18 @@ namespace pf {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaveRows = 32;                        // query rows per wave (two 16-row tiles)
 constexpr float kRescaleSlack = 8.f;                 // log2 units
 constexpr int kTileTok = 64;                         // attended tokens per LDS tile
-// Row padding (halves) of the K and V^T tiles in LDS. A 16-byte operand read takes 4 cycles per
-// wave when its 64 addresses are spread over the banks and 8 when they pair up; rows of 256 + 32
-// bytes (K, D = 128), 128 + 32 (K, D = 64) and 128 + 32 (V^T) measured 4, rows padded by 16
-// bytes measured 8.
+// Row padding (halves) of the K and V tiles in LDS ([token][d] rows). A 16-byte operand read
+// takes 4 cycles per wave when its 64 addresses are spread over the banks and 8 when they pair
+// up; rows of 256 + 32 bytes (D = 128) and 128 + 32 (D = 64) measured 4, rows padded by 16 bytes
+// measured 8.
 constexpr int kRowPad = 16;
 static_assert(kPrefillRows == kWaves * kWaveRows, "rows per workgroup");
-
-// Column of tile token t (0..63) in the transposed V tile. Within each half of 32 tokens, tokens
-// 4c..4c+3 go to columns 8c..8c+3 and tokens 16+4c..16+4c+3 to columns 8c+4..8c+7: exactly the
-// tokens whose scores lane group c holds after the two 16-token S^T products of that half, so
-// those eight scores and the matching eight V^T values meet in the same contraction slots.
-__device__ __forceinline__ int vt_col(int t) {
-  const int half = t & 32, u = t & 31;
-  return half + ((u & 15) >> 2) * 8 + (u >> 4) * 4 + (u & 3);
-}
-
-// Bank swizzle of the transposed V tile: in row d, the 4-column unit k is stored at unit
-// k ^ (2 * ((d >> 4) & 7)). A staging write instruction has 16 lanes writing the same unit of
-// rows 8c + e (c = 0..15), which without the XOR all start on the same bank (measured 64 cycles
-// per 512-byte write instead of 8). The XOR keeps even unit pairs together, so a reader's
-// 16-byte operand (units 2i, 2i + 1 of one row) stays contiguous, and with the padded row
-// stride those reads stay conflict-free.
-__device__ __forceinline__ int vt_swz(int d, int col) {
-  return col ^ (((d >> 4) & 7) << 3);
-}
 
 // Maximum of x over the four 16-lane rows of the wave (lanes lr, lr + 16, lr + 32, lr + 48),
 // returned in every lane: two cross-row swaps, no LDS round trip.
@@ -74,11 +54,11 @@ __device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
 // sequences that share leading blocks, each member contributes its G query rows, every row sees
 // all prefix tokens, and the prefix is cut into slices of prefix_split tokens, one workgroup
 // each, whose unnormalised (max, sum, value sum) go to slots 0.. of the decode workspace.
-// LDS of one prefill workgroup: the 64-token K tile, the transposed V tile and the block ids of
-// the attended range.
+// LDS of one prefill workgroup: the 64-token K and V tiles and the block ids of the attended
+// range.
 template <int D>
 constexpr size_t prefill_lds_bytes() {
-  return (size_t)(kTileTok * (D + kRowPad) + D * (kTileTok + kRowPad)) * 2 + (size_t)kPrefillMaxBlocks * 4;
+  return (size_t)(2 * kTileTok * (D + kRowPad)) * 2 + (size_t)kPrefillMaxBlocks * 4;
 }
 
 template <int D, int BS, bool KV8, bool PREFIX>
@@ -94,13 +74,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   constexpr int DCH = D / 8;              // 8-element chunks per token row
   constexpr int TPT = kTileTok * DCH / kThreads;  // consecutive tokens staged per thread (4 or 2)
   constexpr int KRS = D + kRowPad;        // LDS row stride of K (halves)
-  constexpr int VRS = kTileTok + kRowPad; // LDS row stride of V^T (halves)
+  constexpr int VRS = D + kRowPad;        // LDS row stride of V (halves)
   static_assert(TPT == 4 || TPT == 2, "staging shape");
 
-  // LDS (prefill_lds_bytes<D>()): [K tile][V^T tile][block ids]
+  // LDS (prefill_lds_bytes<D>()): [K tile][V tile][block ids]
   _Float16* k_lds = reinterpret_cast<_Float16*>(lds);
-  _Float16* vt_lds = k_lds + kTileTok * KRS;
-  int32_t* ids = reinterpret_cast<int32_t*>(vt_lds + D * VRS);
+  _Float16* v_lds = k_lds + kTileTok * KRS;
+  int32_t* ids = reinterpret_cast<int32_t*>(v_lds + kTileTok * VRS);
 
   // ---- which (sequence, KV head, row tile): consecutive ids on one XCD share a KV range ------
   int wid = wid_in;
@@ -218,21 +198,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   };
 
   auto stage = [&]() {
-    h8 vv[TPT];
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       *reinterpret_cast<h8*>(k_lds + (st0 + u) * KRS + 8 * sch) = to_h8(kr[u]);
-      vv[u] = to_h8(vr[u]);
-    }
-    const int col = vt_col(st0);  // st0 .. st0 + TPT - 1 land in consecutive columns
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * sch + e;
-      _Float16* dst = vt_lds + d * VRS + vt_swz(d, col);
-      if constexpr (TPT == 4)
-        *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
-      else
-        *reinterpret_cast<h2*>(dst) = h2{vv[0][e], vv[1][e]};
+      *reinterpret_cast<h8*>(v_lds + (st0 + u) * VRS + 8 * sch) = to_h8(vr[u]);
     }
   };
 
@@ -337,8 +306,20 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int d = 16 * mt + lr;
-        const h8 vA = *reinterpret_cast<const h8*>(vt_lds + d * VRS + vt_swz(d, 32 * ks + 8 * lq));
+        // The A operand is V^T: lane (lr, lq) holds dim 16 mt + lr of the tokens its eight
+        // contraction slots stand for (those of its P^T slots: 32 ks + 4 lq + 0..3, then the
+        // same + 16). ds_read_b64_tr_b16 reads it from the row-major V tile: within each
+        // 16-lane group, lane j passes 4 halves of a row and lane i receives, as its element e,
+        // half i % 4 of lane (4 e + i / 4)'s row; lane lr therefore passes the row of token
+        // 32 ks + 4 lq + lr / 4 at dims 16 mt + 4 (lr % 4) .. + 3, and one read covers four
+        // tokens.
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const _Float16* src = v_lds + (32 * ks + 4 * lq + (lr >> 2)) * VRS + 16 * mt + 4 * (lr & 3);
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(src));
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(src + 16 * VRS));
+        const h8 vA = __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vA, pB[nt][ks], o[nt][mt], 0, 0, 0);

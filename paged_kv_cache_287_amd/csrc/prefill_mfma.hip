@@ -14,8 +14,9 @@
 // 64-token tiles; every tile of K and V is read from the cache once per workgroup, converted to
 // fp16 if the cache is 8-bit, and staged in LDS for all four waves:
 //   * K as [token][d] rows: a wave reads its MFMA A operand (16 tokens x 32 dims) straight out;
-//   * V transposed, as [d][token] rows, with the tokens of each 32-token half permuted so that a
-//     lane's eight contraction slots are one 16-byte read (see vt_col).
+//   * V as [token][d] rows as well; the MFMA A operand V^T (a lane's eight contraction slots of
+//     one dim) comes out of the transposed LDS read of gfx950 (ds_read_b64_tr_b16), two per
+//     operand.
 // Per tile and 16-row tile a wave forms S^T = K Q^T with v_mfma_f32_16x16x32_f16 (a lane ends up
 // with four consecutive tokens of one row), updates that row's online softmax in log2 units, and
 // accumulates O^T += V^T P^T, again with 16x16x32, where P^T is taken as-is from the lanes that
