@@ -186,6 +186,18 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   // it (in bounds; masked later).
   auto issue = [&](int tile) {
     const int t0 = tile * kTileTok + st0;
+    if (tile * kTileTok + kTileTok <= kv_end) {
+      // whole tile inside the range (uniform): one address, constant row offsets
+      const size_t off = (size_t)ids[t0 / BS - blk0] * blk_stride + (size_t)(t0 % BS) * ROW_BYTES;
+      const uint8_t* kp = kbase + off;
+      const uint8_t* vp = vbase + off;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        kr[u] = load_chunk<NWORDS>(kp + u * ROW_BYTES);
+        vr[u] = load_chunk<NWORDS>(vp + u * ROW_BYTES);
+      }
+      return;
+    }
     const int tc = min(t0, kv_end - 1);
     const int last = max(0, kv_end - 1 - t0);
     const size_t off = (size_t)ids[tc / BS - blk0] * blk_stride + (size_t)(tc % BS) * ROW_BYTES;
@@ -221,21 +233,24 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
       }
     }
     // S^T for the four 16-token sub-tiles and both row tiles
+    // (32-dim step outermost: the 4 x NT products of one step are independent, so the matrix
+    // cores never wait on a previous product's result)
     f4 sacc[NT][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      h8 kA[KK];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        kA[kk] = *reinterpret_cast<const h8*>(k_lds + (16 * s + lr) * KRS + 32 * kk + 8 * lq);
+      for (int s = 0; s < 4; ++s) sacc[nt][s] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < KK; ++kk) {
+      h8 kA[4];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qb[nt][kk], acc, 0, 0, 0);
-        sacc[nt][s] = acc;
-      }
+      for (int s = 0; s < 4; ++s)
+        kA[s] = *reinterpret_cast<const h8*>(k_lds + (16 * s + lr) * KRS + 32 * kk + 8 * lq);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          sacc[nt][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[s], qb[nt][kk], sacc[nt][s], 0, 0, 0);
     }
     // online softmax per row (lane lr's row; its 16 tokens of the tile are spread over lq)
     h8 pB[NT][2];
@@ -249,11 +264,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) sv[s][ii] = sacc[nt][s][ii];
       if (masked) {
+        const int lim = pos[nt] - tok0 - 4 * lq;  // token 16 s + ii of the lane is past it
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii)
-            if (tok0 + 16 * s + 4 * lq + ii > pos[nt]) sv[s][ii] = kNegInf;
+            if (16 * s + ii > lim) sv[s][ii] = kNegInf;
       }
       float tm = kNegInf;
 #pragma unroll
