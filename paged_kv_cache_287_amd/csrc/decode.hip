@@ -617,7 +617,7 @@ template <int D, int BS, int GT, bool KV8, bool APPEND>
 __global__ __launch_bounds__(kThreads, 2) void shared_prefix_decode_kernel(DecodeParams p,
                                                                         PrefillParams f,
                                                                         int n_prefix, int nseq) {
-  constexpr size_t kPrefixLds = pf::prefill_lds_bytes<D>();
+  constexpr size_t kPrefixLds = pf::prefill_lds_bytes<D, KV8, true>();
   constexpr size_t kDecodeLds = decode_lds_bytes<D, GT>();
   __shared__ __align__(16) uint8_t lds[kPrefixLds > kDecodeLds ? kPrefixLds : kDecodeLds];
   const int id = blockIdx.x;

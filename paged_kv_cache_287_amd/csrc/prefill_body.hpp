@@ -56,9 +56,31 @@ __device__ __forceinline__ h8 to_h8(const Chunk<NWORDS>& c) {
 // each, whose unnormalised (max, sum, value sum) go to slots 0.. of the decode workspace.
 // LDS of one prefill workgroup: the 64-token K and V tiles and the block ids of the attended
 // range.
-template <int D>
+// An fp16 cache outside the prefix pass is staged by direct global -> LDS loads into two
+// unpadded tile buffers (bank conflicts avoided by an XOR swizzle of the 16-byte chunks of a
+// row); 8-bit caches, which need a conversion, and the prefix pass go through registers into
+// one padded buffer.
+template <bool KV8, bool PREFIX>
+constexpr bool prefill_dma() {
+  return !KV8 && !PREFIX;
+}
+template <int D, bool KV8, bool PREFIX>
 constexpr size_t prefill_lds_bytes() {
-  return (size_t)(2 * kTileTok * (D + kRowPad)) * 2 + (size_t)kPrefillMaxBlocks * 4;
+  return (prefill_dma<KV8, PREFIX>() ? (size_t)(4 * kTileTok * D) * 2
+                                     : (size_t)(2 * kTileTok * (D + kRowPad)) * 2) +
+         (size_t)kPrefillMaxBlocks * 4;
+}
+
+// Physical 16-byte chunk slot of logical chunk c of tile row r in the unpadded buffers: c XOR
+// swz(r). Rows hold D / 8 chunks (16 for D = 128, 8 for D = 64). The operand reads then spread
+// over all 64 banks: a K read (16 lanes, rows r0 .. r0 + 15, one chunk each) meets 16 distinct
+// (row parity, slot) pairs, and a transposed V read (32 lanes, rows r0 .. r0 + 7, two adjacent
+// chunks each) 8 distinct chunk pairs per bank half; swz never flips bit 0 for rows that share
+// a pair's banks, so a pair stays a pair.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
 }
 
 template <int D, int BS, bool KV8, bool PREFIX>
@@ -77,10 +99,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   constexpr int VRS = D + kRowPad;        // LDS row stride of V (halves)
   static_assert(TPT == 4 || TPT == 2, "staging shape");
 
-  // LDS (prefill_lds_bytes<D>()): [K tile][V tile][block ids]
+  constexpr bool DMA = prefill_dma<KV8, PREFIX>();
+  // LDS (prefill_lds_bytes): [K tile][V tile]([K tile][V tile] with DMA)[block ids]
   _Float16* k_lds = reinterpret_cast<_Float16*>(lds);
-  _Float16* v_lds = k_lds + kTileTok * KRS;
-  int32_t* ids = reinterpret_cast<int32_t*>(v_lds + kTileTok * VRS);
+  _Float16* v_lds = k_lds + kTileTok * (DMA ? D : KRS);
+  int32_t* ids = reinterpret_cast<int32_t*>(k_lds + kTileTok * (DMA ? 4 * D : KRS + VRS));
+  constexpr int kBuf = kTileTok * 2 * D;  // halves between the two DMA buffers (K and V pairs)
 
   // ---- which (sequence, KV head, row tile): consecutive ids on one XCD share a KV range ------
   int wid = wid_in;
@@ -218,8 +242,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   };
 
   // masked: the tile reaches some row's causal limit (a uniform branch around the selects)
-  auto compute = [&](int tile, bool masked) {
+  // per-lane swizzle terms of the operand reads (rows 16 s + lr; rows 4 lq + lr / 4 (+16))
+  const int xk = DMA ? swz<D>(lr) ^ lq : 0;
+  const int xv = DMA ? swz<D>(4 * lq + (lr >> 2)) ^ ((lr & 3) >> 1) : 0;
+  auto compute = [&](int tile, bool masked, int buf) {
     const int tok0 = tile * kTileTok;
+    const _Float16* kt = k_lds + buf;
+    const _Float16* vtl = v_lds + buf;
     float kmul[4], vmul[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -244,8 +273,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
     for (int kk = 0; kk < KK; ++kk) {
       h8 kA[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kA[s] = *reinterpret_cast<const h8*>(k_lds + (16 * s + lr) * KRS + 32 * kk + 8 * lq);
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (DMA)
+          kA[s] = *reinterpret_cast<const h8*>(kt + (16 * s + lr) * D + 8 * ((4 * kk) ^ xk));
+        else
+          kA[s] = *reinterpret_cast<const h8*>(kt + (16 * s + lr) * KRS + 32 * kk + 8 * lq);
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -330,11 +363,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
         // 32 ks + 4 lq + lr / 4 at dims 16 mt + 4 (lr % 4) .. + 3, and one read covers four
         // tokens.
         typedef short s4 __attribute__((ext_vector_type(4)));
-        const _Float16* src = v_lds + (32 * ks + 4 * lq + (lr >> 2)) * VRS + 16 * mt + 4 * (lr & 3);
+        constexpr int RS = DMA ? D : VRS;
+        const _Float16* src =
+            DMA ? vtl + (32 * ks + 4 * lq + (lr >> 2)) * D + 8 * ((2 * mt) ^ xv) + 4 * (lr & 1)
+                : vtl + (32 * ks + 4 * lq + (lr >> 2)) * VRS + 16 * mt + 4 * (lr & 3);
         const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s4*)(src));
         const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s4*)(src + 16 * VRS));
+            (__attribute__((address_space(3))) s4*)(src + 16 * RS));
         const h8 vA = __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -351,15 +387,78 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   __syncthreads();  // ids visible
   const int tile_lo = kv_begin / kTileTok;
   const int tile_hi = (kv_end + kTileTok - 1) / kTileTok;
-  if (tile_lo < tile_hi) issue(tile_lo);
-  for (int i = tile_lo; i < tile_hi; ++i) {
-    __syncthreads();  // every wave is done reading the previous tile
-    stage();
-    __syncthreads();
-    if (i + 1 < tile_hi) issue(i + 1);
-    const int tok0 = i * kTileTok;
-    if (tok0 > wpos_hi) continue;  // every token of the tile is in this wave's causal future
-    compute(i, tok0 + kTileTok - 1 > wpos_lo);
+  if constexpr (DMA) {
+    // Direct loads: one instruction moves 1 KB (RPI rows) into LDS, lane l's 16 bytes to byte
+    // 16 l, so lane l loads logical chunk (l % CPR) ^ swz(row) of its row. Wave w fills rows
+    // 16 w .. 16 w + 15 of each tile with NI instructions for K and NI for V.
+    constexpr int CPR = D / 8;
+    constexpr int RPI = 1024 / ROW_BYTES;
+    constexpr int NI = 16 / RPI;
+    int loff[NI];  // byte offset of a lane's chunk in its block's tile (rows within one block)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int t = 16 * wave + RPI * j + lane / CPR;
+      loff[j] = (t % BS) * ROW_BYTES + 16 * ((lane % CPR) ^ swz<D>(t));
+    }
+    const uint8_t* kh = p.k_cache + (size_t)kvh * TILE_BYTES;
+    const uint8_t* vh = p.v_cache + (size_t)kvh * TILE_BYTES;
+    auto dma = [&](int tile, int buf) {
+      typedef __attribute__((address_space(3))) void* lds_ptr;
+      if (tile * kTileTok + kTileTok <= kv_end) {
+        // whole tile in range: the RPI rows of one instruction sit in one block (BS >= 8), and
+        // the wave's 16 rows in one block unless BS is 8 (then in two)
+        constexpr int NB = BS >= 16 ? 1 : 2;
+        int bid[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+          bid[k] = __builtin_amdgcn_readfirstlane(
+              ids[(tile * kTileTok + 16 * wave + 8 * k) / BS - blk0]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int row = 16 * wave + RPI * j;
+          const size_t bo = (size_t)bid[NB == 1 ? 0 : (RPI * j) / 8] * blk_stride;
+          __builtin_amdgcn_global_load_lds(kh + bo + loff[j], (lds_ptr)(k_lds + buf + row * D),
+                                           16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vh + bo + loff[j], (lds_ptr)(v_lds + buf + row * D),
+                                           16, 0, 0);
+        }
+      } else {
+        // last tile: rows past kv_end load the last attended token again (finite; masked)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int row = 16 * wave + RPI * j;
+          const int t = row + lane / CPR;
+          const int tok = min(tile * kTileTok + t, kv_end - 1);
+          const size_t o = (size_t)ids[tok / BS - blk0] * blk_stride +
+                           (size_t)(tok % BS) * ROW_BYTES + 16 * ((lane % CPR) ^ swz<D>(t));
+          __builtin_amdgcn_global_load_lds(kh + o, (lds_ptr)(k_lds + buf + row * D), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vh + o, (lds_ptr)(v_lds + buf + row * D), 16, 0, 0);
+        }
+      }
+    };
+    if (tile_lo < tile_hi) dma(tile_lo, 0);
+    for (int i = tile_lo; i < tile_hi; ++i) {
+      const int buf = ((i - tile_lo) & 1) * kBuf;
+      // this wave's loads of tile i have landed; after the barrier every wave's have, and every
+      // wave is done with tile i - 1, whose buffer the next loads overwrite
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (i + 1 < tile_hi) dma(i + 1, kBuf - buf);
+      const int tok0 = i * kTileTok;
+      if (tok0 > wpos_hi) continue;  // every token of the tile is in this wave's causal future
+      compute(i, tok0 + kTileTok - 1 > wpos_lo, buf);
+    }
+  } else {
+    if (tile_lo < tile_hi) issue(tile_lo);
+    for (int i = tile_lo; i < tile_hi; ++i) {
+      __syncthreads();  // every wave is done reading the previous tile
+      stage();
+      __syncthreads();
+      if (i + 1 < tile_hi) issue(i + 1);
+      const int tok0 = i * kTileTok;
+      if (tok0 > wpos_hi) continue;  // every token of the tile is in this wave's causal future
+      compute(i, tok0 + kTileTok - 1 > wpos_lo, 0);
+    }
   }
 
   // ---- normalise and write this wave's rows ------------------------------------------------

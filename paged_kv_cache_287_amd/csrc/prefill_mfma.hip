@@ -20,7 +20,10 @@
 // Per tile and 16-row tile a wave forms S^T = K Q^T with v_mfma_f32_16x16x32_f16 (a lane ends up
 // with four consecutive tokens of one row), updates that row's online softmax in log2 units, and
 // accumulates O^T += V^T P^T, again with 16x16x32, where P^T is taken as-is from the lanes that
-// computed it. Loads of the next tile are in flight while the current one is computed.
+// computed it. Loads of the next tile are in flight while the current one is computed: for an
+// fp16 cache they are gfx950's direct global -> LDS loads into the second of two tile buffers
+// (one barrier per tile, no staging registers), for an 8-bit cache register loads that are
+// converted and written to the one padded buffer between two barriers.
 #include "prefill_body.hpp"
 
 namespace pa {
@@ -32,7 +35,7 @@ using pf::prefill_lds_bytes;
 
 template <int D, int BS, bool KV8, bool PREFIX>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p) {
-  __shared__ __align__(16) uint8_t lds[prefill_lds_bytes<D>()];
+  __shared__ __align__(16) uint8_t lds[prefill_lds_bytes<D, KV8, PREFIX>()];
   prefill_body<D, BS, KV8, PREFIX>(p, blockIdx.x, gridDim.x, lds);
 }
 
