@@ -72,15 +72,16 @@ constexpr size_t prefill_lds_bytes() {
 }
 
 // Physical 16-byte chunk slot of logical chunk c of tile row r in the unpadded buffers: c XOR
-// swz(r). Rows hold D / 8 chunks (16 for D = 128, 8 for D = 64). The operand reads then spread
-// over all 64 banks: a K read (16 lanes, rows r0 .. r0 + 15, one chunk each) meets 16 distinct
-// (row parity, slot) pairs, and a transposed V read (32 lanes, rows r0 .. r0 + 7, two adjacent
-// chunks each) 8 distinct chunk pairs per bank half; swz never flips bit 0 for rows that share
-// a pair's banks, so a pair stays a pair.
+// swz(r). Rows hold D / 8 chunks (16 for D = 128, 8 for D = 64). swz moves the rows that share
+// a bank range (every row at D = 128, every other row at D = 64) by distinct even slot counts,
+// so the two chunks a transposed V read takes from a row stay adjacent. With it both operand
+// reads ran without bank conflicts under the LDS counters (a K read 4 cycles per instruction,
+// a transposed V read 2); the same XOR with a bit-0 term for rows 8..15 left the K reads 2-way
+// conflicted.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  if constexpr (D == 128) return 2 * (r & 7);
+  else return 2 * ((r >> 1) & 3);
 }
 
 template <int D, int BS, bool KV8, bool PREFIX>
