@@ -24,14 +24,16 @@ constexpr int kRowPad = 16;
 static_assert(kPrefillRows == kWaves * kWaveRows, "rows per workgroup");
 
 // Maximum of x over the four 16-lane rows of the wave (lanes lr, lr + 16, lr + 32, lr + 48),
-// returned in every lane: two cross-row swaps, no LDS round trip.
+// returned in every lane: two cross-row swaps, no LDS round trip. The IEEE maximum (NaN
+// propagating; scores are never NaN for finite inputs) takes one v_maximum3 per swap, where
+// fmaxf would first quiet both swapped operands.
 __device__ __forceinline__ float row4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float y = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int NWORDS>
