@@ -439,17 +439,22 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
         }
       }
     };
-    if (tile_lo < tile_hi) dma(tile_lo, 0);
-    for (int i = tile_lo; i < tile_hi; ++i) {
-      const int buf = ((i - tile_lo) & 1) * kBuf;
+    // tile i sits in buffer (i - tile_lo) % 2; the loop takes two tiles per trip so that each
+    // buffer's LDS offsets are constants folded into the read instructions
+    auto step = [&](int i, int buf) {
       // this wave's loads of tile i have landed; after the barrier every wave's have, and every
       // wave is done with tile i - 1, whose buffer the next loads overwrite
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (i + 1 < tile_hi) dma(i + 1, kBuf - buf);
       const int tok0 = i * kTileTok;
-      if (tok0 > wpos_hi) continue;  // every token of the tile is in this wave's causal future
+      if (tok0 > wpos_hi) return;  // every token of the tile is in this wave's causal future
       compute(i, tok0 + kTileTok - 1 > wpos_lo, buf);
+    };
+    if (tile_lo < tile_hi) dma(tile_lo, 0);
+    for (int i = tile_lo; i < tile_hi; i += 2) {
+      step(i, 0);
+      if (i + 1 < tile_hi) step(i + 1, kBuf);
     }
   } else {
     if (tile_lo < tile_hi) issue(tile_lo);
