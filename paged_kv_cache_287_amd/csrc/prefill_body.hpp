@@ -113,7 +113,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   int wid = wid_in;
   const int per_xcd = nwg / kNumXcds;
   if (wid < per_xcd * kNumXcds) wid = (wid % kNumXcds) * per_xcd + wid / kNumXcds;
-  const int qt = wid % p.q_tiles;
+  const int qt = p.q_tiles - 1 - wid % p.q_tiles;  // later rows attend more: dispatched first
   const int kvh = (wid / p.q_tiles) % p.num_kv_heads;
   const int unit = wid / (p.q_tiles * p.num_kv_heads);
   // prefix pass: a unit is (group, slice of prefix_split tokens of its prefix)
@@ -186,11 +186,15 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
   const int wpos_hi =
       wrow0 < nrows ? (PREFIX ? base : base + (min(wrow0 + kWaveRows, nrows) - 1) / G) : -1;
 
-  float m[NT], l[NT];
+  // m: running maximum (the reference of l and o); nms and mlim: -m (0 while m is -inf) and
+  // m + kRescaleSlack, kept beside it so a tile without a rescale does not recompute them
+  float m[NT], l[NT], nms[NT], mlim[NT];
   f4 o[NT][MT], osum[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = kNegInf;
+    nms[nt] = 0.f;
+    mlim[nt] = kNegInf;
     l[nt] = 0.f;
     osum[nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -317,7 +321,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
       // the running max is the reference of l and o; it moves (with a rescale) only when a
       // score passes it by more than kRescaleSlack (wave-uniform decision), so most tiles skip
       // the rescale; probabilities stay below 2^kRescaleSlack
-      if (__builtin_amdgcn_ballot_w64(tm > m[nt] + kRescaleSlack) != 0) {
+      if (__builtin_amdgcn_ballot_w64(tm > mlim[nt]) != 0) {
         const float mn = fmaxf(m[nt], tm);
         const float alpha = fexp2(m[nt] - (mn == kNegInf ? 0.f : mn));
         l[nt] *= alpha;
@@ -325,13 +329,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int wid_in,
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
         m[nt] = mn;
+        nms[nt] = mn == kNegInf ? 0.f : -mn;
+        mlim[nt] = mn + kRescaleSlack;
       }
-      const float nms = m[nt] == kNegInf ? 0.f : -m[nt];
       float pw[4][4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) pw[s][ii] = fexp2(fmaf(sv[s][ii], kmul[s], nms));
+        for (int ii = 0; ii < 4; ++ii) pw[s][ii] = fexp2(fmaf(sv[s][ii], kmul[s], nms[nt]));
       if constexpr (KV8) {
         // the probabilities going to the matrix cores carry the V scale, so the row sums are
         // taken here; without it they come out of the P.V product (osum)
