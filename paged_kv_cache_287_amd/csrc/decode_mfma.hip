@@ -6,9 +6,10 @@
 // products against each K row and G weighted sums of each V row: 32 flop per KV byte at G = 32,
 // above what the VALU can sustain at HBM speed. Stacking the G query rows makes QK^T and PV
 // dense 16-row tiles, so they run on MFMA:
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = a 16-token K tile, loaded straight from the
-//     cache in the operand layout (lane l: token l%16, 8 consecutive dims of a 32-dim step);
-//     B = the query rows, held in registers. Lane l then owns query row l%16 and the scores of
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = a 16-token K tile in the operand layout
+//     (lane l: token l%16, 8 consecutive dims of a 32-dim step). An fp16 tile is loaded in
+//     whole rows and passes through a per-wave LDS tile into that layout; an 8-bit tile is
+//     loaded straight in it (16 bytes per lane, two steps). B = the query rows, in registers. Lane l then owns query row l%16 and the scores of
 //     tokens 4(l/16)..4(l/16)+3, so the online softmax (running max / sum per row, as in the
 //     FlashAttention paragraph of the same talk summary) needs only two cross-row exchanges.
 //   * O^T += V^T P^T with v_mfma_f32_16x16x16_f16: B = P^T is exactly the probabilities each
@@ -205,9 +206,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   // 16 rows a wave writes with one instruction fall on different banks
   constexpr int DP = D + 4;
   constexpr int kMergeFloats = kWaves * R * (DP + 2);
-  static_assert(kWaves * D * VTS * 2 <= kMergeFloats * 4, "staging fits the merge area");
-  __shared__ __align__(16) float smem[kMergeFloats];
+  // fp16 caches: a per-wave K tile ([token][row bytes + 32]) as well; K is loaded in whole
+  // rows and read back in the operand layout (see issue_tile)
+  constexpr bool KROW = !KV8;
+  constexpr int KRB = ROW_BYTES + 32;
+  constexpr int kVtBytes = kWaves * D * VTS * 2;
+  constexpr int kStageBytes = kVtBytes + (KROW ? kWaves * kTileTokens * KRB : 0);
+  constexpr int kSmemFloats = kStageBytes > kMergeFloats * 4 ? kStageBytes / 4 : kMergeFloats;
+  __shared__ __align__(16) float smem[kSmemFloats];
   _Float16* vt = reinterpret_cast<_Float16*>(smem) + wave * D * VTS;
+  uint8_t* kt = reinterpret_cast<uint8_t*>(smem) + kVtBytes + wave * kTileTokens * KRB;
 
   // K is loaded in the MFMA operand layout; V as TPL consecutive tokens of one 8-dim chunk per
   // lane, so that it is stored transposed with one TPL-half store per dim
@@ -216,14 +224,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   Chunk<4> ka[KL], kb[KL];
   Chunk<NWORDS> va[TPL], vb[TPL];
 
+  // K loads. fp16: LPR lanes cover one token row with 16 bytes each, RPI rows per instruction,
+  // so every instruction reads whole rows, and consume_tile moves them to the operand layout
+  // through LDS (loads straight into the operand layout read 64-byte row pieces per
+  // instruction, which cost ~10 % of the HBM rate). E4M3: straight into the operand layout
+  // (16 bytes per lane, two steps; the LDS round trip measured slower there).
+  constexpr int LPR = ROW_BYTES / 16;
+  constexpr int RPI = 64 / LPR;
+  static_assert(!KROW || KL * RPI == kTileTokens, "K loads cover the tile");
   auto issue_tile = [&](int i, Chunk<4>(&kc)[KL], Chunk<NWORDS>(&vc)[TPL]) {
-    const int id = block_of(i, lr);
-    const size_t off =
-        (size_t)id * blk_stride + (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES);
-    // load c holds the dims of steps c (fp16) or 2c and 2c + 1 (E4M3)
+    if constexpr (KROW) {
 #pragma unroll
-    for (int c = 0; c < KL; ++c)
-      kc[c] = load_chunk<4, true>(kbase + off + kdim(KV8 ? 2 * c : c) * ESZ);
+      for (int c = 0; c < KL; ++c) {
+        const int r = RPI * c + lane / LPR;
+        const int id = block_of(i, r);
+        const size_t off = (size_t)id * blk_stride +
+                           (size_t)(((woff + kTileTokens * i + r) % BS) * ROW_BYTES) +
+                           (size_t)(lane % LPR) * 16;
+        kc[c] = load_chunk<4, true>(kbase + off);
+      }
+    } else {
+      const int id = block_of(i, lr);
+      const size_t off =
+          (size_t)id * blk_stride + (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES);
+      // load c holds the dims of steps 2c and 2c + 1
+#pragma unroll
+      for (int c = 0; c < KL; ++c) kc[c] = load_chunk<4, true>(kbase + off + kdim(2 * c));
+    }
     // a lane's TPL tokens start at a multiple of TPL, so they share one block
     const int vid = block_of(i, TPL * vtg);
     const size_t voff = (size_t)vid * blk_stride +
@@ -262,9 +289,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       kmul *= last ? s_k : lane_value_of(my_ks, i, 4 * lq);
       vmul = last ? s_v : lane_value_of(my_vs, i, 4 * lq);
     }
+    // chunk c of lane (lr, lq): token lr's dims of step c (fp16) or steps 2c and 2c + 1 (E4M3)
     Chunk<4> kcs[KL];
+    if constexpr (KROW) {
 #pragma unroll
-    for (int c = 0; c < KL; ++c) kcs[c] = kc[c];
+      for (int c = 0; c < KL; ++c)
+        store_chunk(kt + (RPI * c + lane / LPR) * KRB + (lane % LPR) * 16, kc[c]);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < KL; ++c) kcs[c] = load_chunk<4>(kt + lr * KRB + kdim(c) * ESZ);
+      __builtin_amdgcn_wave_barrier();
+    } else {
+#pragma unroll
+      for (int c = 0; c < KL; ++c) kcs[c] = kc[c];
+    }
     if constexpr (APPEND && KV8) {
       // E4M3 append: the K codes of a token of the last block are re-encoded under its grown
       // scale, and stored back by the appending workgroup (positions before the new token);
