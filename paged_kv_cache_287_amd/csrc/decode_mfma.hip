@@ -13,10 +13,12 @@
 //     tokens 4(l/16)..4(l/16)+3, so the online softmax (running max / sum per row, as in the
 //     FlashAttention paragraph of the same talk summary) needs only two cross-row exchanges.
 //   * O^T += V^T P^T with v_mfma_f32_16x16x16_f16: B = P^T is exactly the probabilities each
-//     lane just computed (converted to fp16); A = V^T comes from a per-wave LDS tile stored
-//     transposed ([dim][token]): each lane loads 4 (or 2) consecutive tokens of one 8-dim chunk
-//     of V and stores them as one 8-byte write per dim, and the operand (4 tokens of one dim)
-//     is one 8-byte read. The accumulator lane l holds row l%16, so rescaling by the running
+//     lane just computed (converted to fp16); A = V^T comes from a per-wave LDS tile. fp16: the
+//     tile is stored transposed ([dim][token]): each lane loads 4 (or 2) consecutive tokens of
+//     one 8-dim chunk of V and stores them as one 8-byte write per dim, and the operand (4
+//     tokens of one dim) is one 8-byte read. E4M3: each lane loads 16 codes of one row (whole
+//     rows per load instruction), stores them converted as fp16 rows, and the operand comes
+//     out of gfx950's transposed LDS read (ds_read_b64_tr_b16). The accumulator lane l holds row l%16, so rescaling by the running
 //     max is lane-local.
 // Groups that are not a multiple of 16 fill 16- or 32-row tiles with padding rows of zero
 // queries: the matrix cores still do the dot products for less VALU time than the VALU kernel's
@@ -222,7 +224,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   const int vch = lane / (16 / TPL);   // 8-dim chunk
   const int vtg = lane % (16 / TPL);   // token group: tokens TPL vtg .. +TPL-1
   Chunk<4> ka[KL], kb[KL];
-  Chunk<NWORDS> va[TPL], vb[TPL];
+  // V loads. fp16: TPL consecutive tokens of one 8-dim chunk per lane (stored transposed). E4M3:
+  // 16 bytes (16 dims) of one token row per lane, VLPR lanes per row and VRPI rows per load
+  // instruction, so each instruction reads whole rows; they are stored as fp16 rows and the
+  // P.V operand is read back with the transposed LDS read.
+  constexpr int VLPR = ROW_BYTES / 16;
+  constexpr int VRPI = 64 / VLPR;
+  constexpr int VN = KV8 ? kTileTokens / VRPI : TPL;  // V loads per lane per tile
+  constexpr int VRS = D + 16;                           // row stride (halves) of the E4M3 V tile
+  static_assert(!KV8 || kTileTokens * VRS <= D * VTS, "row-major V tile fits the V^T tile");
+  typedef Chunk<KV8 ? 4 : NWORDS> VChunk;
+  VChunk va[VN], vb[VN];
 
   // K loads. fp16: LPR lanes cover one token row with 16 bytes each, RPI rows per instruction,
   // so every instruction reads whole rows, and consume_tile moves them to the operand layout
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
   constexpr int LPR = ROW_BYTES / 16;
   constexpr int RPI = 64 / LPR;
   static_assert(!KROW || KL * RPI == kTileTokens, "K loads cover the tile");
-  auto issue_tile = [&](int i, Chunk<4>(&kc)[KL], Chunk<NWORDS>(&vc)[TPL]) {
+  auto issue_tile = [&](int i, Chunk<4>(&kc)[KL], VChunk(&vc)[VN]) {
     if constexpr (KROW) {
 #pragma unroll
       for (int c = 0; c < KL; ++c) {
@@ -251,14 +263,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
       for (int c = 0; c < KL; ++c) kc[c] = load_chunk<4, true>(kbase + off + kdim(2 * c));
     }
-    // a lane's TPL tokens start at a multiple of TPL, so they share one block
-    const int vid = block_of(i, TPL * vtg);
-    const size_t voff = (size_t)vid * blk_stride +
-                        (size_t)(((woff + kTileTokens * i + TPL * vtg) % BS) * ROW_BYTES +
-                                 vch * LANE_BYTES);
+    if constexpr (KV8) {
 #pragma unroll
-    for (int u = 0; u < TPL; ++u)
-      vc[u] = load_chunk<NWORDS, true>(vbase + voff + (size_t)u * ROW_BYTES);
+      for (int c = 0; c < VN; ++c) {
+        const int r = VRPI * c + lane / VLPR;
+        const size_t voff = (size_t)block_of(i, r) * blk_stride +
+                            (size_t)(((woff + kTileTokens * i + r) % BS) * ROW_BYTES) +
+                            (size_t)(lane % VLPR) * 16;
+        vc[c] = load_chunk<4, true>(vbase + voff);
+      }
+    } else {
+      // a lane's TPL tokens start at a multiple of TPL, so they share one block
+      const int vid = block_of(i, TPL * vtg);
+      const size_t voff = (size_t)vid * blk_stride +
+                          (size_t)(((woff + kTileTokens * i + TPL * vtg) % BS) * ROW_BYTES +
+                                   vch * LANE_BYTES);
+#pragma unroll
+      for (int u = 0; u < TPL; ++u)
+        vc[u] = load_chunk<NWORDS, true>(vbase + voff + (size_t)u * ROW_BYTES);
+    }
   };
 
   // 8 elements of a chunk as fp16 (E4M3 codes decode exactly)
@@ -277,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     return __builtin_bit_cast(h8, w);
   };
 
-  auto consume_tile = [&](int i, const Chunk<4>(&kc)[KL], const Chunk<NWORDS>(&vc)[TPL],
+  auto consume_tile = [&](int i, const Chunk<4>(&kc)[KL], const VChunk(&vc)[VN],
                           bool masked) {
     const int tok0 = wbase + kTileTokens * i;
     // per-token multipliers: softmax scale (and the K / V block scales of an E4M3 cache) for
@@ -375,53 +398,87 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
       pB[nt] = h4{(_Float16)(pw[0] * vmul), (_Float16)(pw[1] * vmul), (_Float16)(pw[2] * vmul),
                   (_Float16)(pw[3] * vmul)};
     }
-    // stage V transposed as fp16: dim 8 vch + e gets this lane's TPL tokens in one store;
-    // tokens past the context are zeros so that stale or poisoned slots cannot reach the sums
-    h8 vv[TPL];
+    if constexpr (KV8) {
+      // E4M3: each lane's 16 codes of row r (token tok0 + r), converted, into the wave's
+      // row-major fp16 V tile; tokens past the context are zeros so that stale or poisoned
+      // slots cannot reach the sums
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      Chunk<NWORDS> vcs = vc[u];
-      if constexpr (APPEND && KV8) {
-        const int t = tok0 + TPL * vtg + u;
-        if (masked && rv && t >= last_start && t < newtok) {
+      for (int c = 0; c < VN; ++c) {
+        const int r = VRPI * c + lane / VLPR;
+        const int q = lane % VLPR;
+        const int t = tok0 + r;
+        Chunk<4> vcs = vc[c];
+        if constexpr (APPEND) {
+          if (masked && rv && t >= last_start && t < newtok) {
 #pragma unroll
-          for (int w = 0; w < NWORDS; ++w) vcs.w[w] = fp8_reencode_word(vcs.w[w], s_pv, s_v);
-          if (appender) {
-            const int vid = block_of(i, TPL * vtg);
-            const size_t voff = (size_t)vid * blk_stride +
-                                (size_t)(((woff + kTileTokens * i + TPL * vtg) % BS) * ROW_BYTES +
-                                         vch * LANE_BYTES);
-            store_chunk(p.v_cache_w + (size_t)kvh * TILE_BYTES + voff + (size_t)u * ROW_BYTES, vcs);
+            for (int w = 0; w < 4; ++w) vcs.w[w] = fp8_reencode_word(vcs.w[w], s_pv, s_v);
+            if (appender) {
+              const size_t voff = (size_t)block_of(i, r) * blk_stride +
+                                  (size_t)(((woff + kTileTokens * i + r) % BS) * ROW_BYTES);
+              store_chunk(p.v_cache_w + (size_t)kvh * TILE_BYTES + voff + (size_t)q * 16, vcs);
+            }
           }
+          if (masked && t == newtok) vcs = load_chunk<4>(s_new + ROW_BYTES + q * 16);
         }
-        if (masked && t == newtok) vcs = load_chunk<NWORDS>(s_new + ROW_BYTES + vch * LANE_BYTES);
+        Chunk<NWORDS> lo, hi;
+        lo.w[0] = vcs.w[0];
+        lo.w[1] = vcs.w[1];
+        hi.w[0] = vcs.w[2];
+        hi.w[1] = vcs.w[3];
+        h8 vlo = to_h8(lo), vhi = to_h8(hi);
+        if (masked && t >= L) vlo = vhi = h8{0, 0, 0, 0, 0, 0, 0, 0};
+        *reinterpret_cast<h8*>(vt + r * VRS + 16 * q) = vlo;
+        *reinterpret_cast<h8*>(vt + r * VRS + 16 * q + 8) = vhi;
       }
-      vv[u] = to_h8(vcs);
-      if constexpr (APPEND && !KV8) {
-        if (masked && tok0 + TPL * vtg + u == newtok)
-          vv[u] = *reinterpret_cast<const h8*>(s_new + ROW_BYTES + vch * 16);
+      __builtin_amdgcn_wave_barrier();
+      // O^T += V^T P^T; the A operand (dim 16 mt + lr, tokens 4 lq .. +3) comes out of the
+      // row-major tile with gfx950's transposed read: within each 16-lane group, lane lr passes
+      // 4 halves of the row of token 4 lq + lr / 4 and receives, as element e, half lr % 4 of
+      // the row passed by lane 4 e + lr / 4
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const s4 rd = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(
+            vt + (4 * lq + (lr >> 2)) * VRS + 16 * mt + 4 * (lr & 3)));
+        const h4 vA = __builtin_bit_cast(h4, rd);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vA, pB[nt], o[nt][mt], 0, 0, 0);
       }
-      if (masked && tok0 + TPL * vtg + u >= L) vv[u] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      // stage V transposed as fp16: dim 8 vch + e gets this lane's TPL tokens in one store;
+      // tokens past the context are zeros so that stale or poisoned slots cannot reach the sums
+      h8 vv[TPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      _Float16* dst = vt + (8 * vch + e) * VTS + TPL * vtg;
-      if constexpr (TPL == 4)
-        *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
-      else
-        *reinterpret_cast<h2v*>(dst) = h2v{vv[0][e], vv[1][e]};
-    }
-    __builtin_amdgcn_wave_barrier();
-    // O^T[dim][row] += V^T[dim][token] P^T[token][row], 16 dims at a time; the A operand (dim
-    // 16 mt + lr, tokens 4 lq .. +3) is one 8-byte read
+      for (int u = 0; u < TPL; ++u) {
+        vv[u] = to_h8(vc[u]);
+        if constexpr (APPEND) {
+          if (masked && tok0 + TPL * vtg + u == newtok)
+            vv[u] = *reinterpret_cast<const h8*>(s_new + ROW_BYTES + vch * 16);
+        }
+        if (masked && tok0 + TPL * vtg + u >= L) vv[u] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const h4 vA = *reinterpret_cast<const h4*>(vt + (16 * mt + lr) * VTS + 4 * lq);
+      for (int e = 0; e < 8; ++e) {
+        _Float16* dst = vt + (8 * vch + e) * VTS + TPL * vtg;
+        if constexpr (TPL == 4)
+          *reinterpret_cast<h4*>(dst) = h4{vv[0][e], vv[1][e], vv[2][e], vv[3][e]};
+        else
+          *reinterpret_cast<h2v*>(dst) = h2v{vv[0][e], vv[1][e]};
+      }
+      __builtin_amdgcn_wave_barrier();
+      // O^T[dim][row] += V^T[dim][token] P^T[token][row], 16 dims at a time; the A operand (dim
+      // 16 mt + lr, tokens 4 lq .. +3) is one 8-byte read
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vA, pB[nt], o[nt][mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        const h4 vA = *reinterpret_cast<const h4*>(vt + (16 * mt + lr) * VTS + 4 * lq);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vA, pB[nt], o[nt][mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   };
 
   // same double-buffered walk as the VALU kernel (unconditional loads in the steady state)
