@@ -450,6 +450,9 @@ def main():
     shared = case.group_start is not None if args.decode == "auto" else args.decode == "shared_prefix"
     if shared:
         assert case.group_start is not None, "this workload has no shared-prefix groups"
+        # the shared-prefix call has its own automatic size (its kernel choice can differ from
+        # pa_decode's): pass the requested value, 0 letting the library resolve it
+        part_tokens = args.partition_tokens
         ws_bytes = pa.shared_prefix_workspace_bytes(case.num_seqs, case.num_q_heads,
                                                     case.num_kv_heads, case.head_dim,
                                                     case.block_size, max_ctx, kvt, part_tokens)
@@ -711,14 +714,16 @@ def main():
                    "block_size": case.block_size, "kv_dtype": case.kv_dtype,
                    "step": ("copy_blocks(pairs) + decode_append (kv_write of 1 token/seq fused "
                             "into the decode launch)" if case.kv_dtype == "f16" else
-                            "copy_blocks(pairs) + decode_append (E4M3 kv_write of 1 token/seq, "
-                            "then decode, in one call)") if fused else
+                            "copy_blocks(pairs) + decode_append (E4M3 kv_write of 1 token/seq "
+                            "and the decode in one call)") if fused else
                            "copy_blocks(pairs) + kv_write(1 token/seq) + decode",
-                   "partition_tokens": part_tokens,
+                   "partition_tokens": part_tokens if part_tokens else "auto",
                    "decode": "shared_prefix" if shared else "plain",
                    "seq_order": "longest first" if use_order else "batch order",
                    "append": ("separate" if not fused else "fused" if case.kv_dtype == "f16"
-                              else "in the call (E4M3: append kernel, then decode kernel)")},
+                              else "in the call (E4M3: fused into the decode launch when one head "
+                                   "tile covers a KV head's query heads, else the append kernel "
+                                   "first)")},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attainable_read_gbs": attainable,
         "frac_of_attainable": None if attainable is None else value / attainable,

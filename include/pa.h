@@ -78,9 +78,11 @@ int pa_last_hip_error(void);
  * workgroup. partition_tokens = 0 asks for the automatic choice: one partition per sequence
  * (the smallest power of two >= max_context_len, at most 4096 and valid for the block size)
  * when that grid still has at least 512 workgroups (two per compute unit of a 256-CU gfx950;
- * 256 when G = Hq / Hkv >= 5, which runs on matrix-core tiles); otherwise the largest power of
+ * 256 when G = Hq / Hkv >= 4, which runs on matrix-core tiles); otherwise the largest power of
  * two in [256, 4096], at most max_context_len / 2, that still gives at least 1024 workgroups
- * (256 when G >= 5), else 256. Workgroups = num_seqs x Hkv x head tiles per KV head x partitions.
+ * (256 when G >= 4), else 256. Workgroups = num_seqs x Hkv x head tiles per KV head x partitions.
+ * (pa_decode_shared_prefix keeps G = 4 on the vector-ALU kernel and applies these rules with
+ * G >= 5 in place of G >= 4; pa_decode_shared_prefix_workspace_bytes resolves 0 that way.)
  * An explicit value must be a power of two in [256, 4096] with value <= 256 * block_size.
  * Returns 0 if the arguments are invalid.
  */
@@ -136,8 +138,9 @@ int pa_decode_workspace_reset(void* workspace, size_t workspace_bytes, void* str
  * split across context partitions of partition_tokens tokens that are merged exactly (talk
  * summary, FlashAttention paragraph). A sequence that fits one partition is finished by its
  * workgroup; split sequences are merged by a second small kernel on `stream` (groups of at most
- * four query heads per KV head, the vector-ALU kernel) or by the workgroup that finishes a
- * sequence's last partition (larger groups, the matrix-core kernel). L = 0 gives out = 0. For E4M3 caches each value is
+ * three query heads per KV head, the vector-ALU kernel, in batch order) or by the workgroup
+ * that finishes a sequence's last partition (larger groups, the matrix-core kernel, and any
+ * call with seq_order). L = 0 gives out = 0. For E4M3 caches each value is
  * decode(code) * scale[block, g] before use. context_lens counts every token to attend,
  * including one appended by this step's pa_kv_write.
  *
@@ -202,8 +205,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * workgroup covering position context_lens[b] - 1 takes that token's K/V from k_new/v_new[b]
  * instead of the cache, and one workgroup per (sequence, KV head) stores them at
  * slot_mapping[b]. E4M3 caches (whose append may rescale the block) are one launch too when one
- * head tile covers all query heads of a KV head (1 to 4 query heads per KV head on the vector
- * ALU; 5 to 32 in one matrix-core tile): the workgroup that reads the sequence's last block
+ * head tile covers all query heads of a KV head (1 to 3 query heads per KV head on the vector
+ * ALU; 4 to 32 in one matrix-core tile): the workgroup that reads the sequence's last block
  * applies the block-scale policy of pa_kv_write itself (the rows encoded under the updated
  * scale, the block's earlier codes re-encoded in registers when the scale grows) and stores
  * codes and scales. Other E4M3 head layouts (several workgroups per KV head) launch the append

@@ -31,17 +31,19 @@ int hip_status(hipError_t e) {
 }
 
 // Resolves the partition size (0 = automatic) and the grid's partition count; false if invalid.
+// `prefix`: shared-prefix decode, whose kernel choice (and so automatic size) can differ.
 bool resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int block_size,
-                       bool kv8, long long max_ctx, int partition_tokens, int* part_tokens,
-                       int* max_parts) {
+                       bool kv8, bool prefix, long long max_ctx, int partition_tokens,
+                       int* part_tokens, int* max_parts) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_ctx > (1LL << 30)) return false;
   const int group = num_q_heads / num_kv_heads;
-  const int units_per_seq = num_kv_heads * (group / pa::decode_rows(group, kv8));
+  const int units_per_seq = num_kv_heads * (group / pa::decode_rows(group, kv8, prefix));
   const int ctx = (int)(max_ctx > 0 ? max_ctx : 1);
   int pt = partition_tokens;
   if (pt == 0)
     pt = pa::auto_part_tokens(num_seqs, units_per_seq, ctx, block_size,
-                              pa::decode_target_units(group), pa::decode_single_units(group));
+                              pa::decode_target_units(group, prefix),
+                              pa::decode_single_units(group, prefix));
   if (!pa::valid_part_tokens(pt, block_size)) return false;
   const long long parts = pa::ceil_div(ctx, pt);
   if (parts > 65535) return false;
@@ -106,7 +108,7 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_
     return 0;
   int pt = 0, parts = 0;
   if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size,
-                         kv_dtype == PA_KV_FP8_E4M3, max_context_len,
+                         kv_dtype == PA_KV_FP8_E4M3, false, max_context_len,
                          partition_tokens, &pt, &parts))
     return 0;
   return pt;
@@ -121,7 +123,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (pt == 0) return 0;
   const int group = num_q_heads / num_kv_heads;
   const int hg_total =
-      num_kv_heads * (group / pa::decode_rows(group, kv_dtype == PA_KV_FP8_E4M3));
+      num_kv_heads * (group / pa::decode_rows(group, kv_dtype == PA_KV_FP8_E4M3, false));
   return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
                               (int)pa::ceil_div(max_context_len, pt)).total;
 }
@@ -187,11 +189,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (max_ctx > (long long)max_blocks_per_seq * block_size || max_ctx > (1LL << 30))
     return PA_ERR_INVALID_ARG;
   int part_tokens = 0, max_parts = 0;
-  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, fp8, max_ctx,
+  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, fp8, groups, max_ctx,
                          partition_tokens, &part_tokens, &max_parts))
     return partition_tokens != 0 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   const int group = num_q_heads / num_kv_heads;
-  const int gt = pa::decode_rows(group, fp8);
+  const int gt = pa::decode_rows(group, fp8, groups);
+  const bool mfma = pa::decode_uses_mfma(group, groups);
   // prefix blocks beyond the clamp (table width, on-chip id list, host bound on contexts) are
   // simply decoded per sequence, so the clamp never changes the result
   int prefix_blocks = 0, prefix_split = 0, prefix_slices = 0;
@@ -251,13 +254,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // first: 136 against 139.5 us). The matrix-core kernel's workgroups always merge in-kernel
   // (MQA at 64 x 2,048 tokens: 20.5 against 22.2 us with the separate merge). Both merges take
   // the partials in the same order with the same arithmetic.
-  p.deferred_merge =
-      ws.total > 0 && max_parts > 1 && !pa::decode_uses_mfma(group) && seq_order == nullptr;
+  p.deferred_merge = ws.total > 0 && max_parts > 1 && !mfma && seq_order == nullptr;
   // Shared prefixes with the vector-ALU decode: the prefix pass and the decode run in one launch
   // and every partial is merged by the merge kernel (shared-prefix step of 100 sequences: see
   // launch_shared_prefix_decode); with the matrix-core decode the prefix pass is a launch of its
   // own before it.
-  const bool one_launch = groups && prefix_blocks > 0 && !pa::decode_uses_mfma(group);
+  const bool one_launch = groups && prefix_blocks > 0 && !mfma;
   if (one_launch) p.deferred_merge = 2;
   const hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -332,9 +334,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       p.k_scale_w = app->k_scale_w;
       p.v_scale_w = app->v_scale_w;
       const hipError_t e =
-          pa::decode_uses_mfma(group)
-              ? pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, fp8, st)
-              : pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, fp8, st);
+          mfma ? pa::launch_decode_mfma_append(p, num_seqs, head_dim, block_size, gt, fp8, st)
+               : pa::launch_decode_append(p, num_seqs, head_dim, block_size, gt, fp8, st);
       if (e != hipSuccess || !p.deferred_merge) return hip_status(e);
       return hip_status(pa::launch_decode_merge(p, num_seqs, head_dim, block_size, st));
     }
@@ -350,7 +351,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     const int rc = hip_status(e);
     if (rc != PA_OK) return rc;
   }
-  const hipError_t e = pa::decode_uses_mfma(group)
+  const hipError_t e = mfma
                            ? pa::launch_decode_mfma(p, num_seqs, head_dim, block_size, gt, fp8, st)
                            : pa::launch_decode(p, num_seqs, head_dim, block_size, gt, fp8, st);
   if (e != hipSuccess || !p.deferred_merge) return hip_status(e);
@@ -428,13 +429,17 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
                                                int32_t num_kv_heads, int32_t head_dim,
                                                int32_t block_size, int32_t max_context_len,
                                                int32_t kv_dtype, int32_t partition_tokens) {
-  const int pt = pa_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                            block_size, max_context_len, kv_dtype,
-                                            partition_tokens);
-  if (pt == 0) return 0;
+  // the shared-prefix call's own partition policy (its kernel choice can differ from pa_decode's)
+  if (num_seqs <= 0 || num_q_heads <= 0 || !supported_head_dim(head_dim) ||
+      !supported_block_size(block_size) || !known_dtype(kv_dtype) || max_context_len <= 0)
+    return 0;
+  const bool kv8 = kv_dtype == PA_KV_FP8_E4M3;
+  int pt = 0, parts = 0;
+  if (!resolve_partition(num_seqs, num_q_heads, num_kv_heads, block_size, kv8, true,
+                         max_context_len, partition_tokens, &pt, &parts))
+    return 0;
   const int group = num_q_heads / num_kv_heads;
-  const int hg_total =
-      num_kv_heads * (group / pa::decode_rows(group, kv_dtype == PA_KV_FP8_E4M3));
+  const int hg_total = num_kv_heads * (group / pa::decode_rows(group, kv8, true));
   return pa::workspace_layout(num_seqs, num_q_heads, hg_total, head_dim,
                               (int)pa::ceil_div(max_context_len, pt) + pa::kMaxPrefixSlices).total;
 }

@@ -33,26 +33,30 @@ inline bool valid_part_tokens(int pt, int block_size) {
   return pt / kWaves <= kWave * block_size;
 }
 
-// Query heads per workgroup. Groups of 5 or more query heads per KV head use the matrix-core
-// kernel: 32 or 16 heads per tile when G is a multiple of 16; otherwise the group is cut into
-// the fewest tiles of at most 32 rows that divide it evenly (one tile up to G = 32), padded to 16
-// or 32 rows. A padded tile beats the VALU kernel there (GQA-8 at 64 x 2,048 tokens: 51 against
-// 76 us for fp16 KV, 45 against 64 us for E4M3), and the VALU alternative for 5, 6 or 7 heads
-// would read each K/V tile once per small head tile. Groups of 1 to 4 heads (and odd groups
-// above 32) use the VALU kernel with the largest compiled tile dividing G: 8, 4, 3, 2 or 1 query
-// heads for fp16 caches, at most 4 for E4M3 ones (their lanes hold 16 elements of a token, and
-// 8 heads of partial outputs no longer fit the register file). At G = 4 the padded tile was
-// measured as fast as the VALU kernel for fp16 and slower for E4M3.
-inline int mfma_rows(int group) {
-  if (group < 5) return 0;
+// Query heads per workgroup. Groups of 4 or more query heads per KV head (5 or more in
+// shared-prefix decode, `prefix`) use the matrix-core kernel: 32 or 16 heads per tile when G is
+// a multiple of 16; otherwise the group is cut into the fewest tiles of at most 32 rows that
+// divide it evenly (one tile up to G = 32), padded to 16 or 32 rows. A padded tile beats the
+// VALU kernel there (GQA-8 at 64 x 2,048 tokens: 51 against 76 us for fp16 KV, 45 against 64 us
+// for E4M3; GQA-4, 16 rows for 4 heads: 8B shape 161.5 against 165.5-168 us per call, 64 x 2,048
+// tokens with E4M3 47.5 against 57-63 us), and the VALU alternative for 5, 6 or 7 heads would
+// read each K/V tile once per small head tile. Groups of 1 to 3 heads (and odd groups above 32)
+// use the VALU kernel with the largest compiled tile dividing G: 8, 4, 3, 2 or 1 query heads for
+// fp16 caches, at most 4 for E4M3 ones (their lanes hold 16 elements of a token, and 8 heads of
+// partial outputs no longer fit the register file); at G = 2 the padded tile measured no faster.
+// Shared-prefix decode keeps G = 4 on the VALU kernel, whose launch also runs the prefix pass
+// (the matrix-core decode takes the prefix pass as a launch of its own: 48.6 against 42.4 us
+// for the shared-prefix step of 100 sequences).
+inline int mfma_rows(int group, bool prefix) {
+  if (group < (prefix ? 5 : 4)) return 0;
   if (group % 32 == 0) return 32;
   if (group % 16 == 0) return 16;
   const int tiles = (group + 31) / 32;
   return group % tiles == 0 ? group / tiles : 0;
 }
-inline bool decode_uses_mfma(int group) { return mfma_rows(group) > 0; }
-inline int decode_rows(int group, bool kv8) {
-  if (decode_uses_mfma(group)) return mfma_rows(group);
+inline bool decode_uses_mfma(int group, bool prefix) { return mfma_rows(group, prefix) > 0; }
+inline int decode_rows(int group, bool kv8, bool prefix) {
+  if (decode_uses_mfma(group, prefix)) return mfma_rows(group, prefix);
   for (int gt : {8, 4, 3, 2, 1})
     if (group % gt == 0 && !(kv8 && gt > 4)) return gt;
   return 1;
@@ -75,11 +79,11 @@ inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 //     whole long sequence while the rest of the GPU idles. The target is four workgroups per CU
 //     for the VALU kernel and one for the matrix-core kernel, whose 16- or 32-row workgroups
 //     are heavier and whose merges cost more per partition (measured best on MI355X).
-inline long long decode_target_units(int group) {
-  return decode_uses_mfma(group) ? (long long)kNumCUs : 4LL * kNumCUs;
+inline long long decode_target_units(int group, bool prefix) {
+  return decode_uses_mfma(group, prefix) ? (long long)kNumCUs : 4LL * kNumCUs;
 }
-inline long long decode_single_units(int group) {
-  return decode_uses_mfma(group) ? (long long)kNumCUs : 2LL * kNumCUs;
+inline long long decode_single_units(int group, bool prefix) {
+  return decode_uses_mfma(group, prefix) ? (long long)kNumCUs : 2LL * kNumCUs;
 }
 inline int auto_part_tokens(int num_seqs, int units_per_seq, int max_context_len, int block_size,
                             long long target_units, long long single_units) {

@@ -54,20 +54,28 @@ def test_partition_choice_and_workspace_size():
     assert pa.decode_partition_tokens(64, 32, 8, 128, 16, 4096) == 4096
     assert pa.decode_partition_tokens(64, 32, 32, 128, 16, 2048) == 2048
     assert pa.decode_partition_tokens(100, 32, 8, 128, 16, 1409) == 2048
-    # too few workgroups for one partition each: 32 seqs x 8 KV heads = 256 < 512, so
-    # partitions of at most half the longest context with >= 4 workgroups per CU
-    assert pa.decode_partition_tokens(32, 32, 8, 128, 16, 4096) == 1024
+    # too few workgroups for one partition each on the vector-ALU kernel (G = 3): 32 seqs x 8 KV
+    # heads = 256 < 512, so partitions of at most half the longest context with >= 4 workgroups
+    # per CU; the matrix-core kernel (G = 4) keeps one partition with one workgroup per CU
+    assert pa.decode_partition_tokens(32, 24, 8, 128, 16, 4096) == 1024
+    assert pa.decode_partition_tokens(32, 32, 8, 128, 16, 4096) == 4096
     # longest context beyond one partition: 128 seqs of up to 7503 tokens -> 2048
     assert pa.decode_partition_tokens(128, 32, 8, 128, 16, 7503) == 2048
     # block size 8 caps a partition at 2048 tokens, so 4096-token contexts split
     assert pa.decode_partition_tokens(64, 32, 8, 128, 8, 4096) == 2048
-    # matrix-core decode (G >= 5) aims at one workgroup per CU: MQA 64 x 2048 -> 4 partitions
+    # matrix-core decode (G >= 4) aims at one workgroup per CU: MQA 64 x 2048 -> 4 partitions
     assert pa.decode_partition_tokens(64, 32, 1, 128, 16, 2048) == 512
     # padded matrix-core tile, 64 seqs x 4 KV heads = 256 workgroups: one partition each
     assert pa.decode_partition_tokens(64, 32, 4, 128, 16, 2048) == 2048
     # few sequences: smaller partitions for parallelism, down to 256
     assert pa.decode_partition_tokens(1, 32, 8, 128, 16, 4096) == 256
-    assert pa.decode_partition_tokens(4, 32, 8, 128, 16, 32768) == 1024
+    assert pa.decode_partition_tokens(4, 24, 8, 128, 16, 32768) == 1024
+    assert pa.decode_partition_tokens(4, 32, 8, 128, 16, 32768) == 4096
+    # shared-prefix decode keeps G = 4 on the vector-ALU kernel, and its workspace size resolves
+    # an automatic partition size with that kernel's rule (1024 here, not pa_decode's 4096)
+    auto = pa.shared_prefix_workspace_bytes(32, 32, 8, 128, 16, 4096, 0, 0)
+    assert auto == pa.shared_prefix_workspace_bytes(32, 32, 8, 128, 16, 4096, 0, 1024)
+    assert auto > pa.shared_prefix_workspace_bytes(32, 32, 8, 128, 16, 4096, 0, 4096) > 0
     # block size 8 caps a partition at 8 * 64 * 4 = 2048 tokens
     assert pa.decode_partition_tokens(512, 32, 8, 128, 8, 16384) == 2048
     # explicit sizes are validated

@@ -238,6 +238,7 @@ def test_large_groups_relabelling_and_determinism():
 
 # ---- dispatch order: longest contexts first --------------------------------------------------
 @pytest.mark.parametrize("hq,hkv,kv,pt", [(32, 8, "f16", 256), (32, 8, "f16", 0), (16, 16, "f16", 512),
+                                          (24, 8, "f16", 256), (24, 8, "fp8_e4m3", 256),
                                           (32, 1, "f16", 256), (32, 4, "f16", 0),
                                           (32, 8, "fp8_e4m3", 256), (32, 1, "fp8_e4m3", 0)])
 def test_seq_order_gives_bit_identical_outputs(hq, hkv, kv, pt):

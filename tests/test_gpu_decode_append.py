@@ -135,23 +135,24 @@ def test_append_head_groupings(hq, hkv):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq", [8, 64])
+@pytest.mark.parametrize("hq", [6, 8, 64])
 def test_append_fp8_cache(d, hq):
-    """E4M3 caches: the block-scale append fused into the vector-ALU (G 4) and matrix-core (G 32)
-    decode launches."""
+    """E4M3 caches: the block-scale append fused into the vector-ALU (G 3) and matrix-core (G 4,
+    one padded 16-row tile; G 32) decode launches."""
     case = workloads.random_case(740 + d + hq, LENS, hq, 2, d, 16, kv_dtype="fp8_e4m3",
                                  name=f"append_fp8_d{d}_{hq}q")
     check_case(case, 741 + d, skip=(3,), what=f"append E4M3 D{d} {hq}q")
 
 
-@pytest.mark.parametrize("hq", [8, 16, 64])
+@pytest.mark.parametrize("hq", [6, 8, 16, 64])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [8, 16, 32, 64])
 @pytest.mark.parametrize("partition_tokens", [0, 256])
 def test_append_fp8_fused_block_sizes(hq, d, bs, partition_tokens):
     """The fused E4M3 append at every block size (a last block spanning several tiles or two
     waves' ranges at BS 64; 8-byte lanes at D 64, BS 8), with whole and split sequences, on the
-    vector-ALU kernel (G 4), a padded 16-row matrix-core tile (G 8) and two 16-row tiles (G 32):
+    vector-ALU kernel (G 3), padded 16-row matrix-core tiles (G 4 and 8) and two 16-row tiles
+    (G 32):
     codes and scales equal the oracle's append, the output the oracle's decode, and both are
     bit-identical to the append kernel followed by the decode."""
     case = workloads.random_case(780 + d + bs + hq, LENS, hq, 2, d, bs, kv_dtype="fp8_e4m3",
@@ -165,8 +166,8 @@ def test_append_fp8_fused_block_sizes(hq, d, bs, partition_tokens):
                                     (35, 1), (64, 1)])
 def test_append_fp8_scale_kept_or_grown(gain, hq, hkv):
     """New rows 100 times smaller than the cached ones keep every block's scale (no re-encoding);
-    8 times larger ones grow it (every earlier code of the last block re-encoded). G = 1, 2, 3, 4
-    (vector-ALU) and 8, 12, 32 (one matrix-core workgroup per KV head) take the fused launch;
+    8 times larger ones grow it (every earlier code of the last block re-encoded). G = 1, 2, 3
+    (vector-ALU) and 4, 8, 12, 32 (one matrix-core workgroup per KV head) take the fused launch;
     G = 35 (one-head VALU tiles) and 64 (two 32-row tiles), with several workgroups per KV head,
     take the append kernel and then the decode."""
     case = workloads.random_case(800 + hq + hkv, LENS, hq, hkv, 128, 16, kv_dtype="fp8_e4m3",
@@ -273,14 +274,15 @@ def test_append_full_size_workloads(name):
 
 
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 1)])
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (8, 2), (32, 1)])
 def test_append_captured_in_a_graph_replays_exactly(hq, hkv, kv):
     """pa_decode_append captured once into a HIP graph (256-token partitions, so every replay
     also runs the cross-partition merge and returns the arrival counters to zero) and replayed
     several times with eager work between the replays: every replay matches the eager call bit
     for bit. The workspace is passed in, so nothing inside the capture allocates or clears.
     Appending the same rows again leaves an E4M3 block's scale and codes as they are, so the
-    replays of the fused E4M3 append (vector ALU at G 4, matrix cores at G 32) repeat too."""
+    replays of the fused E4M3 append (vector ALU at G 3, matrix cores at G 4 and 32) repeat
+    too."""
     import paged_kv_cache_287_amd as pa
 
     case = workloads.random_case(820 + hq, LENS, hq, hkv, 128, 16, kv_dtype=kv,

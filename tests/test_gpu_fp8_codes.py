@@ -11,8 +11,9 @@ out. Each of the 254 finite codes appears in a V row, under V scales 1 and 2^-3 
 are exact in fp16), and the output is compared value for value with the oracle's E4M3 table
 (+0 and -0 compare equal: the kernels add the product to a +0 accumulator).
 
-Covered: the vector-ALU decode kernel (G = 1 and 4 query heads per KV head), the matrix-core
-decode kernel (G = 8 in a padded 16-row tile, G = 32) and the prefill kernel (one-token chunks),
+Covered: the vector-ALU decode kernel (G = 1 and 3 query heads per KV head), the matrix-core
+decode kernel (G = 4 and 8 in a padded 16-row tile, G = 32) and the prefill kernel (one-token
+chunks),
 for D 64 / 128 and block sizes 8 / 16.
 """
 import numpy as np
@@ -72,7 +73,7 @@ def check(got: torch.Tensor, want: np.ndarray, what: str):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [8, 16])
-@pytest.mark.parametrize("g", [1, 4, 8, 32])
+@pytest.mark.parametrize("g", [1, 3, 4, 8, 32])
 @pytest.mark.parametrize("v_scale_value", [1.0, 0.125])
 def test_decode_dequantizes_every_code(d, bs, g, v_scale_value):
     import paged_kv_cache_287_amd as pa
