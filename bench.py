@@ -30,12 +30,25 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of an MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_8b_traffic.json")
+# sources of the 8B workload's decode kernel (GQA-4: the matrix-core kernel), whose measured HBM
+# traffic profiles/decode_8b_traffic.json holds while they are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_287_amd", "csrc", f)
-                  for f in ("decode.hip", "decode_common.hpp", "pa_internal.hpp")]
+                  for f in ("decode_mfma.hip", "decode_common.hpp", "fp8_append.hpp",
+                            "pa_internal.hpp")]
 
 
 def progress(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_kernel_family(group: int, shared: bool) -> str:
+    """Which decode kernel the library runs for G query heads per KV head (the library's rule:
+    matrix-core tiles from G = 4, from G = 5 in shared-prefix decode, when the group fits one
+    tile of at most 32 rows or splits evenly into such tiles; the vector-ALU kernel otherwise)."""
+    if group >= (5 if shared else 4):
+        if group % 16 == 0 or group % (-(-group // 32)) == 0:
+            return "matrix-core decode kernel"
+    return "vector-ALU decode kernel"
 
 
 def kernel_source_hash() -> str:
@@ -670,6 +683,7 @@ def main():
     if fused:  # the new rows: read from k_new / v_new and written to the cache
         call_bytes += 2 * 2 * int(np.asarray(nk).nbytes)
     achieved = call_bytes / (avg_call_ms * 1e-3) / 1e9
+    kfam = decode_kernel_family(case.num_q_heads // case.num_kv_heads, shared)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
@@ -677,13 +691,13 @@ def main():
             traffic = tr.get("hbm_bytes_per_call")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": ("pa_decode_shared_prefix_append (prefix pass prefill_kernel<PREFIX> + "
-                           "decode partition kernel with the step's append fused)") if shared and fused else
-                          ("pa_decode_shared_prefix (prefix pass prefill_kernel<PREFIX> + decode "
-                           "partition kernel, merge fused)") if shared else
-                          ("pa_decode_append (decode partition kernel with the step's append and "
-                           "the cross-partition merge fused)") if fused else
-                          "pa_decode (decode partition kernel, cross-partition merge fused)",
+                "kernel": ((f"pa_decode_shared_prefix_append (prefix pass prefill_kernel<PREFIX> + "
+                            f"{kfam} with the step's append fused)") if shared and fused else
+                           (f"pa_decode_shared_prefix (prefix pass prefill_kernel<PREFIX> + "
+                            f"{kfam}, merge fused)") if shared else
+                           (f"pa_decode_append ({kfam} with the step's append and the "
+                            "cross-partition merge fused)") if fused else
+                           f"pa_decode ({kfam}, cross-partition merge fused)"),
                 "algorithmic_bytes_per_call": call_bytes, "avg_call_us": avg_call_ms * 1e3,
                 "timing": "HIP events around the timed back-to-back calls of the entry point "
                           "named in kernel"}
