@@ -44,7 +44,8 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int D, int BS, int NT, bool KV8, bool APPEND>
+// KVNT: non-temporal K/V loads (large calls) or cacheable ones (calls whose KV fits the caches)
+template <int D, int BS, int NT, bool KV8, bool APPEND, bool KVNT>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p) {
   constexpr int R = 16 * NT;         // query rows of one KV head handled by a workgroup
   constexpr int TPL = D / 32;        // consecutive V tokens a lane loads (one 8-dim chunk)
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         const size_t off = (size_t)id * blk_stride +
                            (size_t)(((woff + kTileTokens * i + r) % BS) * ROW_BYTES) +
                            (size_t)(lane % LPR) * 16;
-        kc[c] = load_chunk<4, true>(kbase + off);
+        kc[c] = load_chunk<4, KVNT>(kbase + off);
       }
     } else {
       const int id = block_of(i, lr);
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
           (size_t)id * blk_stride + (size_t)(((woff + kTileTokens * i + lr) % BS) * ROW_BYTES);
       // load c holds the dims of steps 2c and 2c + 1
 #pragma unroll
-      for (int c = 0; c < KL; ++c) kc[c] = load_chunk<4, true>(kbase + off + kdim(2 * c));
+      for (int c = 0; c < KL; ++c) kc[c] = load_chunk<4, KVNT>(kbase + off + kdim(2 * c));
     }
     if constexpr (KV8) {
 #pragma unroll
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         const size_t voff = (size_t)block_of(i, r) * blk_stride +
                             (size_t)(((woff + kTileTokens * i + r) % BS) * ROW_BYTES) +
                             (size_t)(lane % VLPR) * 16;
-        vc[c] = load_chunk<4, true>(vbase + voff);
+        vc[c] = load_chunk<4, KVNT>(vbase + voff);
       }
     } else {
       // a lane's TPL tokens start at a multiple of TPL, so they share one block
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                                    vch * LANE_BYTES);
 #pragma unroll
       for (int u = 0; u < TPL; ++u)
-        vc[u] = load_chunk<NWORDS, true>(vbase + voff + (size_t)u * ROW_BYTES);
+        vc[u] = load_chunk<NWORDS, KVNT>(vbase + voff + (size_t)u * ROW_BYTES);
     }
   };
 
@@ -674,7 +675,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 template <int D, int BS, int NT, bool KV8, bool APPEND>
 hipError_t launch_one(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.head_groups, num_seqs, p.max_parts);
-  decode_mfma_kernel<D, BS, NT, KV8, APPEND><<<grid, kThreads, 0, stream>>>(p);
+  if (p.kv_cached)
+    decode_mfma_kernel<D, BS, NT, KV8, APPEND, false><<<grid, kThreads, 0, stream>>>(p);
+  else
+    decode_mfma_kernel<D, BS, NT, KV8, APPEND, true><<<grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

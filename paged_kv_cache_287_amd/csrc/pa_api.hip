@@ -255,6 +255,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // (MQA at 64 x 2,048 tokens: 20.5 against 22.2 us with the separate merge). Both merges take
   // the partials in the same order with the same arithmetic.
   p.deferred_merge = ws.total > 0 && max_parts > 1 && !mfma && seq_order == nullptr;
+  // Matrix-core decode: cacheable K/V loads when the call reads at most 256 MiB of KV (the
+  // Infinity Cache's size; bounded by num_seqs x max_context_len), non-temporal loads above.
+  p.kv_cached = (long long)num_seqs * max_ctx * num_kv_heads * head_dim * (fp8 ? 1 : 2) * 2 <=
+                (256LL << 20);
   // Shared prefixes with the vector-ALU decode: the prefix pass and the decode run in one launch
   // and every partial is merged by the merge kernel (shared-prefix step of 100 sequences: see
   // launch_shared_prefix_decode); with the matrix-core decode the prefix pass is a launch of its

@@ -177,6 +177,7 @@ struct DecodeParams {
   // 2: as 1, and sequences with prefix partials publish theirs too (the prefix pass runs in the
   // same launch, so nothing may read its partials before the merge kernel)
   int32_t deferred_merge;
+  int32_t kv_cached;  // matrix-core decode: cacheable (1) or non-temporal (0) K/V loads
   // Fused append (pa_decode_append): the new token of sequence b sits at position
   // context_lens[b] - 1; its rows k_new/v_new[b] ([S, Hkv, D] fp16) are attended in place of
   // the cache's and stored at slot_mapping[b] (< 0: no append). Null for plain decode. With an
