@@ -237,24 +237,33 @@ def sq(args) -> None:
     roof = b.get("roofline", {})
     per_kib = roof.get("algorithmic_bytes_per_call")
     flops = b.get("flops_per_call")
-    for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
-        if g(name) is None:
+    # SQ_INSTS_VALU counts the matrix-core instructions too (the prefill kernel's tile loop holds
+    # 122 vector-ALU and 68 MFMA instructions in its assembly, and the counter reads ~205 per
+    # tile), so the vector-ALU rows below take SQ_INSTS_VALU - SQ_INSTS_MFMA.
+    valu_only = None
+    if g("SQ_INSTS_VALU") is not None:
+        valu_only = g("SQ_INSTS_VALU") - g("SQ_INSTS_MFMA", 0)
+    rows = [("VALU excl. MFMA", valu_only, "(SQ_INSTS_VALU - SQ_INSTS_MFMA)")]
+    rows += [(name[9:], g(name), name)
+             for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU")]
+    for label, val, defn in rows:
+        if val is None:
             continue
         if waves:
-            out.append(f"| {name[9:]} per wave | {g(name) / waves:.0f} | {name} / SQ_WAVES |")
+            out.append(f"| {label} per wave | {val / waves:.0f} | {defn} / SQ_WAVES |")
         if flops:
-            out.append(f"| {name[9:]} per GFLOP | {g(name) / (flops / 1e9):.0f} | "
-                       f"{name} / algorithmic GFLOP per call |")
+            out.append(f"| {label} per GFLOP | {val / (flops / 1e9):.0f} | "
+                       f"{defn} / algorithmic GFLOP per call |")
         elif per_kib:
-            out.append(f"| {name[9:]} per KiB | {g(name) / (per_kib / 1024):.1f} | "
-                       f"{name} / algorithmic KiB per call |")
+            out.append(f"| {label} per KiB | {val / (per_kib / 1024):.1f} | "
+                       f"{defn} / algorithmic KiB per call |")
     if cyc and g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
         out.append(f"| matrix-core busy | {g('SQ_VALU_MFMA_BUSY_CYCLES') / (N_SIMDS * cyc):.3f} | "
                    f"SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) |")
-    if cyc and g("SQ_INSTS_VALU") is not None:
+    if cyc and valu_only is not None:
         out.append(f"| vector-ALU issue share | "
-                   f"{VALU_CYCLES * g('SQ_INSTS_VALU') / (N_SIMDS * cyc):.3f} | "
-                   f"4 cycles x SQ_INSTS_VALU / (1024 SIMDs x cycles) |")
+                   f"{VALU_CYCLES * valu_only / (N_SIMDS * cyc):.3f} | "
+                   f"4 cycles x (SQ_INSTS_VALU - SQ_INSTS_MFMA) / (1024 SIMDs x cycles) |")
     if cyc and g("SQ_LDS_IDX_ACTIVE"):
         out.append(f"| LDS active | {g('SQ_LDS_IDX_ACTIVE') / (N_CUS * cyc):.3f} | "
                    f"SQ_LDS_IDX_ACTIVE / (256 CUs x cycles) |")
