@@ -67,6 +67,7 @@ def parse():
                          "calls after the GPU idled run ~6 %% slower on MI355X)")
     ap.add_argument("--workload", default="8b",
                     help="8b | tiny | prefix | sweep_bs{8,16,32,64} | variant_hkv{32,8,1}_{f16,fp8_e4m3}"
+                         " | shard_kvhead (one GPU's share of 8b under 8-way KV-head sharding)"
                          " | prefill_8b (chunked prefill: its own JSON line in TFLOP/s)")
     ap.add_argument("--flushed-calls", type=int, default=50,
                     help="pa_decode calls timed one by one after evicting the caches")

@@ -1,7 +1,7 @@
 """GPU parity of pa_decode against the float64 oracle (through the C ABI via the binding).
 
-Covers every workload shape (tiny; 8B-shaped at full size; shared prefix; block-size sweep;
-MHA / GQA / MQA in fp16 and E4M3), small cases that span several tiles, waves and partitions
+Covers every workload shape (tiny; 8B-shaped at full size and its KV-head shard; shared prefix;
+block-size sweep; MHA / GQA / MQA in fp16 and E4M3), small cases that span several tiles, waves and partitions
 with ragged tails, and the bit-exact properties: physical relabelling, run-to-run
 determinism, block-size invariance of the arithmetic, L = 1 returning v exactly, L = 0
 returning zeros, and NaN-poisoned unattended slots having no effect.
@@ -47,6 +47,12 @@ def test_8b_workload_split_in_two_partitions():
     torch.cuda.synchronize()
     seqs = [0, 9, 18, 27, 36, 45, 54, 63]
     assert_attention_close(out[seqs], oracle_decode(case, seqs=seqs), "8b, 2048-token partitions")
+
+
+def test_kv_head_shard_workload_full_size():
+    """One GPU's share of the 8B shape under 8-way KV-head sharding (Hq 4, Hkv 1, 64 x 4096
+    tokens) in the benchmark's launch configuration, every sequence against the oracle."""
+    run_case(gen(workloads.kv_head_shard))
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32, 64])

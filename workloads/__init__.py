@@ -8,6 +8,7 @@ from .configs import (  # noqa: F401
     StepInputs,
     by_name,
     eight_b,
+    kv_head_shard,
     normal_f16,
     prefill_8b,
     prefill_case,

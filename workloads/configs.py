@@ -35,7 +35,7 @@ F16_NAN = np.uint16(0x7E00)
 
 # fixed seeds per workload
 SEEDS = {"tiny": 1, "8b": 2, "prefix": 3, "prefix_fork": 31, "sweep": 4, "variants": 5,
-         "prefill": 6}
+         "prefill": 6, "shard_kvhead": 7}
 
 
 @dataclass
@@ -357,6 +357,14 @@ def variant(num_kv_heads: int, kv_dtype: str = "f16", num_seqs: int = 64, ctx: i
     return case
 
 
+def kv_head_shard(num_seqs: int = 64, ctx: int = 4096) -> DecodeCase:
+    """One GPU's share of the 8B-shaped decode under 8-way KV-head sharding: the same 64 x 4096
+    tokens, BS 16, D 128, fp16, but one KV head and its 4 query heads (Hq 4, Hkv 1), so the call
+    reads 1/8 of the 8B workload's KV."""
+    return random_case(SEEDS["shard_kvhead"], [ctx] * num_seqs, 4, 1, 128, 16,
+                       name="shard_kvhead")
+
+
 # --------------------------------------------------------------------------------------------
 # Prefill (a chunk of new tokens per sequence attending causally over its cache)
 # --------------------------------------------------------------------------------------------
@@ -408,7 +416,7 @@ def prefill_8b(num_seqs: int = 16, ctx: int = 4096, chunk: int = 1024) -> Prefil
 
 def by_name(name: str) -> DecodeCase:
     """Lookup used by the benchmark and tests: tiny, 8b, prefix, prefix_fork, sweep_bs{8,16,32,64},
-    variant_hkv{32,8,1}_{f16,fp8_e4m3}."""
+    variant_hkv{32,8,1}_{f16,fp8_e4m3}, shard_kvhead."""
     if name == "tiny":
         return tiny()
     if name == "8b":
@@ -419,6 +427,8 @@ def by_name(name: str) -> DecodeCase:
         return shared_prefix(True)
     if name.startswith("sweep_bs"):
         return sweep(int(name[len("sweep_bs"):]))
+    if name == "shard_kvhead":
+        return kv_head_shard()
     if name.startswith("variant_hkv"):
         rest = name[len("variant_hkv"):]
         hkv, dt = rest.split("_", 1)
