@@ -512,8 +512,10 @@ def main():
                          max_context_len=max_ctx, partition_tokens=part_tokens, workspace=ws,
                          seq_order=g_order)
 
+    has_pairs = g_pairs.shape[0] > 0
+
     def step():
-        if g_pairs.shape[0]:
+        if has_pairs:
             pa.pa_copy_blocks(kc, vc, g_pairs, k_scale=ks, v_scale=vs)
         if not fused:
             pa.pa_kv_write(g_nk, g_nv, kc, vc, g_slots, k_scale=ks, v_scale=vs)
