@@ -25,7 +25,7 @@
 // dot2 chains (GQA-8 at 64 x 2,048 tokens: 51 us against 76 us for fp16 KV, 45 against 64 for
 // E4M3; GQA-4 in one 16-row tile, 4 rows real: the 8B shape 161.5 against 165.5-168 us, and
 // 64 x 2,048 tokens with E4M3 47.5 against 57-63 us).
-// Everything else (partitioning, block-id walk, double-buffered non-temporal loads, fp8 scales,
+// Everything else (partitioning, block-id walk, double-buffered loads, fp8 scales,
 // merge through LDS, partial publish / last-arrival merge, the fused append) follows the VALU
 // kernel. For the fused append the new K/V rows of the workgroup's (sequence, KV head) are
 // staged once in LDS (512 bytes at D 128), where the lanes of position L - 1 read them in the
@@ -44,7 +44,8 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// KVNT: non-temporal K/V loads (large calls) or cacheable ones (calls whose KV fits the caches)
+// KVNT: non-temporal K/V loads (large calls, as in the VALU kernel) or cacheable ones (calls of
+// at most 256 MiB of KV, which fit the Infinity Cache: measured faster there, slower above)
 template <int D, int BS, int NT, bool KV8, bool APPEND, bool KVNT>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p) {
   constexpr int R = 16 * NT;         // query rows of one KV head handled by a workgroup
