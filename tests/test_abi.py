@@ -237,6 +237,24 @@ def test_binding_rejects_host_tensors_before_calling_the_library():
                      torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, dtype=torch.int32), 0.1)
 
 
+def test_binding_argument_checks_name_the_problem():
+    """The per-tensor check takes one combined test on the common path; a failing tensor still
+    gets the specific error (type, dtype, rank, layout, then placement)."""
+    import torch
+
+    good = torch.zeros(2, 4, 128, dtype=torch.float16)
+    with pytest.raises(TypeError, match="must be a torch.Tensor"):
+        pa._check([1, 2], "q", (torch.float16,), 3)
+    with pytest.raises(TypeError, match="has dtype"):
+        pa._check(good.float(), "q", (torch.float16,), 3)
+    with pytest.raises(ValueError, match="dimensions"):
+        pa._check(good[0], "q", (torch.float16,), 3)
+    with pytest.raises(ValueError, match="contiguous"):
+        pa._check(good.transpose(0, 1), "q", (torch.float16,), 3)
+    with pytest.raises(ValueError, match="device tensor"):
+        pa._check(good, "q", (torch.float16,), 3)
+
+
 def swap_args(**over):
     a = dict(src_k=FAKE, src_v=FAKE, src_ks=None, src_vs=None, dst_k=FAKE, dst_v=FAKE, dst_ks=None,
              dst_vs=None, block_mapping=FAKE, num_pairs=2, num_kv_heads=8, head_dim=128,
