@@ -230,3 +230,80 @@ def test_fused_append_ragged_groups(kv):
         assert np.array_equal(bits(d["k_scale"]), host_bits(eks))
         assert np.array_equal(bits(d["v_scale"]), host_bits(evs))
     assert_attention_close(out, ref, f"fused shared-prefix append, ragged groups, {kv}")
+
+
+@pytest.mark.parametrize("hq,hkv,kv", [(16, 4, "f16"), (16, 4, "fp8_e4m3"), (32, 4, "f16"),
+                                       (32, 1, "fp8_e4m3")])
+def test_fused_append_captured_in_a_graph_replays_exactly(hq, hkv, kv):
+    """pa_decode_shared_prefix_append captured once into a HIP graph over ragged groups (the
+    vector-ALU launch with its prefix pass at G 4, the matrix-core decode after a prefix launch
+    at G 8 and 32, split tails merged by the merge kernel) and replayed with eager work between
+    the replays: every replay equals the eager call bit for bit, the pool equals the oracle's
+    append, and the arrival counters are back at zero. The workspace is passed in and appending
+    the same rows again leaves the cache (and an E4M3 block's scale) as it is."""
+    import paged_kv_cache_287_amd as pa
+
+    case = workloads.prefix_groups(150 + hq + hkv, GROUPS, hq, hkv, 128, 16, kv_dtype=kv)
+    rng = np.random.default_rng(151)
+    s, d_, bs = case.num_seqs, case.head_dim, case.block_size
+    nk = rng.standard_normal((s, hkv, d_), dtype=np.float32).astype(np.float16)
+    nv = rng.standard_normal((s, hkv, d_), dtype=np.float32).astype(np.float16)
+    slots = np.full(s, -1, np.int64)
+    gpb = np.repeat(case.group_prefix_blocks, np.diff(case.group_start))
+    for b, L in enumerate(case.context_lens):
+        L = int(L)
+        if L >= 1 and L - 1 >= int(gpb[b]) * bs:
+            slots[b] = int(case.block_tables[b, (L - 1) // bs]) * bs + (L - 1) % bs
+    if kv == "f16":
+        ek, ev = oracle.kv_write(nk, nv, case.k_cache, case.v_cache, slots)
+        eks = evs = None
+    else:
+        ek, ev, eks, evs = oracle.kv_write_fp8(nk, nv, case.k_cache, case.v_cache, case.k_scale,
+                                               case.v_scale, slots)
+    ref = oracle.decode(case.q, ek, ev, case.block_tables, case.context_lens, case.scale,
+                        kv_dtype=kv, k_scale=eks, v_scale=evs)
+    d = case_to_device(case)
+    gs = case.group_start
+    g_nk, g_nv, g_slots, g_gs, g_gpb = dev(nk), dev(nv), dev(slots), dev(gs), dev(case.group_prefix_blocks)
+    max_ctx = int(case.context_lens.max())
+    kvt = pa.PA_KV_F16 if kv == "f16" else pa.PA_KV_FP8_E4M3
+    need = pa.shared_prefix_workspace_bytes(s, hq, hkv, d_, bs, max_ctx, kvt, 256)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+
+    def step():
+        pa.pa_decode_shared_prefix_append(
+            out, d["q"], g_nk, g_nv, d["k_cache"], d["v_cache"], g_slots, d["block_tables"],
+            d["context_lens"], g_gs, g_gpb, float(case.scale),
+            max_group_seqs=int(np.diff(gs).max()),
+            max_prefix_blocks=max(1, int(case.group_prefix_blocks.max())), k_scale=d["k_scale"],
+            v_scale=d["v_scale"], max_context_len=max_ctx, partition_tokens=256, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_attention_close(eager, ref, f"eager fused shared-prefix step {hq}q/{hkv}kv {kv}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+    assert np.array_equal(bits(d["k_cache"]), host_bits(ek))
+    assert np.array_equal(bits(d["v_cache"]), host_bits(ev))
+    if eks is not None:
+        assert np.array_equal(bits(d["k_scale"]), host_bits(eks))
+        assert np.array_equal(bits(d["v_scale"]), host_bits(evs))
+    assert int(ws[:256].count_nonzero()) == 0, "arrival counters not returned to zero"
