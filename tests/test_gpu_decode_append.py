@@ -245,8 +245,9 @@ def test_append_matrix_core_ragged(d, bs):
 def test_append_full_size_workloads(name):
     """The benchmark's other workloads at full size in the launch configuration it times
     (automatic partition size): MQA and GQA-8 through the matrix-core fused launch, MHA with an
-    E4M3 cache through the append-then-decode route, uneven lengths split over several
-    partitions, and the one-KV-head shard of the 8B shape (4 partitions per sequence). Fused against two calls bit for bit (outputs and caches), the oracle on sampled
+    E4M3 cache through the vector-ALU kernel's fused E4M3 append (one query head per tile),
+    uneven lengths split over several partitions, and the one-KV-head shard of the 8B shape
+    (4 partitions per sequence). Fused against two calls bit for bit (outputs and caches), the oracle on sampled
     sequences."""
     case = gen(workloads.by_name, name)
     nk, nv, slots = new_rows(case, 790)
