@@ -105,12 +105,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 # The checks and the stream lookup below run on every call, so they are kept cheap: a decode
 # call of a small batch runs for 15-20 us on the GPU, and the host spent ~15 us per call when
 # it looked up torch.cuda.current_stream() (~2.8 us) and tested each tensor attribute apart.
-_raw_stream = torch._C._cuda_getCurrentRawStream
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream) -> Optional[int]:
     if stream is None:
-        return _raw_stream(torch.cuda.current_device())
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
+        return torch.cuda.current_stream().cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
