@@ -118,3 +118,22 @@ def test_sq_ratios_from_two_counter_passes(tmp_path):
     assert "| LDS active | 0.250 |" in text
     assert "| LDS bank-conflict share | 0.312 |" in text
     assert "| wave time waiting to issue (dependencies, busy units) | 0.500 |" in text
+
+
+def test_sq_vector_alu_rows_leave_out_the_mfma_instructions(tmp_path):
+    # SQ_INSTS_VALU counts the matrix-core instructions as well: the vector-ALU rows subtract
+    # SQ_INSTS_MFMA, the raw VALU row keeps the counter as read
+    cyc = 200_000
+    valu, mfma = 1024 * cyc // 8, 3_000_000
+    sq_csv(str(tmp_path / "a" / "a_counter_collection.csv"), DECODE,
+           {"SQ_WAVES": 2048, "SQ_INSTS_VALU": valu + mfma, "SQ_INSTS_MFMA": mfma,
+            "SQ_VALU_MFMA_BUSY_CYCLES": 0, "GRBM_GUI_ACTIVE": 8 * cyc})
+    bench_log(str(tmp_path / "b.log"), 1 << 30)
+    out = str(tmp_path / "sq.md")
+    run("sq", str(tmp_path / "a"), "--bench-log", str(tmp_path / "b.log"),
+        "--kernel", "decode_partition_kernel", "--command", "ca", "--out", out)
+    text = open(out).read()
+    assert "| vector-ALU issue share | 0.500 |" in text
+    assert f"| VALU excl. MFMA per wave | {valu / 2048:.0f} |" in text
+    assert f"| VALU per wave | {(valu + mfma) / 2048:.0f} |" in text
+    assert f"| MFMA per wave | {mfma / 2048:.0f} |" in text
