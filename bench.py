@@ -419,8 +419,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence or KV head with no exchange; see the design notes)",
-              file=sys.stderr)
+              "(the decode path shards by sequence or by KV head with no exchange inside "
+              "attention: one process per GPU, each on its own share)", file=sys.stderr)
         sys.exit(2)
     if args.workload.startswith("prefill"):
         return main_prefill(args)

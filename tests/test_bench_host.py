@@ -45,3 +45,26 @@ def test_step_inputs_rewrite_the_newest_position_in_place():
         # the row already cached there, so repeated steps keep the inputs unchanged
         assert np.array_equal(nk[b].view(np.uint16), case.k_cache[blk, :, off, :].view(np.uint16))
         assert np.array_equal(nv[b].view(np.uint16), case.v_cache[blk, :, off, :].view(np.uint16))
+
+
+def test_kv_head_shard_reads_an_eighth_of_the_8b_workload():
+    # the shard keeps the 8B shape's sequences, lengths, block size and head dim with one of
+    # its eight KV heads (and that head's four query heads)
+    shard, full = workloads.kv_head_shard(), workloads.eight_b()
+    assert (shard.num_seqs, shard.head_dim, shard.block_size) == (full.num_seqs, full.head_dim,
+                                                                  full.block_size)
+    assert np.array_equal(shard.context_lens, full.context_lens)
+    assert (shard.num_q_heads, shard.num_kv_heads) == (4, 1)
+    assert bench.kv_bytes(shard) * 8 == bench.kv_bytes(full) == 1 << 30
+
+
+def test_bench_measures_one_gpu_only():
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=root, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
