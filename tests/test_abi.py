@@ -375,3 +375,43 @@ def test_noalloc_rejects_calls_beyond_its_array_before_touching_the_device():
                                          FAKE, FAKE, None, 512, 32, 8, 128, 16, 40000, 256, 4096, 256,
                                          0.088, pa.PA_KV_F16, None)
     assert st == pa.PA_ERR_WORKSPACE
+
+
+def test_partition_and_workspace_contract_over_random_shapes():
+    """For random decode shapes the automatic partition size is a valid one (a power of two in
+    [256, 4096], at most 256 x block size), an explicit valid size comes back unchanged and an
+    invalid one is refused, and a workspace of pa_decode_workspace_bytes holds what the header
+    says: nothing for one partition per sequence, else whole 16 KiB granules whose counter zone
+    (1/64 of the buffer) has room for at least one counter per (sequence, KV head) and whose
+    partial zone has room for a (max, sum, D floats) row per (sequence, query head, partition)."""
+    from hypothesis import given, settings
+    from hypothesis import strategies as st
+
+    @settings(max_examples=400, deadline=None)
+    @given(s=st.integers(1, 3000), hkv=st.sampled_from([1, 2, 4, 8, 16, 32]),
+           g=st.sampled_from([1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 33, 35, 64]),
+           d=st.sampled_from([64, 128]), bs=st.sampled_from([8, 16, 32, 64]),
+           ctx=st.integers(1, 200_000), kv=st.sampled_from([pa.PA_KV_F16, pa.PA_KV_FP8_E4M3]),
+           explicit=st.sampled_from([0, 128, 256, 384, 512, 1024, 2048, 4096, 8192]))
+    def check(s, hkv, g, d, bs, ctx, kv, explicit):
+        hq = hkv * g
+        pt = pa.decode_partition_tokens(s, hq, hkv, d, bs, ctx, kv, explicit)
+        valid = lambda v: 256 <= v <= 4096 and v & (v - 1) == 0 and v <= 256 * bs
+        if explicit:
+            assert pt == (explicit if valid(explicit) else 0)
+            if pt == 0:
+                return
+        assert valid(pt), (s, hq, hkv, d, bs, ctx, kv, pt)
+        parts = -(-ctx // pt)
+        if parts > 65535:
+            return
+        ws = pa.decode_workspace_bytes(s, hq, hkv, d, bs, ctx, kv, explicit)
+        if parts == 1:
+            assert ws == 0
+            return
+        assert ws > 0 and ws % 16384 == 0
+        counter_zone = 256 * (ws // 16384)
+        assert counter_zone >= s * hkv * 4
+        assert ws - counter_zone >= s * hq * parts * (2 + d) * 4
+
+    check()
